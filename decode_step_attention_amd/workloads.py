@@ -1,0 +1,188 @@
+"""Seeded synthetic inputs for decode-step attention, shared by the tests, the
+smoke check and the benchmark.
+
+This module draws numbers and lays them out; it holds none of the
+attention's arithmetic (no bias add, no rounding rule of the cache, no
+quantiser, no softmax).  Both the GPU path and the CPU oracle receive the
+very same bytes from here.
+
+Workloads (shapes, types, value distributions) follow the pages' decode
+setting: a pre-allocated [B, H_kv, L_max, D] cache per layer
+([intelliparadigm.com .../2131745] section 2.1), fp16 caches of a
+7B/13B-class model with hidden 4096 ([pptc.cn/news/144085] section 3.1, the
+32-sequence / 2048-token / 32-layer sizing example), grouped KV heads
+([pptc.cn/news/144085] section 3.4) and an INT8 cache ([pptc.cn/news/144085]
+section 3.1).
+
+Generation: one ``torch.Generator`` per (seed, tensor tag, layer), on the
+device the tensor is made on.  Small cases are generated on the host and
+copied; full-size cases are generated on the GPU and the oracle receives
+copies of those bytes.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Dict, List, Optional
+
+import torch
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+
+_TAGS = {"q": 1, "k_new": 2, "v_new": 3, "bias": 4, "k_cache": 5, "v_cache": 6,
+         "k_scale": 7, "v_scale": 8, "lens": 9}
+
+
+def act_dtype(kv_dtype: str) -> str:
+    """Activation type (q, k_new, v_new, bias, out): the cache type for float
+    caches and fp16 next to an INT8 cache."""
+    return "f16" if kv_dtype == "i8" else kv_dtype
+
+
+@dataclass(frozen=True)
+class Case:
+    """One decode-step problem.
+
+    ``lens``: None for every sequence at ``ctx`` tokens (after the append),
+    or (lo, hi) for lengths drawn uniformly from [lo, hi] per sequence.
+    ``value_scale``: standard deviation of every drawn real value.
+    ``int8_code_gain``: prefilled INT8 rows hold codes round(gain * N(0,1))
+    clamped to +-127, with a per-row scale of (1 +- 5%) / gain, so that the
+    dequantised values are again about N(0,1) * value_scale-free."""
+    name: str
+    batch: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    kv_dtype: str
+    ctx: int
+    max_seq_len: int
+    value_scale: float
+    lens: Optional[tuple] = None
+    layers: int = 1
+    rotate: int = 1
+    seed: int = 1000
+    int8_code_gain: float = 127.0 / 3.0
+
+    @property
+    def act_dtype(self) -> str:
+        return act_dtype(self.kv_dtype)
+
+    @property
+    def group(self) -> int:
+        return self.n_heads // self.n_kv_heads
+
+    def with_(self, **kw) -> "Case":
+        return replace(self, **kw)
+
+
+# The five workloads.  Value scales: N(0,1)/sqrt(D) where stated; the INT8
+# workload states N(0,1) data (absmax/127 scales) and no 1/sqrt(D) factor.
+CASES: Dict[str, Case] = {
+    "tiny": Case("tiny", 1, 8, 8, 64, "f32", ctx=128, max_seq_len=128,
+                 value_scale=1 / 8.0, seed=1000),
+    "7b": Case("7b", 8, 32, 32, 128, "f16", ctx=2048, max_seq_len=2048,
+               value_scale=1 / math.sqrt(128), rotate=32, seed=1001),
+    "sizing32": Case("sizing32", 32, 32, 32, 128, "f16", ctx=2048, max_seq_len=2048,
+                     value_scale=1 / math.sqrt(128), layers=32, seed=1002),
+    "gqa": Case("gqa", 16, 64, 8, 128, "bf16", ctx=8192, max_seq_len=8192,
+                value_scale=1 / math.sqrt(128), lens=(512, 8192), rotate=8, seed=1003),
+    "int8": Case("int8", 64, 40, 40, 128, "i8", ctx=4096, max_seq_len=4096,
+                 value_scale=1.0, rotate=2, seed=1004),
+}
+
+
+def _gen(case: Case, tag: str, layer: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed((case.seed * 1_000_003 + _TAGS[tag] * 10_007 + layer * 101) % (2 ** 62))
+    return g
+
+
+def seq_lens(case: Case) -> torch.Tensor:
+    """Per-sequence lengths after the append (host int32 tensor)."""
+    if case.lens is None:
+        return torch.full((case.batch,), case.ctx, dtype=torch.int32)
+    lo, hi = case.lens
+    g = _gen(case, "lens", 0, "cpu")
+    return torch.randint(lo, hi + 1, (case.batch,), generator=g, dtype=torch.int32)
+
+
+def _normal(case: Case, tag: str, layer: int, shape, dtype: str, device) -> torch.Tensor:
+    g = _gen(case, tag, layer, device)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    x.mul_(case.value_scale)
+    return x.to(TORCH_DTYPES[dtype])
+
+
+def _fill_cache_float(t: torch.Tensor, case: Case, tag: str, layer: int) -> None:
+    """Fill a [B, Hkv, Lmax, D] float cache one (b) slab at a time so the
+    fp32 temporary stays small."""
+    g = _gen(case, tag, layer, t.device)
+    tmp = torch.empty(t.shape[1:], device=t.device, dtype=torch.float32)
+    for b in range(t.shape[0]):
+        tmp.normal_(generator=g).mul_(case.value_scale)
+        t[b].copy_(tmp)
+
+
+def _fill_cache_int8(codes: torch.Tensor, scales: torch.Tensor, case: Case, tag: str,
+                     stag: str, layer: int) -> None:
+    g = _gen(case, tag, layer, codes.device)
+    tmp = torch.empty(codes.shape[1:], device=codes.device, dtype=torch.float32)
+    for b in range(codes.shape[0]):
+        tmp.normal_(generator=g).mul_(case.int8_code_gain).round_().clamp_(-127, 127)
+        codes[b].copy_(tmp)
+    gs = _gen(case, stag, layer, codes.device)
+    u = torch.rand(scales.shape, generator=gs, device=codes.device, dtype=torch.float32)
+    scales.copy_((0.95 + 0.1 * u) / case.int8_code_gain)
+
+
+def make_inputs(case: Case, device="cpu", layer: int = 0, poison: bool = True,
+                lens: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """All inputs of one layer's decode step.
+
+    Cache rows [0, L_b - 1) hold prefilled history; row L_b - 1 is the slot
+    the step appends into.  With ``poison`` every row >= L_b - 1 is NaN (float
+    caches) or has a NaN scale (INT8), so a read of anything but the history
+    shows up in the output."""
+    B, H, Hkv, D, Lmax = case.batch, case.n_heads, case.n_kv_heads, case.head_dim, case.max_seq_len
+    act = case.act_dtype
+    L = (seq_lens(case) if lens is None else lens.to(torch.int32).cpu())
+    t: Dict[str, torch.Tensor] = {}
+    t["q"] = _normal(case, "q", layer, (B, H, D), act, device)
+    t["k_new"] = _normal(case, "k_new", layer, (B, Hkv, D), act, device)
+    t["v_new"] = _normal(case, "v_new", layer, (B, Hkv, D), act, device)
+    t["bias"] = _normal(case, "bias", layer, ((H + 2 * Hkv) * D,), act, device)
+    shape = (B, Hkv, Lmax, D)
+    kvt = TORCH_DTYPES[case.kv_dtype]
+    k = torch.empty(shape, dtype=kvt, device=device)
+    v = torch.empty(shape, dtype=kvt, device=device)
+    if case.kv_dtype == "i8":
+        sc = torch.empty((2, B, Hkv, Lmax), dtype=torch.float32, device=device)
+        _fill_cache_int8(k, sc[0], case, "k_cache", "k_scale", layer)
+        _fill_cache_int8(v, sc[1], case, "v_cache", "v_scale", layer)
+        t["kv_scales"] = sc
+    else:
+        _fill_cache_float(k, case, "k_cache", layer)
+        _fill_cache_float(v, case, "v_cache", layer)
+    if poison:
+        for b in range(B):
+            p = int(L[b]) - 1
+            if case.kv_dtype == "i8":
+                t["kv_scales"][:, b, :, max(p, 0):] = float("nan")
+            else:
+                k[b, :, max(p, 0):, :] = float("nan")
+                v[b, :, max(p, 0):, :] = float("nan")
+    t["k_cache"] = k
+    t["v_cache"] = v
+    t["seq_lens"] = L.to(device)
+    t["step"] = int(L.max())
+    return t
+
+
+def kv_bytes(case: Case, lens: Optional[List[int]] = None) -> int:
+    """Bytes of K and V (and INT8 scales) that one step must read: every
+    position [0, L_b) of every (sequence, KV head), K and V."""
+    L = seq_lens(case).tolist() if lens is None else list(lens)
+    row = case.head_dim * ELEM_BYTES[case.kv_dtype] + (4 if case.kv_dtype == "i8" else 0)
+    return sum(L) * case.n_kv_heads * 2 * row

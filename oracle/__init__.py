@@ -1,0 +1,151 @@
+"""CPU oracle for one decode step of masked multi-head attention over a KV cache.
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The GPU library never imports, links
+or runs anything here, and nothing here imports the GPU library.
+
+The arithmetic lives in ``ftm_oracle.c`` (plain C, fp64 attention, fp32
+append); this module only builds it with gcc and marshals numpy arrays.
+
+Element types are passed as numpy arrays holding the raw values: float32,
+float16, bfloat16 as its uint16 bit pattern, int8.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ftm_oracle.c")
+_LIB = os.path.join(_HERE, "libftm_oracle.so")
+
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
+_NP = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "i8": np.int8}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with IEEE semantics (no fast-math, no contraction)."""
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+           "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
+           _SRC, "-o", _LIB + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.orc_decode_mha.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                   i32, i32, i32, i32, vp, vp, vp, i32]
+    lib.orc_decode_mha.restype = i32
+    lib.orc_f16_bits_to_double.argtypes = [ctypes.c_uint16]
+    lib.orc_f16_bits_to_double.restype = ctypes.c_double
+    lib.orc_bf16_bits_to_double.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_bits_to_double.restype = ctypes.c_double
+    lib.orc_float_to_f16_rne.argtypes = [ctypes.c_float]
+    lib.orc_float_to_f16_rne.restype = ctypes.c_uint16
+    lib.orc_float_to_bf16_rne.argtypes = [ctypes.c_float]
+    lib.orc_float_to_bf16_rne.restype = ctypes.c_uint16
+    lib.orc_quantize_row_i8.argtypes = [vp, i32, vp]
+    lib.orc_quantize_row_i8.restype = ctypes.c_float
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _need(a, dtype, shape, name, writable=False):
+    if a.dtype != np.dtype(dtype):
+        raise TypeError(f"{name}: dtype {a.dtype}, expected {np.dtype(dtype)}")
+    if tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {a.shape}, expected {tuple(shape)}")
+    if not a.flags.c_contiguous or (writable and not a.flags.writeable):
+        raise ValueError(f"{name}: must be C-contiguous" + (" and writable" if writable else ""))
+
+
+def act_dtype_of(kv_dtype: str) -> str:
+    """Activation type: the cache type for float caches, fp16 for INT8."""
+    return "f16" if kv_dtype == "i8" else kv_dtype
+
+
+def decode_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step,
+               n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales=None,
+               n_threads=1, want_probs=False) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """One decode step; appends into k_cache/v_cache/kv_scales in place.
+
+    Returns (out[B,H,D] float64, probs[B,H,step] float64 or None)."""
+    lib = _load()
+    B, Hkv, Lmax, D = k_cache.shape
+    H = n_heads
+    if D != head_dim or Hkv != n_kv_heads:
+        raise ValueError("cache shape does not match head_dim / n_kv_heads")
+    act = _NP[act_dtype_of(kv_dtype)]
+    _need(q, act, (B, H, D), "q")
+    _need(k_new, act, (B, Hkv, D), "k_new")
+    _need(v_new, act, (B, Hkv, D), "v_new")
+    if qkv_bias is not None:
+        _need(qkv_bias, act, ((H + 2 * Hkv) * D,), "qkv_bias")
+    _need(k_cache, _NP[kv_dtype], (B, Hkv, Lmax, D), "k_cache", True)
+    _need(v_cache, _NP[kv_dtype], (B, Hkv, Lmax, D), "v_cache", True)
+    if seq_lens is not None:
+        _need(seq_lens, np.int32, (B,), "seq_lens")
+    if kv_scales is not None:
+        _need(kv_scales, np.float32, (2, B, Hkv, Lmax), "kv_scales", True)
+    out = np.empty((B, H, D), dtype=np.float64)
+    probs = np.empty((B, H, step), dtype=np.float64) if want_probs else None
+    rc = lib.orc_decode_mha(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias),
+                            _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                            B, Lmax, int(step), H, Hkv, D, DTYPES[kv_dtype],
+                            _ptr(kv_scales), _ptr(out), _ptr(probs), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out, probs
+
+
+def f16_bits_to_double(bits: int) -> float:
+    return _load().orc_f16_bits_to_double(bits)
+
+
+def bf16_bits_to_double(bits: int) -> float:
+    return _load().orc_bf16_bits_to_double(bits)
+
+
+def float_to_f16_rne(x: float) -> int:
+    return _load().orc_float_to_f16_rne(x)
+
+
+def float_to_bf16_rne(x: float) -> int:
+    return _load().orc_float_to_bf16_rne(x)
+
+
+def quantize_row_i8(x: np.ndarray) -> Tuple[np.ndarray, float]:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.shape[0], dtype=np.int8)
+    s = _load().orc_quantize_row_i8(_ptr(x), x.shape[0], _ptr(codes))
+    return codes, float(np.float32(s))
+
+
+def cache_to_f64(cache: np.ndarray, kv_dtype: str, scales: Optional[np.ndarray] = None) -> np.ndarray:
+    """Stored cache values widened exactly to float64 (INT8: code * scale).
+    ``scales`` is broadcast over the last axis."""
+    if kv_dtype == "f32":
+        return cache.astype(np.float64)
+    if kv_dtype == "f16":
+        return cache.astype(np.float64)
+    if kv_dtype == "bf16":
+        return (cache.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return cache.astype(np.float64) * scales.astype(np.float64)[..., None]
