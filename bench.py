@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of fused masked multi-head attention over a
+KV cache on one MI355X.
+
+A step is one pass of the whole path (bias add, append, q.K, softmax, P.V,
+and the combine when the sequence is split) over one batch: one layer's
+ftm_decode_mha call, or all layers back-to-back for the 32-layer sizing
+workload.  Inputs are seeded synthetic tensors already resident in HBM; the
+layer caches rotate so that the working set exceeds the 256 MB last-level
+cache.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config 7b]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from decode_step_attention_amd import workloads as W  # noqa: E402
+
+METRIC = "decode-MHA KV read GB/s (% of HBM peak) + attention tokens/s at batch×ctx"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+CSRC = os.path.join(ROOT, "decode_step_attention_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(config: str):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attention_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t
+
+
+def describe(case: W.Case) -> str:
+    lens = (f"L in U[{case.lens[0]}, {case.lens[1]}]" if case.lens else f"ctx {case.ctx}")
+    grp = f"{case.n_heads}q/{case.n_kv_heads}kv heads" if case.group > 1 else f"{case.n_heads} heads"
+    return (f"{case.name}: batch {case.batch}, {grp} x {case.head_dim}, {case.kv_dtype} cache, {lens}"
+            + (f", {case.layers} layers" if case.layers > 1 else ""))
+
+
+def cpu_baseline(case, inputs, lens, budget_s: float):
+    """The CPU oracle, as it stands, on the host cores: a bounded sample of the
+    same workload (whole sequences of layer 0), timed like the GPU step."""
+    import oracle
+    ncores = min(len(os.sched_getaffinity(0)), 16)
+    inp = inputs[0]
+    act, kvd = case.act_dtype, case.kv_dtype
+    per_seq = case.n_kv_heads * 2 * case.max_seq_len * case.head_dim * W.ELEM_BYTES[kvd]
+    nb = int(max(1, min(case.batch, (512 << 20) // per_seq)))
+
+    def host(t, dt):
+        t = t.detach().contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16).copy() if dt == "bf16" else t.numpy().copy()
+
+    H, Hkv, D = case.n_heads, case.n_kv_heads, case.head_dim
+    q = host(inp["q"][:nb], act)
+    kn = host(inp["k_new"][:nb], act)
+    vn = host(inp["v_new"][:nb], act)
+    bias = host(inp["bias"], act)
+    kc0 = host(inp["k_cache"][:nb], kvd)
+    vc0 = host(inp["v_cache"][:nb], kvd)
+    sc0 = host(inp["kv_scales"][:, :nb], "f32") if kvd == "i8" else None
+    sl = np.ascontiguousarray(lens[:nb].astype(np.int32))
+    step = int(sl.max())
+    sample_bytes = int(W.kv_bytes(case.with_(batch=nb), sl.tolist()))
+    runs, total = 0, 0.0
+    best = float("inf")
+    while runs < 3 or (total < budget_s and runs < 50):
+        kc, vc = kc0.copy(), vc0.copy()
+        sc = sc0.copy() if sc0 is not None else None
+        t0 = time.perf_counter()
+        oracle.decode_mha(q, kn, vn, bias, kc, vc, sl, step, H, Hkv, D, kvd, sc, n_threads=ncores)
+        dt = time.perf_counter() - t0
+        best = min(best, dt)
+        total += dt
+        runs += 1
+    return {"value": sample_bytes / best / 1e9, "unit": "GB/s", "cores": ncores, "kind": "oracle",
+            "tokens_per_s": nb / best,
+            "sample": f"layer 0, sequences 0..{nb - 1} of {case.batch} ({sample_bytes / 2**20:.0f} MiB "
+                      f"of K/V), fp64 oracle, best of {runs} runs, {total:.1f} s in total"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="7b", choices=sorted(W.CASES))
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time for the CPU baseline (0 skips it)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from decode_step_attention_amd import ftm
+
+    dev = torch.device("cuda:0")
+    case = W.CASES[args.config]
+    layers = case.layers
+    rotate = max(case.rotate, layers)
+    lens = W.seq_lens(case)
+    print(f"# {describe(case)}; {rotate} cache sets; generating inputs", file=sys.stderr, flush=True)
+    inputs = [W.make_inputs(case, dev, layer=i, poison=False, lens=lens) for i in range(rotate)]
+    outs = [torch.empty((case.batch, case.n_heads, case.head_dim),
+                        dtype=W.TORCH_DTYPES[case.act_dtype], device=dev) for _ in range(2)]
+    step = int(lens.max())
+    lens_np = lens.numpy()
+    kv_layer = W.kv_bytes(case, lens_np.tolist())
+    kv_step = kv_layer * layers
+    stream = torch.cuda.current_stream(dev)
+
+    def call(i):
+        inp = inputs[i % rotate]
+        ftm.ftm_decode_mha(inp["q"], inp["k_new"], inp["v_new"], inp["bias"], inp["k_cache"],
+                           inp["v_cache"], inp["seq_lens"], step, outs[i & 1], inp.get("kv_scales"),
+                           stream=stream.cuda_stream)
+
+    # a plain device copy of known size: reference bandwidth, and the
+    # calibration dispatch for the HBM byte counters
+    n_copy = 256 << 20
+    src = torch.empty(n_copy, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n_copy * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    k = 0
+    for _ in range(args.warmup):
+        for _l in range(layers):
+            call(k)
+            k += 1
+    torch.cuda.synchronize()
+    ftm.ftm_timing_enable(args.steps * layers + 8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for _l in range(layers):
+            call(k)
+            k += 1
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_att, ms_att = ftm.ftm_timing_read(0)
+    n_cmb, ms_cmb = ftm.ftm_timing_read(1)
+    ftm.ftm_timing_disable()
+    elapsed = t1 - t0
+    ms_step = elapsed * 1e3 / args.steps
+    gbs = kv_step * args.steps / elapsed / 1e9
+    avg_att_us = ms_att * 1e3 / max(n_att, 1)
+    achieved = kv_layer / (avg_att_us * 1e-6) / 1e9
+    traffic = read_traffic(args.config)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
+            "kernel": "attention_kernel", "avg_launch_us": round(avg_att_us, 2),
+            "launches": n_att, "algorithmic_bytes_per_launch": kv_layer}
+    result = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.kv_dtype, "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": describe(case), "batch": case.batch, "n_heads": case.n_heads,
+                   "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim,
+                   "context": step, "kv_dtype": case.kv_dtype, "act_dtype": case.act_dtype,
+                   "layers_per_step": layers, "cache_sets_rotated": rotate},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(case.batch * args.steps / elapsed, 1),
+        "kv_bytes_per_step": kv_step,
+        "combine_avg_launch_us": round(ms_cmb * 1e3 / n_cmb, 2) if n_cmb else None,
+        "device_copy_GBs": round(copy_gbs, 1),
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case, inputs, lens_np, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,624 @@
+// decode_attention.hip -- gfx950 kernels for one decode step of masked
+// multi-head attention over a [B, Hkv, Lmax, D] KV cache.
+//
+// attention_kernel: one workgroup (4 wave64) owns one (sequence b, KV head j,
+//   query-head group, chunk of positions).  It folds the QKV bias into the
+//   query, streams the chunk's K and V rows once from HBM as 16-byte
+//   vectors through buffer loads (rows past the valid range read as zero
+//   and fetch nothing), reduces each q.k across the lanes holding one row
+//   with DPP, keeps an online softmax state per row slot, and merges slots
+//   and waves at the end.  The workgroup whose chunk holds the new position
+//   appends the biased K/V row (fp32 add, RNE rounding or INT8 quantising)
+//   and feeds it to the softmax from registers.  With one chunk per
+//   sequence it writes the output; otherwise it writes the chunk's
+//   (max, sum, unnormalised output) for the combine kernel.
+// combine_kernel: merges the chunks' softmax states per (b, h).
+//
+// The method: fused decode attention with the new K/V appended to a
+// pre-allocated cache ([lpnh.cn/news/2765398] sections 2.1 and 2.2), the
+// maximum subtracted before exponentiation ([lpnh.cn/news/2765398] section
+// 6.1), blockwise softmax statistics so a long sequence can be split into
+// independent pieces ([pptc.cn/news/144085] section 2.2), grouped KV heads
+// ([pptc.cn/news/144085] section 3.4) and an INT8 cache converted back at
+// compute time ([pptc.cn/news/144085] section 3.1; [intelliparadigm.com
+// .../2131745] section 2.1).  Scores never leave registers.
+#include "ftm_internal.hpp"
+
+namespace ftm {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+// Buffer descriptor word 3 for raw (untyped) buffer access on the gfx9 family.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Number formats
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+// fp32 -> binary16, round to nearest even (the hardware's default mode).
+__device__ __forceinline__ uint32_t float_to_half_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+// fp32 -> bfloat16, round to nearest even on the integer pattern; NaN maps
+// to the canonical quiet NaN with its sign.
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Cache element type: size and how a 16-byte vector unpacks into fp32.
+template <int KV> struct Elem;
+template <> struct Elem<KV_F32> {
+    static constexpr int bytes = 4;
+    __device__ static void unpack(const u32x4 w, float* x) {
+        x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+        x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+    }
+};
+template <> struct Elem<KV_F16> {
+    static constexpr int bytes = 2;
+    __device__ static void unpack(const u32x4 w, float* x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = half_bits_to_float(w[i] & 0xffffu);
+            x[2 * i + 1] = half_bits_to_float(w[i] >> 16);
+        }
+    }
+};
+template <> struct Elem<KV_BF16> {
+    static constexpr int bytes = 2;
+    __device__ static void unpack(const u32x4 w, float* x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Elem<KV_I8> {
+    static constexpr int bytes = 1;
+    // INT8 codes as fp32 (the scale is applied to the reduced dot product
+    // and to the softmax weight, so it is not multiplied in here).
+    __device__ static void unpack(const u32x4 w, float* x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[4 * i + k] = (float)(int8_t)((w[i] >> (8 * k)) & 0xffu);
+    }
+};
+
+// Activation type (q, k_new, v_new, bias, out): the cache type for float
+// caches and fp16 next to an INT8 cache.
+template <int KV> struct Act;
+template <> struct Act<KV_F32> {
+    __device__ static float ld(const void* p, size_t i) { return ((const float*)p)[i]; }
+    __device__ static void st(void* p, size_t i, float v) { ((float*)p)[i] = v; }
+};
+template <> struct Act<KV_F16> {
+    __device__ static float ld(const void* p, size_t i) { return half_bits_to_float(((const uint16_t*)p)[i]); }
+    __device__ static void st(void* p, size_t i, float v) { ((uint16_t*)p)[i] = (uint16_t)float_to_half_bits(v); }
+};
+template <> struct Act<KV_BF16> {
+    __device__ static float ld(const void* p, size_t i) { return bf16_bits_to_float(((const uint16_t*)p)[i]); }
+    __device__ static void st(void* p, size_t i, float v) { ((uint16_t*)p)[i] = (uint16_t)float_to_bf16_bits(v); }
+};
+template <> struct Act<KV_I8> : Act<KV_F16> {};
+
+// N consecutive activation elements starting at element `off` of `base`, as
+// fp32, read as 16-byte vectors (rows of q, k_new, v_new and the bias are
+// 16-byte aligned: D * element size is a multiple of 16 and the pointers
+// are checked on the host).
+template <int KV, int N>
+__device__ __forceinline__ void load_act(const void* base, size_t off, float* x) {
+    if constexpr (KV == KV_F32) {
+        static_assert(N % 4 == 0, "");
+        const u32x4* v = (const u32x4*)((const float*)base + off);
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) Elem<KV_F32>::unpack(v[i], x + 4 * i);
+    } else {
+        static_assert(N % 8 == 0, "");
+        const u32x4* v = (const u32x4*)((const uint16_t*)base + off);
+#pragma unroll
+        for (int i = 0; i < N / 8; ++i) {
+            if constexpr (KV == KV_BF16) Elem<KV_BF16>::unpack(v[i], x + 8 * i);
+            else Elem<KV_F16>::unpack(v[i], x + 8 * i);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions.  A cache row is held by LPR consecutive lanes
+// (LPR in {4, 8, 16, 32}); the all-reduce over those lanes stays inside a
+// DPP row where it can: quad swaps, then the half-row mirror (8 lanes) or
+// rotations by 4 and 8 (16 lanes); a 32-lane row adds one cross-row swap.
+// ---------------------------------------------------------------------------
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+
+template <int LPR> __device__ __forceinline__ float group_sum(float v) {
+    v += dpp<kQuadSwap1>(v);
+    v += dpp<kQuadSwap2>(v);
+    if constexpr (LPR == 8) v += dpp<kRowHalfMirror>(v);
+    if constexpr (LPR >= 16) {
+        v += dpp<kRowRor4>(v);
+        v += dpp<kRowRor8>(v);
+    }
+    if constexpr (LPR == 32) v += __shfl_xor(v, 16);
+    return v;
+}
+template <int LPR> __device__ __forceinline__ float group_max(float v) {
+    v = fmaxf(v, dpp<kQuadSwap1>(v));
+    v = fmaxf(v, dpp<kQuadSwap2>(v));
+    if constexpr (LPR == 8) v = fmaxf(v, dpp<kRowHalfMirror>(v));
+    if constexpr (LPR >= 16) {
+        v = fmaxf(v, dpp<kRowRor4>(v));
+        v = fmaxf(v, dpp<kRowRor8>(v));
+    }
+    if constexpr (LPR == 32) v = fmaxf(v, __shfl_xor(v, 16));
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer descriptor over [base, base + bytes).  Both are the same across the
+// wave; readfirstlane states that, so the descriptor sits in scalar
+// registers instead of being rebuilt per lane around every load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0, n, kRsrcWord3);
+}
+
+// ---------------------------------------------------------------------------
+// The new row: x = fl32(new + bias), stored as the cache type.  `stored`
+// receives what the cache now holds, as fp32 (INT8: the code), `scale` the
+// INT8 scale (1 otherwise), `packed` the 16 bytes this lane writes.
+// ---------------------------------------------------------------------------
+template <int KV, int D, int EPL, int LPR>
+__device__ __forceinline__ void make_new_row(const Params& p, const void* src, int bias_row,
+                                             size_t src_row, int c, float* stored, float& scale,
+                                             u32x4& packed) {
+    float x[EPL];
+    load_act<KV, EPL>(src, src_row * D + c * EPL, x);
+    if (p.bias) {
+        float bx[EPL];
+        load_act<KV, EPL>(p.bias, (size_t)bias_row * D + c * EPL, bx);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] = x[e] + bx[e];   // one fp32 rounding
+    }
+    scale = 1.0f;
+    if constexpr (KV == KV_F32) {
+        packed = u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                       __float_as_uint(x[3])};
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) stored[e] = x[e];
+    } else if constexpr (KV == KV_F16 || KV == KV_BF16) {
+        uint32_t hb[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            hb[e] = KV == KV_F16 ? float_to_half_bits(x[e]) : float_to_bf16_bits(x[e]);
+            stored[e] = KV == KV_F16 ? half_bits_to_float(hb[e]) : bf16_bits_to_float(hb[e]);
+        }
+        packed = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
+                       hb[6] | (hb[7] << 16)};
+    } else {
+        // symmetric INT8: s = absmax / 127 (IEEE division), code = rint(x / s)
+        // clamped to [-127, 127]; a zero row keeps s = 0 and zero codes.
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        amax = group_max<LPR>(amax);
+        scale = amax / 127.0f;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            float q = 0.0f;
+            if (scale != 0.0f) q = fminf(fmaxf(rintf(x[e] / scale), -127.0f), 127.0f);
+            stored[e] = q;
+            w[e / 4] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (e % 4));
+        }
+        packed = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Attention pass.  Template: cache type, head dim, query heads per pass (GT),
+// 16-byte loads per lane per K/V stream per iteration (U).
+// ---------------------------------------------------------------------------
+template <int KV, int D, int GT, int U>
+__global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
+    using E = Elem<KV>;
+    using A = Act<KV>;
+    constexpr int EPL = 16 / E::bytes;      // elements per lane per load
+    constexpr int LPR = D / EPL;            // lanes per cache row
+    constexpr int RPI = 64 / LPR;           // rows per wave-wide load
+    constexpr int ROW_BYTES = D * E::bytes;
+    constexpr int WAVE_ROWS = RPI * U;      // rows per wave per iteration
+    constexpr int BLOCK_ROWS = kWaves * WAVE_ROWS;
+    constexpr bool I8 = KV == KV_I8;
+    static_assert(LPR >= 4 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "row must span 4..32 lanes");
+
+    __shared__ float sm_m[kWaves][GT];
+    __shared__ float sm_l[kWaves][GT];
+    __shared__ float sm_o[kWaves][GT][D];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane / LPR;               // row slot of this lane
+    const int c = lane % LPR;               // 16-byte column slice of the row
+    const int chunk = blockIdx.x;
+    const int j = blockIdx.y / p.n_hg;
+    const int hgi = blockIdx.y - j * p.n_hg;
+    const int b = blockIdx.z;
+    const int h0 = j * p.G + hgi * GT;
+    const int heads_here = min(GT, p.G - hgi * GT);
+    // the length is the same for the whole workgroup; say so, so that the
+    // buffer descriptors built from it live in scalar registers
+    const int L = __builtin_amdgcn_readfirstlane(p.seq_lens ? p.seq_lens[b] : p.step);
+
+    if (L < 1 || L > p.step) {              // invalid length: NaN rows, no append
+        if (p.direct && chunk == 0)
+            for (int idx = threadIdx.x; idx < GT * D; idx += kThreads)
+                if (idx / D < heads_here)
+                    A::st(p.out, ((size_t)b * p.H + h0 + idx / D) * D + idx % D, __builtin_nanf(""));
+        return;
+    }
+    const int n_chunks = (L + p.chunk - 1) / p.chunk;
+    if (chunk >= n_chunks) return;
+    const int c0 = chunk * p.chunk;
+    const int c1 = min(c0 + p.chunk, L);
+    const int stream_end = min(c1, L - 1);  // the new row L-1 comes from registers
+    const bool owns_new = c1 == L;
+
+    // query with bias, in fp32, pre-scaled by log2(e)/sqrt(D) so the softmax
+    // runs on exp2
+    // (heads past the group read a valid row and are zeroed)
+    float qv[GT][EPL];
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+        load_act<KV, EPL>(p.q, ((size_t)b * p.H + min(h0 + g, p.H - 1)) * D + c * EPL, qv[g]);
+    if (p.bias) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float bx[EPL];
+            load_act<KV, EPL>(p.bias, (size_t)min(h0 + g, p.H - 1) * D + c * EPL, bx);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qv[g][e] = qv[g][e] + bx[e];
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[g][e] = g < heads_here ? qv[g][e] * p.qscale : 0.0f;
+
+    const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;   // row 0 of this (b, j)
+    const char* kbase = (const char*)p.k_cache + row0 * ROW_BYTES;
+    const char* vbase = (const char*)p.v_cache + row0 * ROW_BYTES;
+    const uint32_t valid_bytes = (uint32_t)max(stream_end, 0) * ROW_BYTES;
+    const auto krs = make_rsrc(kbase, valid_bytes);
+    const auto vrs = make_rsrc(vbase, valid_bytes);
+    const size_t plane = (size_t)p.B * p.Hkv * p.Lmax;       // INT8 scale plane
+    const auto ksrs = make_rsrc(I8 ? p.kv_scales + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
+    const auto vsrs = make_rsrc(I8 ? p.kv_scales + plane + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
+
+    float m[GT], l[GT], o[GT][EPL];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        m[g] = kNegInf;
+        l[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
+    }
+
+    for (int base = c0 + wave * WAVE_ROWS; base < stream_end; base += BLOCK_ROWS) {
+        u32x4 kr[U], vr[U];
+        float ksc[U], vsc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, 0);
+        if constexpr (I8) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                ksc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (base + u * RPI + r) * 4, 0, 0));
+                vsc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, (base + u * RPI + r) * 4, 0, 0));
+            }
+        }
+        // keep every load of this iteration in flight before any math: the
+        // scheduler would otherwise interleave load/wait/use and leave one
+        // 16-byte request per wave outstanding
+        __builtin_amdgcn_sched_barrier(0);
+        // scores (log2 domain)
+        float s[GT][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[EPL];
+            E::unpack(kr[u], x);
+            const bool valid = base + u * RPI + r < stream_end;
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                float d = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d = fmaf(qv[g][e], x[e], d);
+                d = group_sum<LPR>(d);
+                if constexpr (I8) d *= ksc[u];
+                s[g][u] = valid ? d : kNegInf;
+            }
+        }
+        // online softmax: new running max, rescale, weights
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float mt = s[g][0];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[g][u]);
+            const float mn = fmaxf(m[g], mt);
+            const float ms = mn == kNegInf ? 0.0f : mn;
+            const float a = fast_exp2(m[g] - ms);
+            l[g] *= a;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[g][e] *= a;
+            m[g] = mn;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                s[g][u] = fast_exp2(s[g][u] - ms);
+                l[g] += s[g][u];
+            }
+        }
+        // weighted sum of V
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[EPL];
+            E::unpack(vr[u], x);
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                float w = s[g][u];
+                if constexpr (I8) w *= vsc[u];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(w, x[e], o[g][e]);
+            }
+        }
+    }
+
+    // append the new row and add it to the softmax of row slot 0 of wave 0
+    if (owns_new && wave == 0) {
+        const int pnew = L - 1;
+        const size_t src_row = (size_t)b * p.Hkv + j;
+        float kx[EPL], vx[EPL], ks, vs;
+        u32x4 kpk, vpk;
+        make_new_row<KV, D, EPL, LPR>(p, p.k_new, p.H + j, src_row, c, kx, ks, kpk);
+        make_new_row<KV, D, EPL, LPR>(p, p.v_new, p.H + p.Hkv + j, src_row, c, vx, vs, vpk);
+        if (hgi == 0 && r == 0) {
+            *(u32x4*)((char*)p.k_cache + (row0 + pnew) * ROW_BYTES + c * 16) = kpk;
+            *(u32x4*)((char*)p.v_cache + (row0 + pnew) * ROW_BYTES + c * 16) = vpk;
+            if constexpr (I8) {
+                if (c == 0) {
+                    p.kv_scales[row0 + pnew] = ks;
+                    p.kv_scales[plane + row0 + pnew] = vs;
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) d = fmaf(qv[g][e], kx[e], d);
+            d = group_sum<LPR>(d);
+            if constexpr (I8) d *= ks;
+            if (r == 0) {
+                const float mn = fmaxf(m[g], d);
+                const float a = fast_exp2(m[g] - mn);
+                const float w = fast_exp2(d - mn);
+                l[g] = l[g] * a + w;
+                const float wv = I8 ? w * vs : w;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(wv, vx[e], o[g][e] * a);
+                m[g] = mn;
+            }
+        }
+    }
+
+    // merge the row slots of each wave
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const float m2 = __shfl_xor(m[g], off);
+            const float l2 = __shfl_xor(l[g], off);
+            const float mn = fmaxf(m[g], m2);
+            const float ms = mn == kNegInf ? 0.0f : mn;
+            const float a1 = fast_exp2(m[g] - ms);
+            const float a2 = fast_exp2(m2 - ms);
+            l[g] = l[g] * a1 + l2 * a2;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[g][e] = o[g][e] * a1 + __shfl_xor(o[g][e], off) * a2;
+            m[g] = mn;
+        }
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm_o[wave][g][c * EPL + e] = o[g][e];
+            if (c == 0) {
+                sm_m[wave][g] = m[g];
+                sm_l[wave][g] = l[g];
+            }
+        }
+    }
+    __syncthreads();
+
+    // merge the waves and write
+    for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
+        const int g = idx / D;
+        const int d = idx - g * D;
+        if (g >= heads_here) continue;
+        float M = sm_m[0][g];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
+        const float ms = M == kNegInf ? 0.0f : M;
+        float lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float a = fast_exp2(sm_m[w][g] - ms);
+            lsum += a * sm_l[w][g];
+            acc += a * sm_o[w][g][d];
+        }
+        const size_t bh = (size_t)b * p.H + h0 + g;
+        if (p.direct) {
+            A::st(p.out, bh * D + d, acc / lsum);
+        } else {
+            p.ws_o[(bh * p.S + chunk) * D + d] = acc;
+            if (d == 0) {
+                p.ws_ml[(bh * p.S + chunk) * 2] = M;
+                p.ws_ml[(bh * p.S + chunk) * 2 + 1] = lsum;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one wave per (b, h).  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// ---------------------------------------------------------------------------
+template <int KV, int D>
+__global__ void __launch_bounds__(kThreads) combine_kernel(const Params p) {
+    using A = Act<KV>;
+    constexpr int EL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (bh >= p.B * p.H) return;
+    const int b = bh / p.H;
+    const int L = __builtin_amdgcn_readfirstlane(p.seq_lens ? p.seq_lens[b] : p.step);
+    if (L < 1 || L > p.step) {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) A::st(p.out, (size_t)bh * D + lane * EL + e, __builtin_nanf(""));
+        return;
+    }
+    const int n_chunks = (L + p.chunk - 1) / p.chunk;
+    const float* ml = p.ws_ml + (size_t)bh * p.S * 2;
+    const float* wo = p.ws_o + (size_t)bh * p.S * D;
+    float M = kNegInf;
+    for (int s = lane; s < n_chunks; s += 64) M = fmaxf(M, ml[2 * s]);
+    M = wave_max(M);
+    float lsum = 0.0f;
+    for (int s = lane; s < n_chunks; s += 64) lsum += fast_exp2(ml[2 * s] - M) * ml[2 * s + 1];
+    lsum = wave_sum(lsum);
+    float acc[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] = 0.0f;
+#pragma unroll 4
+    for (int s = 0; s < n_chunks; ++s) {
+        const float a = fast_exp2(ml[2 * s] - M);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc[e] = fmaf(a, wo[(size_t)s * D + lane * EL + e], acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < EL; ++e) A::st(p.out, (size_t)bh * D + lane * EL + e, acc[e] / lsum);
+}
+
+constexpr int unroll_for(int gt) { return gt <= 2 ? 8 : 4; }
+
+template <int KV, int D, int GT>
+hipError_t launch_attention_t(const Params& p, hipStream_t s) {
+    dim3 grid(p.S, p.Hkv * p.n_hg, p.B);
+    hipLaunchKernelGGL((attention_kernel<KV, D, GT, unroll_for(GT)>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int KV, int D>
+hipError_t dispatch_gt(const Params& p, int gt, hipStream_t s) {
+    switch (gt) {
+    case 1: return launch_attention_t<KV, D, 1>(p, s);
+    case 2: return launch_attention_t<KV, D, 2>(p, s);
+    case 4: return launch_attention_t<KV, D, 4>(p, s);
+    case 8: return launch_attention_t<KV, D, 8>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int KV>
+hipError_t dispatch_d(const Params& p, int d, int gt, hipStream_t s) {
+    switch (d) {
+    case 64: return dispatch_gt<KV, 64>(p, gt, s);
+    case 128: return dispatch_gt<KV, 128>(p, gt, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int KV, int D>
+hipError_t launch_combine_t(const Params& p, hipStream_t s) {
+    const int blocks = (p.B * p.H + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL((combine_kernel<KV, D>), dim3(blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int group_tile(int G) {
+    if (G >= 8) return 8;
+    int t = 1;
+    while (t < G) t <<= 1;
+    return t;
+}
+
+int tile_rows(int kv, int head_dim, int gtile) {
+    const int bytes = kv == KV_F32 ? 4 : (kv == KV_I8 ? 1 : 2);
+    const int lpr = head_dim * bytes / 16;
+    return kWaves * (64 / lpr) * unroll_for(gtile);
+}
+
+hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, hipStream_t s) {
+    switch (kv) {
+    case KV_F32: return dispatch_d<KV_F32>(p, head_dim, gtile, s);
+    case KV_F16: return dispatch_d<KV_F16>(p, head_dim, gtile, s);
+    case KV_BF16: return dispatch_d<KV_BF16>(p, head_dim, gtile, s);
+    case KV_I8: return dispatch_d<KV_I8>(p, head_dim, gtile, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s) {
+#define FTM_COMBINE_CASE(K)                                               \
+    case K:                                                               \
+        return head_dim == 64 ? launch_combine_t<K, 64>(p, s)             \
+                              : launch_combine_t<K, 128>(p, s);
+    switch (kv) {
+        FTM_COMBINE_CASE(KV_F32)
+        FTM_COMBINE_CASE(KV_F16)
+        FTM_COMBINE_CASE(KV_BF16)
+        FTM_COMBINE_CASE(KV_I8)
+    default: return hipErrorInvalidValue;
+    }
+#undef FTM_COMBINE_CASE
+}
+
+}  // namespace ftm

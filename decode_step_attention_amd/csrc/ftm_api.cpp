@@ -1,0 +1,330 @@
+// ftm_api.cpp -- the C ABI of libftm (include/ftm.h): argument checks, the
+// split-sequence choice, the per-(device, stream) workspace, launches and
+// the optional kernel timing.  Host code only; the kernels live in
+// decode_attention.hip.
+#include "ftm.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "ftm_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+    g_last_error = msg;
+    return status;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace: one growing buffer per (device, stream).  Reused across calls
+// ([lpnh.cn/news/2765398] section 2.2: intermediate buffers are pooled and
+// recycled instead of allocated per layer).
+// ---------------------------------------------------------------------------
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[{device, stream}];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            // hipFree waits for the device, so work still using the old
+            // buffer has finished before it goes away
+            hipError_t e = hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipFree: ") + hipGetErrorString(e));
+        }
+        size_t grow = bytes + bytes / 4;
+        hipError_t e = hipMalloc(&w.ptr, grow);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            (void)hipGetLastError();
+            return fail(FTM_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(grow) +
+                                                   " bytes: " + hipGetErrorString(e));
+        }
+        w.bytes = grow;
+    }
+    *out = w.ptr;
+    return FTM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing (measurement only).
+// ---------------------------------------------------------------------------
+struct Timing {
+    bool on = false;
+    int capacity = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[2];
+    int used[2] = {0, 0};
+};
+std::mutex g_t_mutex;
+Timing g_t;
+
+void destroy_events_locked() {
+    for (int k = 0; k < 2; ++k) {
+        for (auto& pr : g_t.ev[k]) {
+            (void)hipEventDestroy(pr.first);
+            (void)hipEventDestroy(pr.second);
+        }
+        g_t.ev[k].clear();
+        g_t.used[k] = 0;
+    }
+}
+
+// Returns the event pair for the next launch of `kind`, or nulls.
+std::pair<hipEvent_t, hipEvent_t> timing_slot(int kind) {
+    std::lock_guard<std::mutex> lock(g_t_mutex);
+    if (!g_t.on || g_t.used[kind] >= (int)g_t.ev[kind].size()) return {nullptr, nullptr};
+    return g_t.ev[kind][g_t.used[kind]++];
+}
+
+std::atomic<int> g_split_chunk{0};
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    return v && *v ? std::atoi(v) : dflt;
+}
+
+// Chunk length.  Enough (sequence, KV head, head-group, chunk) workgroups
+// to give every CU several, never shorter than one streaming tile.
+int choose_chunk(int units, int step, int tile, int n_cu) {
+    int forced = g_split_chunk.load();
+    if (forced == 0) forced = env_int("FTM_SPLIT_CHUNK", 0);
+    int chunk;
+    if (forced > 0) {
+        chunk = forced;
+    } else {
+        const long target_blocks = 8L * n_cu;
+        long want_s = (target_blocks + units - 1) / units;
+        if (want_s < 1) want_s = 1;
+        chunk = (int)((step + want_s - 1) / want_s);
+        if (chunk < 2 * tile) chunk = 2 * tile;
+    }
+    chunk = (chunk + tile - 1) / tile * tile;
+    return chunk;
+}
+
+int cu_count(int device) {
+    static std::mutex m;
+    static std::map<int, int> cache;
+    std::lock_guard<std::mutex> lock(m);
+    auto it = cache.find(device);
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0)
+        n = 256;
+    cache[device] = n;
+    return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ftm_version(void) { return "libftm 0.1 (gfx950)"; }
+
+const char* ftm_last_error(void) { return g_last_error.c_str(); }
+
+size_t ftm_kv_cache_bytes(int batch, int n_kv_heads, int max_seq_len, int head_dim, int kv_dtype) {
+    if (batch < 1 || n_kv_heads < 1 || max_seq_len < 1 || head_dim < 1) return 0;
+    size_t elem;
+    switch (kv_dtype) {
+    case FTM_F32: elem = 4; break;
+    case FTM_F16:
+    case FTM_BF16: elem = 2; break;
+    case FTM_I8: elem = 1; break;
+    default: return 0;
+    }
+    const size_t rows = (size_t)batch * n_kv_heads * max_seq_len;
+    return 2 * rows * ((size_t)head_dim * elem + (kv_dtype == FTM_I8 ? 4 : 0));
+}
+
+int ftm_set_split_chunk(int positions) {
+    if (positions < 0) return -1;
+    return g_split_chunk.exchange(positions);
+}
+
+void ftm_release_workspaces(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    for (auto& kv : g_ws) {
+        if (kv.second.ptr) {
+            int cur = 0;
+            (void)hipGetDevice(&cur);
+            (void)hipSetDevice(kv.first.first);
+            (void)hipFree(kv.second.ptr);
+            (void)hipSetDevice(cur);
+        }
+    }
+    g_ws.clear();
+}
+
+int ftm_timing_enable(int capacity) {
+    if (capacity < 1) return fail(FTM_ERR_INVALID_ARG, "timing capacity must be >= 1");
+    std::lock_guard<std::mutex> lock(g_t_mutex);
+    destroy_events_locked();
+    for (int k = 0; k < 2; ++k) {
+        g_t.ev[k].reserve(capacity);
+        for (int i = 0; i < capacity; ++i) {
+            hipEvent_t a, b;
+            if (hipEventCreate(&a) != hipSuccess) return fail(FTM_ERR_HIP, "hipEventCreate failed");
+            if (hipEventCreate(&b) != hipSuccess) {
+                (void)hipEventDestroy(a);
+                return fail(FTM_ERR_HIP, "hipEventCreate failed");
+            }
+            g_t.ev[k].push_back({a, b});
+        }
+    }
+    g_t.capacity = capacity;
+    g_t.on = true;
+    return FTM_OK;
+}
+
+int ftm_timing_disable(void) {
+    std::lock_guard<std::mutex> lock(g_t_mutex);
+    g_t.on = false;
+    destroy_events_locked();
+    return FTM_OK;
+}
+
+int ftm_timing_read(int kind, int* launches, double* total_ms) {
+    if (kind < 0 || kind > 1 || !launches || !total_ms)
+        return fail(FTM_ERR_INVALID_ARG, "ftm_timing_read: bad arguments");
+    std::lock_guard<std::mutex> lock(g_t_mutex);
+    double total = 0.0;
+    const int n = g_t.used[kind];
+    for (int i = 0; i < n; ++i) {
+        auto& pr = g_t.ev[kind][i];
+        hipError_t e = hipEventSynchronize(pr.second);
+        if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, pr.first, pr.second);
+        if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipEventElapsedTime: ") + hipGetErrorString(e));
+        total += ms;
+    }
+    g_t.used[kind] = 0;
+    *launches = n;
+    *total_ms = total;
+    return FTM_OK;
+}
+
+int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                   void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
+                   int max_seq_len, int step, int n_heads, int n_kv_heads, int head_dim,
+                   int kv_dtype, float* kv_scales, void* out, void* stream_ptr) {
+    // ---- host-side checks: nothing is enqueued on failure ----
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
+        return fail(FTM_ERR_INVALID_ARG, "a required pointer (q, k_new, v_new, k_cache, v_cache, out) is NULL");
+    if (batch < 1 || max_seq_len < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
+        return fail(FTM_ERR_INVALID_ARG, "batch, max_seq_len, n_heads, n_kv_heads and head_dim must be >= 1");
+    if (n_heads % n_kv_heads != 0)
+        return fail(FTM_ERR_INVALID_ARG, "n_heads (" + std::to_string(n_heads) +
+                                             ") is not a multiple of n_kv_heads (" +
+                                             std::to_string(n_kv_heads) + ")");
+    if (step < 1 || step > max_seq_len)
+        return fail(FTM_ERR_INVALID_ARG, "step " + std::to_string(step) + " outside [1, max_seq_len=" +
+                                             std::to_string(max_seq_len) + "]");
+    if (kv_dtype < FTM_F32 || kv_dtype > FTM_I8)
+        return fail(FTM_ERR_INVALID_ARG, "unknown kv_dtype " + std::to_string(kv_dtype));
+    if ((kv_dtype == FTM_I8) != (kv_scales != nullptr))
+        return fail(FTM_ERR_INVALID_ARG, kv_dtype == FTM_I8 ? "an INT8 cache needs kv_scales"
+                                                             : "kv_scales is only for an INT8 cache");
+    {
+        const void* vec[] = {q, k_new, v_new, qkv_bias, k_cache, v_cache, out};
+        for (const void* v : vec)
+            if (((uintptr_t)v & 15u) != 0)
+                return fail(FTM_ERR_INVALID_ARG, "q, k_new, v_new, qkv_bias, k_cache, v_cache and out must be 16-byte aligned");
+        if (((uintptr_t)seq_lens & 3u) != 0 || ((uintptr_t)kv_scales & 3u) != 0)
+            return fail(FTM_ERR_INVALID_ARG, "seq_lens and kv_scales must be 4-byte aligned");
+    }
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FTM_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) + " (built: 64, 128)");
+    const int G = n_heads / n_kv_heads;
+    const int gtile = ftm::group_tile(G);
+    const int n_hg = (G + gtile - 1) / gtile;
+    if ((long)n_kv_heads * n_hg > 65535 || batch > 65535)
+        return fail(FTM_ERR_UNSUPPORTED, "grid too large: n_kv_heads * head groups and batch must be <= 65535");
+    const size_t elem = kv_dtype == FTM_F32 ? 4 : (kv_dtype == FTM_I8 ? 1 : 2);
+    if ((size_t)max_seq_len * head_dim * elem > 0x7fffffffu)
+        return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
+
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    int device = 0;
+    hipError_t he = hipGetDevice(&device);
+    if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
+
+    if (env_int("FTM_VALIDATE", 0) && seq_lens) {
+        std::vector<int32_t> h(batch);
+        he = hipMemcpyAsync(h.data(), seq_lens, sizeof(int32_t) * batch, hipMemcpyDeviceToHost, stream);
+        if (he == hipSuccess) he = hipStreamSynchronize(stream);
+        if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("FTM_VALIDATE copy: ") + hipGetErrorString(he));
+        for (int b = 0; b < batch; ++b)
+            if (h[b] < 1 || h[b] > step)
+                return fail(FTM_ERR_INVALID_ARG, "seq_lens[" + std::to_string(b) + "] = " +
+                                                     std::to_string(h[b]) + " outside [1, step]");
+    }
+
+    ftm::Params p{};
+    p.q = q;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.bias = qkv_bias;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.seq_lens = seq_lens;
+    p.kv_scales = kv_scales;
+    p.out = out;
+    p.B = batch;
+    p.Lmax = max_seq_len;
+    p.step = step;
+    p.H = n_heads;
+    p.Hkv = n_kv_heads;
+    p.G = G;
+    p.n_hg = n_hg;
+    p.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+
+    const int tile = ftm::tile_rows(kv_dtype, head_dim, gtile);
+    const int units = batch * n_kv_heads * n_hg;
+    p.chunk = choose_chunk(units, step, tile, cu_count(device));
+    p.S = (step + p.chunk - 1) / p.chunk;
+    p.direct = p.S == 1;
+    if (!p.direct) {
+        const size_t n_part = (size_t)batch * n_heads * p.S;
+        void* ws = nullptr;
+        int st = get_workspace(device, stream, n_part * (head_dim + 2) * sizeof(float), &ws);
+        if (st != FTM_OK) return st;
+        p.ws_o = (float*)ws;
+        p.ws_ml = p.ws_o + n_part * head_dim;
+    }
+
+    auto ev = timing_slot(0);
+    if (ev.first) (void)hipEventRecord(ev.first, stream);
+    he = ftm::launch_attention(p, kv_dtype, head_dim, gtile, stream);
+    if (ev.second) (void)hipEventRecord(ev.second, stream);
+    if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(he));
+    if (!p.direct) {
+        auto ev2 = timing_slot(1);
+        if (ev2.first) (void)hipEventRecord(ev2.first, stream);
+        he = ftm::launch_combine(p, kv_dtype, head_dim, stream);
+        if (ev2.second) (void)hipEventRecord(ev2.second, stream);
+        if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("combine launch: ") + hipGetErrorString(he));
+    }
+    g_last_error.clear();
+    return FTM_OK;
+}
+
+}  // extern "C"

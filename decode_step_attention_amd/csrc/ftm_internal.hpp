@@ -1,0 +1,43 @@
+// ftm_internal.hpp -- what the host dispatcher and the gfx950 kernels share:
+// the launch parameters and the launcher entry points.  Not part of the
+// public C ABI (include/ftm.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ftm {
+
+enum KvKind : int { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2, KV_I8 = 3 };
+
+// Everything one decode step needs, by value into the kernels.
+struct Params {
+    const void* q;          // [B, H, D] act
+    const void* k_new;      // [B, Hkv, D] act
+    const void* v_new;      // [B, Hkv, D] act
+    const void* bias;       // [(H + 2 Hkv) D] act or null
+    void* k_cache;          // [B, Hkv, Lmax, D] kv
+    void* v_cache;          // [B, Hkv, Lmax, D] kv
+    const int32_t* seq_lens;// [B] or null
+    float* kv_scales;       // [2, B, Hkv, Lmax] (INT8) or null
+    void* out;              // [B, H, D] act
+    float* ws_o;            // [B, H, S, D]  un-normalised partial outputs
+    float* ws_ml;           // [B, H, S, 2]  partial (max, sum), log2 domain
+    int B, Lmax, step, H, Hkv, G;
+    int n_hg;               // query-head groups per KV head (ceil(G / group tile))
+    int chunk;              // positions per split chunk (multiple of the tile)
+    int S;                  // chunks per sequence at length `step`
+    int direct;             // 1: single pass writes `out`; 0: write partials
+    float qscale;           // log2(e) / sqrt(D), folded into the query
+};
+
+// Group tile (query heads served by one pass over a KV head) for G heads.
+int group_tile(int G);
+// Positions one workgroup covers per iteration of its streaming loop.
+int tile_rows(int kv, int head_dim, int group_tile);
+
+hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, hipStream_t s);
+hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);
+
+}  // namespace ftm

@@ -1,0 +1,158 @@
+"""Python binding of libftm (include/ftm.h): argument marshalling only.
+
+Each function has the C entry point's name.  Tensors supply device pointers
+and shapes; torch supplies the current HIP stream.  Every step of the
+computation runs in the library's gfx950 kernels; there is no fallback, and
+importing this module fails loudly if the built library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libftm.so")
+
+FTM_F32, FTM_F16, FTM_BF16, FTM_I8 = 0, 1, 2, 3
+KV_DTYPES = {"f32": FTM_F32, "f16": FTM_F16, "bf16": FTM_BF16, "i8": FTM_I8}
+_TORCH_TO_KV = {torch.float32: FTM_F32, torch.float16: FTM_F16, torch.bfloat16: FTM_BF16,
+                torch.int8: FTM_I8}
+_ACT = {FTM_F32: torch.float32, FTM_F16: torch.float16, FTM_BF16: torch.bfloat16,
+        FTM_I8: torch.float16}
+
+# Every symbol include/ftm.h declares.
+EXPORTS = ("ftm_decode_mha", "ftm_kv_cache_bytes", "ftm_last_error", "ftm_version",
+           "ftm_set_split_chunk", "ftm_release_workspaces", "ftm_timing_enable",
+           "ftm_timing_disable", "ftm_timing_read")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libftm.so is not built ({LIB_PATH}); run "
+                          "`python -m decode_step_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.ftm_decode_mha.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   i32, vp, vp, vp]
+    lib.ftm_decode_mha.restype = i32
+    lib.ftm_kv_cache_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.ftm_kv_cache_bytes.restype = ctypes.c_size_t
+    lib.ftm_last_error.argtypes = []
+    lib.ftm_last_error.restype = ctypes.c_char_p
+    lib.ftm_version.argtypes = []
+    lib.ftm_version.restype = ctypes.c_char_p
+    lib.ftm_set_split_chunk.argtypes = [i32]
+    lib.ftm_set_split_chunk.restype = i32
+    lib.ftm_release_workspaces.argtypes = []
+    lib.ftm_release_workspaces.restype = None
+    lib.ftm_timing_enable.argtypes = [i32]
+    lib.ftm_timing_enable.restype = i32
+    lib.ftm_timing_disable.argtypes = []
+    lib.ftm_timing_disable.restype = i32
+    lib.ftm_timing_read.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
+    lib.ftm_timing_read.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def ftm_last_error() -> str:
+    return lib.ftm_last_error().decode()
+
+
+def ftm_version() -> str:
+    return lib.ftm_version().decode()
+
+
+def ftm_kv_cache_bytes(batch: int, n_kv_heads: int, max_seq_len: int, head_dim: int,
+                       kv_dtype: int) -> int:
+    return int(lib.ftm_kv_cache_bytes(batch, n_kv_heads, max_seq_len, head_dim, kv_dtype))
+
+
+def ftm_set_split_chunk(positions: int) -> int:
+    return int(lib.ftm_set_split_chunk(positions))
+
+
+def ftm_release_workspaces() -> None:
+    lib.ftm_release_workspaces()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise RuntimeError(f"libftm status {rc}: {ftm_last_error()}")
+
+
+def ftm_timing_enable(capacity: int) -> None:
+    _check(lib.ftm_timing_enable(capacity))
+
+
+def ftm_timing_disable() -> None:
+    _check(lib.ftm_timing_disable())
+
+
+def ftm_timing_read(kind: int) -> Tuple[int, float]:
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib.ftm_timing_read(kind, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def ftm_decode_mha_raw(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch,
+                       max_seq_len, step, n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales,
+                       out, stream) -> int:
+    """The C entry point with integer pointers, unchanged status code."""
+    return int(lib.ftm_decode_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch,
+                                  max_seq_len, step, n_heads, n_kv_heads, head_dim, kv_dtype,
+                                  kv_scales, out, stream))
+
+
+def ftm_decode_mha(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   qkv_bias: Optional[torch.Tensor], k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   seq_lens: Optional[torch.Tensor], step: int, out: torch.Tensor,
+                   kv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One decode step (see include/ftm.h).  Shapes: q/out [B, H, D],
+    k_new/v_new [B, Hkv, D], k_cache/v_cache [B, Hkv, Lmax, D],
+    qkv_bias [(H + 2 Hkv) D] or None, seq_lens int32 [B] or None,
+    kv_scales fp32 [2, B, Hkv, Lmax] for an int8 cache.  Caches and scales
+    are updated in place; out is written."""
+    if k_cache.dim() != 4 or q.dim() != 3:
+        raise ValueError("q must be [B, H, D] and k_cache [B, Hkv, Lmax, D]")
+    B, H, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    kv = _TORCH_TO_KV.get(k_cache.dtype)
+    if kv is None:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    act = _ACT[kv]
+    dev = k_cache.device
+    tensors = {"q": (q, act, (B, H, D)), "k_new": (k_new, act, (B, Hkv, D)),
+               "v_new": (v_new, act, (B, Hkv, D)), "k_cache": (k_cache, k_cache.dtype, (B, Hkv, Lmax, D)),
+               "v_cache": (v_cache, k_cache.dtype, (B, Hkv, Lmax, D)), "out": (out, act, (B, H, D))}
+    if qkv_bias is not None:
+        tensors["qkv_bias"] = (qkv_bias, act, ((H + 2 * Hkv) * D,))
+    if seq_lens is not None:
+        tensors["seq_lens"] = (seq_lens, torch.int32, (B,))
+    if kv_scales is not None:
+        tensors["kv_scales"] = (kv_scales, torch.float32, (2, B, Hkv, Lmax))
+    for name, (t, dt, shape) in tensors.items():
+        if t.dtype != dt:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {dt}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the cache on {dev}")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ftm_decode_mha(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_cache),
+                            _ptr(v_cache), _ptr(seq_lens), B, Lmax, int(step), H, Hkv, D, kv,
+                            _ptr(kv_scales), _ptr(out), ctypes.c_void_p(stream))
+    _check(rc)

@@ -1,0 +1,158 @@
+/*
+ * ftm.h -- C ABI of libftm: fused decode-step masked multi-head attention
+ * over a KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * One call performs one decode step of one attention layer for a batch of
+ * sequences.  For every sequence b and every query head h it
+ *   1. adds the QKV bias to the step's query and to its new key/value row
+ *      ([lpnh.cn/news/2765398] section 2.1: Q, K and V come out of one fused
+ *      projection, are split three ways and carry their bias);
+ *   2. appends the biased new K/V row to a pre-allocated cache
+ *      ([lpnh.cn/news/2765398] section 2.2; [intelliparadigm.com .../2131745]
+ *      section 2.1: the cache is allocated once and filled position by
+ *      position; [framerc.cn/news/4453289] section 3.2);
+ *   3. dots the single query with every cached key, scaled by 1/sqrt(D);
+ *   4. takes a softmax with the maximum subtracted
+ *      ([lpnh.cn/news/2765398] section 6.1: Q.K can leave the fp16 range
+ *      without care; [intelliparadigm.com .../2131745] section 6.2);
+ *   5. forms the softmax-weighted sum of the cached values,
+ * in fused kernels that never write a score matrix to memory
+ * ([lpnh.cn/news/2765398] section 2.1; [framerc.cn/news/4453289] section 2.2).
+ *
+ * All pointers are caller-owned device pointers unless stated otherwise.
+ * Calls only enqueue work on the given stream: they never synchronise and
+ * never read device memory on the host.  Errors are returned before anything
+ * is enqueued; the library never aborts the process.
+ */
+#ifndef FTM_H
+#define FTM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache element types ([lpnh.cn/news/2765398] section 6.1 and
+ * [intelliparadigm.com .../2131745] section 4.1: fp16/bf16 storage;
+ * [pptc.cn/news/144085] section 3.1: an INT8 KV cache). */
+typedef enum {
+    FTM_F32 = 0,
+    FTM_F16 = 1,
+    FTM_BF16 = 2,
+    FTM_I8 = 3
+} ftm_dtype;
+
+typedef enum {
+    FTM_OK = 0,
+    FTM_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent shapes   */
+    FTM_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim, head grouping  */
+    FTM_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed    */
+    FTM_ERR_OUT_OF_MEMORY = 4  /* the library's split workspace could not grow  */
+} ftm_status;
+
+/*
+ * ftm_decode_mha -- one decode step of masked multi-head attention.
+ *
+ * Shapes (row-major, contiguous, D = head_dim, G = n_heads / n_kv_heads):
+ *   q         [batch, n_heads, D]             act type, read
+ *   k_new     [batch, n_kv_heads, D]          act type, read
+ *   v_new     [batch, n_kv_heads, D]          act type, read
+ *   qkv_bias  [(n_heads + 2 n_kv_heads) D]    act type, read; [b_q | b_k | b_v],
+ *             each head-major, shared by all sequences; NULL means no bias
+ *   k_cache, v_cache [batch, n_kv_heads, max_seq_len, D]  kv_dtype, read, and
+ *             row seq_lens[b]-1 of every (b, KV head) written
+ *   seq_lens  [batch] int32 device array, or NULL (every length = step).
+ *             seq_lens[b] counts the token appended by this call: the new
+ *             row goes to position seq_lens[b]-1 and the query attends to
+ *             positions [0, seq_lens[b]).
+ *   step      the largest seq_lens[b]; 1 <= step <= max_seq_len
+ *   kv_scales [2, batch, n_kv_heads, max_seq_len] fp32, INT8 caches only
+ *             (K scales first, then V): read at positions below the new
+ *             row, written at the new row; must be NULL otherwise
+ *   out       [batch, n_heads, D]             act type, written
+ *   stream    a hipStream_t; NULL is the null stream
+ * The act type is kv_dtype for float caches and fp16 for an INT8 cache.
+ *
+ * Arithmetic: the bias add is an fp32 add; the appended row is stored
+ * rounded to nearest even (fp16/bf16), as is (fp32), or as symmetric INT8
+ * codes rint(x / s) clamped to [-127, 127] with s = absmax(row) / 127 (a
+ * zero row stores s = 0 and zero codes).  The attention reads the stored
+ * values back (INT8: code * scale), accumulates in fp32 and writes out
+ * rounded to nearest even.  Query head h uses KV head h / G
+ * ([pptc.cn/news/144085] section 3.4: heads share K/V in groups).
+ *
+ * Supported: head_dim 64 or 128; any n_heads that is a multiple of
+ * n_kv_heads.  Up to 8 query heads of a group are served by one pass over
+ * the group's K/V; larger groups take one pass per 8 heads.
+ *
+ * Alignment: q, k_new, v_new, qkv_bias, k_cache, v_cache and out 16 bytes
+ * (every row of D elements then starts on a 16-byte boundary); seq_lens and
+ * kv_scales 4 bytes.
+ *
+ * Errors (nothing is enqueued): FTM_ERR_INVALID_ARG for a null required
+ * pointer, a misaligned pointer, non-positive sizes, n_heads % n_kv_heads != 0, step outside
+ * [1, max_seq_len], an unknown kv_dtype, or kv_scales given/missing against
+ * the cache type; FTM_ERR_UNSUPPORTED for another head_dim;
+ * FTM_ERR_OUT_OF_MEMORY if the internal workspace cannot grow;
+ * FTM_ERR_HIP if a launch fails.  ftm_last_error() tells which.
+ * A sequence whose device-side length lies outside [1, step] is not
+ * appended and gets NaN output rows (no host synchronisation is needed to
+ * see the error).
+ *
+ * Ownership: the library never frees or keeps caller pointers.  It owns one
+ * split-sequence workspace per (device, stream), grown on the first call
+ * that needs more and reused afterwards.  out must not alias any input.
+ * Calls on different streams may run concurrently; calls that share a cache
+ * row on different streams race, as any two writers would.
+ */
+int ftm_decode_mha(const void* q, const void* k_new, const void* v_new,
+                   const void* qkv_bias, void* k_cache, void* v_cache,
+                   const int32_t* seq_lens, int batch, int max_seq_len, int step,
+                   int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
+                   float* kv_scales, void* out, void* stream);
+
+/* Bytes of one layer's K and V cache (plus INT8 scales) for the layout
+ * above: 2 * batch * n_kv_heads * max_seq_len * (head_dim * elem + scale),
+ * scale = 4 bytes for INT8, 0 otherwise.  Sizing as in
+ * [pptc.cn/news/144085] section 3.1 (batch x length x layers x hidden x
+ * bytes, counted for K and V).  Returns 0 for invalid arguments. */
+size_t ftm_kv_cache_bytes(int batch, int n_kv_heads, int max_seq_len, int head_dim,
+                          int kv_dtype);
+
+/* Message for the last failed call on this host thread ("" if none).
+ * Owned by the library; valid until the next call on this thread. */
+const char* ftm_last_error(void);
+
+/* Library version string, owned by the library. */
+const char* ftm_version(void);
+
+/* Chunk length, in positions, of the split-sequence pass (flash-decoding:
+ * independent partial softmax states per chunk, merged by a combine
+ * kernel; [pptc.cn/news/144085] section 2.2 on running softmax statistics).
+ * 0 restores the automatic choice.  Values are rounded up to the kernel's
+ * tile; a chunk of max_seq_len or more forces the single-pass kernel.
+ * Process-wide; returns the previous setting, or -1 for a negative value. */
+int ftm_set_split_chunk(int positions);
+
+/* Frees every workspace the library holds (all devices and streams).  The
+ * caller must make sure no call of this library is still running. */
+void ftm_release_workspaces(void);
+
+/* ---- kernel timing -------------------------------------------------------
+ * For measurement only.  While enabled, every ftm_decode_mha call records a
+ * HIP event pair around each kernel it launches, on the call's stream.
+ * ftm_timing_read() waits for the recorded events, returns the number of
+ * launches and their summed duration in milliseconds for one kernel kind
+ * and clears that kind's records.  Kinds: 0 = attention pass (split or
+ * single-pass), 1 = combine.  At most `capacity` launches are kept per
+ * kind; later ones are not recorded.  Returns FTM_OK or an error. */
+int ftm_timing_enable(int capacity);
+int ftm_timing_disable(void);
+int ftm_timing_read(int kind, int* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FTM_H */

@@ -1,0 +1,322 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bar: the appended cache rows (and INT8 scales) are bit-exact and every other
+byte of the caches is unchanged; out is within max-abs 1e-5 / row-rel 1e-5
+for an fp32 cache and max-abs 2e-3 / row-rel 1e-2 for fp16, bf16 and INT8
+caches (fp32 accumulation).  Row-rel is max_d |err| / max_d |ref| per
+(b, h) row, the normwise form (outputs near zero make an elementwise
+relative error meaningless).  Cosine similarity is reported and must stay
+above 0.99 as a diagnostic."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_step_attention_amd import workloads as W
+from tests.helpers import errors, inputs_to_np, out_to_f64, run_oracle, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2), "i8": (2e-3, 1e-2)}
+
+
+@pytest.fixture(scope="module")
+def ftm():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from decode_step_attention_amd import ftm as m
+    yield m
+    m.ftm_set_split_chunk(0)
+
+
+def gpu_call(ftm, inp, case, with_bias=True, with_lens=True, stream=None):
+    out = torch.empty((case.batch, case.n_heads, case.head_dim), dtype=W.TORCH_DTYPES[case.act_dtype],
+                      device=inp["q"].device)
+    ftm.ftm_decode_mha(inp["q"], inp["k_new"], inp["v_new"], inp["bias"] if with_bias else None,
+                       inp["k_cache"], inp["v_cache"], inp["seq_lens"] if with_lens else None,
+                       inp["step"], out, inp.get("kv_scales"), stream=stream)
+    return out
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    """Bit pattern view, so that equality is bitwise (signed zeros, NaNs)."""
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()])
+
+
+def check(case, out, ref, tag="", tol=None):
+    atol, rtol = tol or TOL[case.kv_dtype]
+    got = out if isinstance(out, np.ndarray) else out_to_f64(out)
+    finite = np.isfinite(ref).all(axis=-1)
+    assert np.array_equal(np.isfinite(got).all(axis=-1), finite), f"{tag}: NaN rows differ"
+    a, r, cos = errors(got[finite], ref[finite]) if finite.any() else (0, 0, 1)
+    print(f"[{tag}] max_abs={a:.3e} row_rel={r:.3e} min_cos={cos:.6f}", flush=True)
+    assert a <= atol, f"{tag}: max abs err {a}"
+    assert r <= rtol, f"{tag}: max row-rel err {r}"
+    assert cos > 0.99, f"{tag}: cosine {cos}"
+
+
+def run_and_compare(ftm, case, chunk=0, device="cuda", poison=True, with_bias=True,
+                    with_lens=True, lens=None, mutate=None, tag="", tol=None):
+    """Full comparison at a size the oracle finishes quickly."""
+    inp = W.make_inputs(case, "cpu", poison=poison, lens=lens)
+    if mutate:
+        mutate(inp)
+    npi = inputs_to_np(inp, case.kv_dtype)
+    if not with_bias:
+        npi["bias"] = None
+    if not with_lens:
+        npi["seq_lens"] = None
+    ref_out, _ = run_oracle(oracle, case, npi, n_threads=8)
+    g = {k: (v.to(device) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    ftm.ftm_set_split_chunk(chunk)
+    try:
+        out = gpu_call(ftm, g, case, with_bias, with_lens)
+        torch.cuda.synchronize()
+    finally:
+        ftm.ftm_set_split_chunk(0)
+    # caches: every byte equals the oracle's (appended rows bit-exact, the
+    # rest untouched); NaN-poisoned rows compare as bytes too
+    assert to_np(g["k_cache"], case.kv_dtype).tobytes() == npi["k_cache"].tobytes(), f"{tag}: k_cache"
+    assert to_np(g["v_cache"], case.kv_dtype).tobytes() == npi["v_cache"].tobytes(), f"{tag}: v_cache"
+    if case.kv_dtype == "i8":
+        assert to_np(g["kv_scales"], "f32").tobytes() == npi["kv_scales"].tobytes(), f"{tag}: scales"
+    check(case, out, ref_out, tag, tol)
+    return out, ref_out
+
+
+def small(kv, D=128, B=3, H=8, Hkv=4, Lmax=1100, lens=(1, 1033), seed=7):
+    scale = 1.0 if kv == "i8" else 1 / np.sqrt(D)
+    return W.Case("p", B, H, Hkv, D, kv, ctx=Lmax, max_seq_len=Lmax, value_scale=scale,
+                  lens=lens, seed=seed)
+
+
+# ---- dtype x head_dim x grouping, ragged lengths, several tiles ----------
+GRID = [(kv, D, H, Hkv) for kv in ("f32", "f16", "bf16", "i8") for D in (64, 128)
+        for (H, Hkv) in ((4, 4), (8, 4), (8, 2), (8, 1))]
+
+
+@pytest.mark.parametrize("kv,D,H,Hkv", GRID)
+def test_parity_grid(ftm, kv, D, H, Hkv):
+    case = small(kv, D=D, H=H, Hkv=Hkv, seed=11 + D + H * 3 + Hkv)
+    run_and_compare(ftm, case, tag=f"{kv} D{D} H{H}/{Hkv}")
+
+
+@pytest.mark.parametrize("G", [3, 5, 12, 16])
+def test_parity_odd_and_large_groups(ftm, G):
+    """Group sizes that are not a power of two, and groups above 8 heads
+    (served by several passes)."""
+    case = small("f16", H=2 * G, Hkv=2, B=2, seed=40 + G)
+    run_and_compare(ftm, case, tag=f"G{G}")
+
+
+@pytest.mark.parametrize("chunk", [1, 128, 256, 384, 1024, 4096])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8"])
+def test_split_count_invariance(ftm, kv, chunk):
+    """Every chunk length (one tile up to a single pass) matches the oracle,
+    and the outputs of different splittings agree to fp32 rounding."""
+    case = small(kv, B=2, H=4, Hkv=2, Lmax=1500, lens=(900, 1500), seed=3)
+    run_and_compare(ftm, case, chunk=chunk, tag=f"{kv} chunk{chunk}")
+
+
+def test_split_outputs_agree_with_each_other(ftm):
+    case = small("f32", B=2, H=4, Hkv=2, Lmax=2000, lens=(1900, 2000), seed=4)
+    outs = []
+    for chunk in (128, 512, 4096):
+        o, _ = run_and_compare(ftm, case, chunk=chunk, tag=f"agree chunk{chunk}")
+        outs.append(out_to_f64(o))
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 2e-6
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16", "bf16"])
+def test_single_position_output_is_the_appended_v(ftm, kv):
+    """t = 1: the only weight is exactly 1, so out equals the stored new V
+    row bit for bit when the output type equals the cache type."""
+    case = small(kv, B=4, H=8, Hkv=4, Lmax=16, lens=(1, 1), seed=9)
+    inp = W.make_inputs(case, "cpu")
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    out = gpu_call(ftm, g, case)
+    torch.cuda.synchronize()
+    G = case.group
+    v_rows = g["v_cache"][:, :, 0, :]                        # [B, Hkv, D]
+    expect = v_rows.repeat_interleave(G, dim=1)               # query head h -> KV head h // G
+    assert torch.equal(bits(out), bits(expect.contiguous()))
+
+
+def test_single_position_int8(ftm):
+    case = small("i8", B=2, H=4, Hkv=2, Lmax=8, lens=(1, 1), seed=10)
+    run_and_compare(ftm, case, tag="i8 t=1")
+
+
+def test_identical_keys_give_mean_of_v(ftm):
+    case = small("f32", B=2, H=4, Hkv=2, Lmax=700, lens=(650, 700), seed=12)
+
+    def same_keys(inp):
+        key = torch.linspace(-1, 1, case.head_dim)
+        inp["k_cache"][:] = key
+        inp["k_new"][:] = key
+        H, Hkv, D = case.n_heads, case.n_kv_heads, case.head_dim
+        inp["bias"][H * D:(H + Hkv) * D] = 0
+    out, ref = run_and_compare(ftm, case, poison=False, mutate=same_keys, tag="same keys")
+    # equal weights: out is the plain mean of the V rows (oracle's cache
+    # after the append, widened to double)
+    inp = W.make_inputs(case, "cpu", poison=False)
+    same_keys(inp)
+    npi = inputs_to_np(inp, case.kv_dtype)
+    run_oracle(oracle, case, npi)
+    got = out_to_f64(out)
+    for b in range(case.batch):
+        L = int(npi["seq_lens"][b])
+        for h in range(case.n_heads):
+            mean = npi["v_cache"][b, h // case.group, :L].astype(np.float64).mean(axis=0)
+            np.testing.assert_allclose(got[b, h], mean, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+def test_large_scores_stay_stable(ftm, kv):
+    """Keys sharing a large component put every score near 100, where exp()
+    overflows fp32: the softmax must subtract the running maximum.  fp16 is
+    held to the usual bar.  For fp32 each score carries a relative rounding
+    of 2^-24 of its size (about 1e-5 at 144 in the log2 domain), which moves
+    the weights by that much, so the fp32 bar here is 1e-4."""
+    case = small(kv, B=2, H=4, Hkv=2, D=64, Lmax=900, lens=(800, 900), seed=13)
+
+    def big(inp):
+        inp["k_cache"][..., 0] += 100.0
+        inp["k_new"][..., 0] += 100.0
+        inp["q"][..., 0] = 8.0
+    run_and_compare(ftm, case, poison=True, mutate=big, tag=f"large scores {kv}",
+                    tol=(1e-4, 1e-4) if kv == "f32" else None)
+
+
+def test_no_bias_and_no_lengths(ftm):
+    case = small("f16", B=3, H=8, Hkv=4, Lmax=600, lens=None, seed=14).with_(ctx=600)
+    run_and_compare(ftm, case, with_bias=False, with_lens=False, tag="no bias, no lens")
+
+
+def test_invalid_lengths_give_nan_rows_and_no_append(ftm):
+    case = small("bf16", B=4, H=4, Hkv=2, Lmax=600, lens=(300, 500), seed=15)
+    lens = W.seq_lens(case).clone()
+    lens[1] = 0
+    lens[3] = int(lens.max()) + 7           # above `step` once step is the valid max
+    inp = W.make_inputs(case, "cpu", lens=lens)
+    inp["step"] = int(max(lens[0], lens[2]))
+    npi = inputs_to_np(inp, case.kv_dtype)
+    ref, _ = run_oracle(oracle, case, npi)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    for chunk in (0, 128):
+        ftm.ftm_set_split_chunk(chunk)
+        out = gpu_call(ftm, g, case)
+        torch.cuda.synchronize()
+        ftm.ftm_set_split_chunk(0)
+        o = out_to_f64(out)
+        assert np.isnan(o[1]).all() and np.isnan(o[3]).all()
+        check(case, out, ref, f"invalid lens chunk{chunk}")
+    assert to_np(g["k_cache"], "bf16").tobytes() == npi["k_cache"].tobytes()
+    assert to_np(g["v_cache"], "bf16").tobytes() == npi["v_cache"].tobytes()
+
+
+def test_deterministic(ftm):
+    case = small("f16", B=2, H=8, Hkv=2, Lmax=2048, lens=(1500, 2048), seed=16)
+    inp = W.make_inputs(case, "cuda")
+    a = gpu_call(ftm, inp, case)
+    b = gpu_call(ftm, inp, case)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_side_stream(ftm):
+    case = small("f16", B=2, H=4, Hkv=4, Lmax=800, seed=17)
+    inp = W.make_inputs(case, "cpu")
+    npi = inputs_to_np(inp, case.kv_dtype)
+    ref, _ = run_oracle(oracle, case, npi)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = gpu_call(ftm, g, case)
+    s.synchronize()
+    check(case, out, ref, "side stream")
+
+
+# ---- full-size workloads, sampled against the oracle ----------------------
+def sub_problem(case, host, b, j):
+    """Inputs of one (sequence, KV head) unit as a B=1, Hkv=1 problem."""
+    G, D, H, Hkv = case.group, case.head_dim, case.n_heads, case.n_kv_heads
+    bias = host["bias"]
+    sub_bias = np.concatenate([bias[j * G * D:(j + 1) * G * D],
+                               bias[(H + j) * D:(H + j + 1) * D],
+                               bias[(H + Hkv + j) * D:(H + Hkv + j + 1) * D]])
+    L = int(host["seq_lens"][b])
+    sub = {"q": host["q"][b:b + 1, j * G:(j + 1) * G].copy(),
+           "k_new": host["k_new"][b:b + 1, j:j + 1].copy(),
+           "v_new": host["v_new"][b:b + 1, j:j + 1].copy(),
+           "bias": sub_bias.copy(),
+           "k_cache": host["k_slab"][(b, j)].copy(), "v_cache": host["v_slab"][(b, j)].copy(),
+           "seq_lens": np.array([L], np.int32), "step": L,
+           "kv_scales": host["s_slab"][(b, j)].copy() if case.kv_dtype == "i8" else None}
+    return sub, case.with_(batch=1, n_heads=G, n_kv_heads=1)
+
+
+@pytest.mark.parametrize("name", ["tiny", "7b", "sizing32", "gqa", "int8"])
+def test_full_size_workload(ftm, name):
+    """The five workloads at full size, in the launch configuration the
+    benchmark times (automatic split).  Appended rows of every (b, j) are
+    checked bytewise, the rest of the caches must be unchanged, and sampled
+    (b, j) units are recomputed by the oracle."""
+    import oracle
+    case = W.CASES[name]
+    print(f"[full {name}] generating", flush=True)
+    inp = W.make_inputs(case, "cuda", poison=False)
+    kvd, act = case.kv_dtype, case.act_dtype
+    B, Hkv = case.batch, case.n_kv_heads
+    rng = np.random.default_rng(case.seed)
+    units = sorted({(int(b), int(j)) for b, j in zip(rng.integers(0, B, 6), rng.integers(0, Hkv, 6))}
+                   | {(0, 0), (B - 1, Hkv - 1)})
+    host = {k: to_np(inp[k], act) for k in ("q", "k_new", "v_new", "bias")}
+    host["seq_lens"] = inp["seq_lens"].cpu().numpy().astype(np.int32)
+    host["k_slab"] = {u: to_np(inp["k_cache"][u[0]:u[0] + 1, u[1]:u[1] + 1], kvd) for u in units}
+    host["v_slab"] = {u: to_np(inp["v_cache"][u[0]:u[0] + 1, u[1]:u[1] + 1], kvd) for u in units}
+    if kvd == "i8":
+        host["s_slab"] = {u: to_np(inp["kv_scales"][:, u[0]:u[0] + 1, u[1]:u[1] + 1], "f32")
+                          for u in units}
+    k_before = inp["k_cache"].clone()
+    v_before = inp["v_cache"].clone()
+    s_before = inp["kv_scales"].clone() if kvd == "i8" else None
+    print(f"[full {name}] running", flush=True)
+    out = gpu_call(ftm, inp, case)
+    torch.cuda.synchronize()
+    # expected appended rows for every (b, j): the oracle on a one-slot cache
+    one = case.with_(max_seq_len=1)
+    tiny_k = np.zeros((B, Hkv, 1, case.head_dim), dtype=host["k_slab"][units[0]].dtype)
+    tiny_v = tiny_k.copy()
+    tiny_s = np.zeros((2, B, Hkv, 1), np.float32) if kvd == "i8" else None
+    oracle.decode_mha(host["q"], host["k_new"], host["v_new"], host["bias"], tiny_k, tiny_v,
+                      np.ones(B, np.int32), 1, case.n_heads, Hkv, case.head_dim, kvd, tiny_s,
+                      n_threads=8)
+    pos = torch.as_tensor(host["seq_lens"] - 1, device="cuda").long()
+    bi = torch.arange(B, device="cuda")
+    got_k = inp["k_cache"][bi, :, pos]            # [B, Hkv, D]
+    got_v = inp["v_cache"][bi, :, pos]
+    assert to_np(got_k, kvd).tobytes() == tiny_k[:, :, 0].tobytes(), "appended K rows"
+    assert to_np(got_v, kvd).tobytes() == tiny_v[:, :, 0].tobytes(), "appended V rows"
+    k_before[bi, :, pos] = got_k
+    v_before[bi, :, pos] = got_v
+    assert torch.equal(bits(k_before), bits(inp["k_cache"])), "other K rows changed"
+    assert torch.equal(bits(v_before), bits(inp["v_cache"])), "other V rows changed"
+    if kvd == "i8":
+        got_s = inp["kv_scales"][:, bi, :, pos]    # [2, B, Hkv]
+        assert got_s.cpu().numpy().tobytes() == tiny_s[:, :, :, 0].tobytes(), "appended scales"
+        s_before[:, bi, :, pos] = got_s
+        assert torch.equal(bits(s_before), bits(inp["kv_scales"])), "other scales changed"
+    del k_before, v_before
+    out_h = out_to_f64(out)
+    for (b, j) in units:
+        sub, sc = sub_problem(case, host, b, j)
+        ref, _ = oracle.decode_mha(sub["q"], sub["k_new"], sub["v_new"], sub["bias"],
+                                   sub["k_cache"], sub["v_cache"], sub["seq_lens"], sub["step"],
+                                   sc.n_heads, 1, sc.head_dim, kvd, sub["kv_scales"])
+        G = case.group
+        check(case, out_h[b:b + 1, j * G:(j + 1) * G], ref,
+              f"full {name} b{b} j{j} L{int(host['seq_lens'][b])}")

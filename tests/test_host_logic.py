@@ -1,0 +1,112 @@
+"""Host-side logic of libftm, runnable without a GPU: the library loads and
+exports every symbol of include/ftm.h, argument errors are reported before
+anything touches the device, and the cache sizing matches the pages'
+worked examples (tests/golden/kv_cache_sizing.json)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from decode_step_attention_amd import ftm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "ftm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ftm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_exactly_the_binding_exports():
+    assert header_functions() == sorted(ftm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ftm.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in ftm.ftm_version()
+
+
+def test_kv_cache_bytes_pages_examples():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "kv_cache_sizing.json")))
+    ex1, ex2 = g["examples"]
+    per_layer = ftm.ftm_kv_cache_bytes(ex1["batch"], ex1["n_kv_heads"], ex1["context"],
+                                       ex1["head_dim"], ftm.FTM_F16)
+    assert per_layer * ex1["layers"] == ex1["expected_kv_bytes_all_layers"]
+    # the page's own product is one of K and V
+    assert per_layer * ex1["layers"] == 2 * ex1["page_product_bytes"]
+    # "about 32 GB": 32 GiB is 34.4 GB, within the page's rounding
+    assert abs(per_layer * ex1["layers"] / 2 ** 30 - 32) < 1e-9
+    one_tok = ftm.ftm_kv_cache_bytes(1, ex2["n_kv_heads"], 1, ex2["head_dim"], ftm.FTM_F16)
+    assert one_tok // 2 * ex2["layers"] == ex2["expected_k_only_per_token_all_layers"]
+    assert one_tok // 2 * ex2["layers"] == ex2["page_per_token_bytes"]
+    assert one_tok // 2 * ex2["layers"] * ex2["context"] == ex2["expected_k_only_per_request"]
+
+
+def test_kv_cache_bytes_dtypes_and_invalid():
+    assert ftm.ftm_kv_cache_bytes(2, 3, 5, 64, ftm.FTM_F32) == 2 * 2 * 3 * 5 * 64 * 4
+    assert ftm.ftm_kv_cache_bytes(2, 3, 5, 64, ftm.FTM_BF16) == 2 * 2 * 3 * 5 * 64 * 2
+    assert ftm.ftm_kv_cache_bytes(2, 3, 5, 128, ftm.FTM_I8) == 2 * 2 * 3 * 5 * (128 + 4)
+    assert ftm.ftm_kv_cache_bytes(0, 3, 5, 64, ftm.FTM_F16) == 0
+    assert ftm.ftm_kv_cache_bytes(1, 1, 1, 64, 9) == 0
+
+
+A = 0x10000  # a 16-byte aligned fake device address; never dereferenced
+
+
+def call(**kw):
+    args = dict(q=A, k_new=A, v_new=A, qkv_bias=A, k_cache=A, v_cache=A, seq_lens=A, batch=2,
+                max_seq_len=16, step=8, n_heads=4, n_kv_heads=2, head_dim=128,
+                kv_dtype=ftm.FTM_F16, kv_scales=None, out=A, stream=None)
+    args.update(kw)
+    rc = ftm.ftm_decode_mha_raw(**args)
+    return rc, ftm.ftm_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "NULL"),
+    (dict(out=None), 1, "NULL"),
+    (dict(k_cache=None), 1, "NULL"),
+    (dict(batch=0), 1, ">= 1"),
+    (dict(n_heads=5), 1, "multiple"),
+    (dict(step=0), 1, "step"),
+    (dict(step=17), 1, "step"),
+    (dict(kv_dtype=7), 1, "kv_dtype"),
+    (dict(kv_dtype=ftm.FTM_I8), 1, "kv_scales"),
+    (dict(kv_scales=A), 1, "kv_scales"),
+    (dict(q=A + 2), 1, "aligned"),
+    (dict(k_cache=A + 8), 1, "aligned"),
+    (dict(seq_lens=A + 2), 1, "aligned"),
+    (dict(head_dim=96), 2, "head_dim"),
+    (dict(head_dim=256), 2, "head_dim"),
+])
+def test_argument_errors_return_before_any_device_call(kw, status, needle):
+    rc, msg = call(**kw)
+    assert rc == status
+    assert needle in msg
+
+
+def test_split_chunk_setting_roundtrip():
+    prev = ftm.ftm_set_split_chunk(512)
+    assert ftm.ftm_set_split_chunk(prev) == 512
+    assert ftm.ftm_set_split_chunk(-1) == -1
+
+
+def test_binding_rejects_mismatched_tensors():
+    import torch
+    q = torch.zeros(2, 4, 128, dtype=torch.float16)
+    kc = torch.zeros(2, 2, 16, 128, dtype=torch.float16)
+    kn = torch.zeros(2, 2, 128, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        ftm.ftm_decode_mha(q.float(), kn, kn, None, kc, kc, None, 8, q)
+    with pytest.raises(ValueError):
+        ftm.ftm_decode_mha(q, kn[:, :1], kn, None, kc, kc, None, 8, q)
+    with pytest.raises(ValueError):
+        ftm.ftm_decode_mha(q, kn, kn, None, kc, kc.transpose(2, 3), None, 8, q)
