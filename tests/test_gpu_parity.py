@@ -227,7 +227,7 @@ def test_deterministic(ftm):
 
 
 def test_side_stream(ftm):
-    case = small("f16", B=2, H=4, Hkv=4, Lmax=800, seed=17)
+    case = small("f16", B=2, H=4, Hkv=4, Lmax=800, lens=(1, 800), seed=17)
     inp = W.make_inputs(case, "cpu")
     npi = inputs_to_np(inp, case.kv_dtype)
     ref, _ = run_oracle(oracle, case, npi)
@@ -306,9 +306,12 @@ def test_full_size_workload(ftm, name):
     assert torch.equal(bits(k_before), bits(inp["k_cache"])), "other K rows changed"
     assert torch.equal(bits(v_before), bits(inp["v_cache"])), "other V rows changed"
     if kvd == "i8":
-        got_s = inp["kv_scales"][:, bi, :, pos]    # [2, B, Hkv]
+        # (index each plane separately: non-adjacent index tensors would move
+        # the batch axis first)
+        got_s = torch.stack([inp["kv_scales"][w][bi, :, pos] for w in range(2)])   # [2, B, Hkv]
         assert got_s.cpu().numpy().tobytes() == tiny_s[:, :, :, 0].tobytes(), "appended scales"
-        s_before[:, bi, :, pos] = got_s
+        for w in range(2):
+            s_before[w][bi, :, pos] = got_s[w]
         assert torch.equal(bits(s_before), bits(inp["kv_scales"])), "other scales changed"
     del k_before, v_before
     out_h = out_to_f64(out)
