@@ -29,7 +29,7 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                 // waves per combine workgroup
 constexpr int kThreads = 64 * kWaves;
 // Buffer descriptor word 3 for raw (untyped) buffer access on the gfx9 family.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -251,24 +251,33 @@ __device__ __forceinline__ void make_new_row(const Params& p, const void* src, i
 
 // ---------------------------------------------------------------------------
 // Attention pass.  Template: cache type, head dim, query heads per pass (GT),
-// 16-byte loads per lane per K/V stream per iteration (U).
+// 16-byte loads per lane per K/V stream per iteration (U), waves per
+// workgroup (NW).
+//
+// Each wave streams its own rows with a software pipeline at half-iteration
+// granularity: while the softmax and P.V of iteration i run, the K loads of
+// iteration i+1 are already in flight, and the V loads of i+1 go out as soon
+// as P.V of i has consumed its registers.  Loads past the valid range are
+// clipped by the buffer descriptor (they return zeros and fetch nothing), so
+// the prefetch after the last iteration costs issue slots only.
 // ---------------------------------------------------------------------------
-template <int KV, int D, int GT, int U>
-__global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
+template <int KV, int D, int GT, int U, int NW>
+__global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
     using E = Elem<KV>;
     using A = Act<KV>;
+    constexpr int NT = 64 * NW;
     constexpr int EPL = 16 / E::bytes;      // elements per lane per load
     constexpr int LPR = D / EPL;            // lanes per cache row
     constexpr int RPI = 64 / LPR;           // rows per wave-wide load
     constexpr int ROW_BYTES = D * E::bytes;
     constexpr int WAVE_ROWS = RPI * U;      // rows per wave per iteration
-    constexpr int BLOCK_ROWS = kWaves * WAVE_ROWS;
+    constexpr int BLOCK_ROWS = NW * WAVE_ROWS;
     constexpr bool I8 = KV == KV_I8;
     static_assert(LPR >= 4 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "row must span 4..32 lanes");
 
-    __shared__ float sm_m[kWaves][GT];
-    __shared__ float sm_l[kWaves][GT];
-    __shared__ float sm_o[kWaves][GT][D];
+    __shared__ float sm_m[NW][GT];
+    __shared__ float sm_l[NW][GT];
+    __shared__ float sm_o[NW][GT][D];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -286,7 +295,7 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
 
     if (L < 1 || L > p.step) {              // invalid length: NaN rows, no append
         if (p.direct && chunk == 0)
-            for (int idx = threadIdx.x; idx < GT * D; idx += kThreads)
+            for (int idx = threadIdx.x; idx < GT * D; idx += NT)
                 if (idx / D < heads_here)
                     A::st(p.out, ((size_t)b * p.H + h0 + idx / D) * D + idx % D, __builtin_nanf(""));
         return;
@@ -298,9 +307,48 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
     const int stream_end = min(c1, L - 1);  // the new row L-1 comes from registers
     const bool owns_new = c1 == L;
 
+    const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;   // row 0 of this (b, j)
+    const char* kbase = (const char*)p.k_cache + row0 * ROW_BYTES;
+    const char* vbase = (const char*)p.v_cache + row0 * ROW_BYTES;
+    const uint32_t valid_bytes = (uint32_t)max(stream_end, 0) * ROW_BYTES;
+    const auto krs = make_rsrc(kbase, valid_bytes);
+    const auto vrs = make_rsrc(vbase, valid_bytes);
+    const size_t plane = (size_t)p.B * p.Hkv * p.Lmax;       // INT8 scale plane
+    const auto ksrs = make_rsrc(I8 ? p.kv_scales + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
+    const auto vsrs = make_rsrc(I8 ? p.kv_scales + plane + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
+
+    u32x4 kr[U], vr[U];
+    float ksc[U], vsc[U];
+    auto issue_k = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, 0);
+        if constexpr (I8) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                ksc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (base + u * RPI + r) * 4, 0, 0));
+        }
+    };
+    auto issue_v = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, 0);
+        if constexpr (I8) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                vsc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, (base + u * RPI + r) * 4, 0, 0));
+        }
+    };
+
+    // the first K/V loads go out before the query is read, so their latency
+    // and the query's overlap
+    int base = c0 + wave * WAVE_ROWS;
+    issue_k(base);
+    issue_v(base);
+    __builtin_amdgcn_sched_barrier(0);
+
     // query with bias, in fp32, pre-scaled by log2(e)/sqrt(D) so the softmax
-    // runs on exp2
-    // (heads past the group read a valid row and are zeroed)
+    // runs on exp2 (heads past the group read a valid row and are zeroed)
     float qv[GT][EPL];
 #pragma unroll
     for (int g = 0; g < GT; ++g)
@@ -319,16 +367,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qv[g][e] = g < heads_here ? qv[g][e] * p.qscale : 0.0f;
 
-    const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;   // row 0 of this (b, j)
-    const char* kbase = (const char*)p.k_cache + row0 * ROW_BYTES;
-    const char* vbase = (const char*)p.v_cache + row0 * ROW_BYTES;
-    const uint32_t valid_bytes = (uint32_t)max(stream_end, 0) * ROW_BYTES;
-    const auto krs = make_rsrc(kbase, valid_bytes);
-    const auto vrs = make_rsrc(vbase, valid_bytes);
-    const size_t plane = (size_t)p.B * p.Hkv * p.Lmax;       // INT8 scale plane
-    const auto ksrs = make_rsrc(I8 ? p.kv_scales + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
-    const auto vsrs = make_rsrc(I8 ? p.kv_scales + plane + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
-
     float m[GT], l[GT], o[GT][EPL];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
@@ -338,27 +376,8 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
         for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
     }
 
-    for (int base = c0 + wave * WAVE_ROWS; base < stream_end; base += BLOCK_ROWS) {
-        u32x4 kr[U], vr[U];
-        float ksc[U], vsc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, 0);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, 0);
-        if constexpr (I8) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                ksc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (base + u * RPI + r) * 4, 0, 0));
-                vsc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, (base + u * RPI + r) * 4, 0, 0));
-            }
-        }
-        // keep every load of this iteration in flight before any math: the
-        // scheduler would otherwise interleave load/wait/use and leave one
-        // 16-byte request per wave outstanding
-        __builtin_amdgcn_sched_barrier(0);
-        // scores (log2 domain)
+    for (; base < stream_end; base += BLOCK_ROWS) {
+        // scores (log2 domain) from this iteration's K
         float s[GT][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -375,6 +394,10 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
                 s[g][u] = valid ? d : kNegInf;
             }
         }
+        // K registers are free: next iteration's K goes out now
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(base + BLOCK_ROWS);
+        __builtin_amdgcn_sched_barrier(0);
         // online softmax: new running max, rescale, weights
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
@@ -407,6 +430,9 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
                 for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(w, x[e], o[g][e]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(base + BLOCK_ROWS);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // append the new row and add it to the softmax of row slot 0 of wave 0
@@ -478,17 +504,17 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const Params p) {
     __syncthreads();
 
     // merge the waves and write
-    for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < GT * D; idx += NT) {
         const int g = idx / D;
         const int d = idx - g * D;
         if (g >= heads_here) continue;
         float M = sm_m[0][g];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
         const float ms = M == kNegInf ? 0.0f : M;
         float lsum = 0.0f, acc = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float a = fast_exp2(sm_m[w][g] - ms);
             lsum += a * sm_l[w][g];
             acc += a * sm_o[w][g][d];
@@ -546,30 +572,41 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const Params p) {
 }
 
 constexpr int unroll_for(int gt) { return gt <= 2 ? 8 : 4; }
+// 16-wave workgroups cap a wave at 128 registers; only the one-head passes
+// of the fp32/fp16/bf16 caches fit without spilling.
+constexpr bool wide_built(int kv, int gt) { return gt == 1 && kv != KV_I8; }
 
 template <int KV, int D, int GT>
-hipError_t launch_attention_t(const Params& p, hipStream_t s) {
+hipError_t launch_attention_t(const Params& p, int nw, hipStream_t s) {
     dim3 grid(p.S, p.Hkv * p.n_hg, p.B);
-    hipLaunchKernelGGL((attention_kernel<KV, D, GT, unroll_for(GT)>), grid, dim3(kThreads), 0, s, p);
+    constexpr int U = unroll_for(GT);
+    if constexpr (wide_built(KV, GT)) {
+        if (nw == 16) {
+            hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 16>), grid, dim3(64 * 16), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    if (nw != 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 4>), grid, dim3(64 * 4), 0, s, p);
     return hipGetLastError();
 }
 
 template <int KV, int D>
-hipError_t dispatch_gt(const Params& p, int gt, hipStream_t s) {
+hipError_t dispatch_gt(const Params& p, int gt, int nw, hipStream_t s) {
     switch (gt) {
-    case 1: return launch_attention_t<KV, D, 1>(p, s);
-    case 2: return launch_attention_t<KV, D, 2>(p, s);
-    case 4: return launch_attention_t<KV, D, 4>(p, s);
-    case 8: return launch_attention_t<KV, D, 8>(p, s);
+    case 1: return launch_attention_t<KV, D, 1>(p, nw, s);
+    case 2: return launch_attention_t<KV, D, 2>(p, nw, s);
+    case 4: return launch_attention_t<KV, D, 4>(p, nw, s);
+    case 8: return launch_attention_t<KV, D, 8>(p, nw, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int KV>
-hipError_t dispatch_d(const Params& p, int d, int gt, hipStream_t s) {
+hipError_t dispatch_d(const Params& p, int d, int gt, int nw, hipStream_t s) {
     switch (d) {
-    case 64: return dispatch_gt<KV, 64>(p, gt, s);
-    case 128: return dispatch_gt<KV, 128>(p, gt, s);
+    case 64: return dispatch_gt<KV, 64>(p, gt, nw, s);
+    case 128: return dispatch_gt<KV, 128>(p, gt, nw, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -590,18 +627,20 @@ int group_tile(int G) {
     return t;
 }
 
-int tile_rows(int kv, int head_dim, int gtile) {
+int tile_rows(int kv, int head_dim, int gtile, int nw) {
     const int bytes = kv == KV_F32 ? 4 : (kv == KV_I8 ? 1 : 2);
     const int lpr = head_dim * bytes / 16;
-    return kWaves * (64 / lpr) * unroll_for(gtile);
+    return nw * (64 / lpr) * unroll_for(gtile);
 }
 
-hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, hipStream_t s) {
+bool wide_ok(int kv, int gtile) { return wide_built(kv, gtile); }
+
+hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, int nw, hipStream_t s) {
     switch (kv) {
-    case KV_F32: return dispatch_d<KV_F32>(p, head_dim, gtile, s);
-    case KV_F16: return dispatch_d<KV_F16>(p, head_dim, gtile, s);
-    case KV_BF16: return dispatch_d<KV_BF16>(p, head_dim, gtile, s);
-    case KV_I8: return dispatch_d<KV_I8>(p, head_dim, gtile, s);
+    case KV_F32: return dispatch_d<KV_F32>(p, head_dim, gtile, nw, s);
+    case KV_F16: return dispatch_d<KV_F16>(p, head_dim, gtile, nw, s);
+    case KV_BF16: return dispatch_d<KV_BF16>(p, head_dim, gtile, nw, s);
+    case KV_I8: return dispatch_d<KV_I8>(p, head_dim, gtile, nw, s);
     default: return hipErrorInvalidValue;
     }
 }

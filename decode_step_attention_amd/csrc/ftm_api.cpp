@@ -94,29 +94,46 @@ std::pair<hipEvent_t, hipEvent_t> timing_slot(int kind) {
 }
 
 std::atomic<int> g_split_chunk{0};
+std::atomic<int> g_waves{0};
 
 int env_int(const char* name, int dflt) {
     const char* v = std::getenv(name);
     return v && *v ? std::atoi(v) : dflt;
 }
 
-// Chunk length.  Enough (sequence, KV head, head-group, chunk) workgroups
-// to give every CU several, never shorter than one streaming tile.
-int choose_chunk(int units, int step, int tile, int n_cu) {
+// Launch shape: waves per workgroup and chunk length.
+//
+// The kernel is bound by HBM bandwidth, which needs about 64 KiB of loads in
+// flight per CU, all CUs busy and equal work per workgroup.  When the
+// (sequence, KV head, head group) units are about one per CU, a 16-wave
+// workgroup per unit (split only if there are fewer units than CUs) keeps a
+// CU full with one launch and no combine.  With many units, 4-wave
+// workgroups several to a CU balance better.  Passes over several query
+// heads, and INT8 caches, need more registers per wave and take 4 waves.
+struct Shape {
+    int nw;
+    int chunk;
+};
+
+Shape choose_shape(int kv, int head_dim, int gtile, int units, int step, int n_cu) {
+    int nw = g_waves.load();
+    if (nw == 0) nw = env_int("FTM_WAVES", 0);
+    if (nw != 4 && nw != 16) nw = (ftm::wide_ok(kv, gtile) && units < 2 * n_cu) ? 16 : 4;
+    if (nw == 16 && !ftm::wide_ok(kv, gtile)) nw = 4;
+    const int tile = ftm::tile_rows(kv, head_dim, gtile, nw);
     int forced = g_split_chunk.load();
     if (forced == 0) forced = env_int("FTM_SPLIT_CHUNK", 0);
     int chunk;
     if (forced > 0) {
         chunk = forced;
     } else {
-        const long target_blocks = 8L * n_cu;
+        const long target_blocks = nw == 16 ? n_cu : 4L * n_cu;
         long want_s = (target_blocks + units - 1) / units;
         if (want_s < 1) want_s = 1;
         chunk = (int)((step + want_s - 1) / want_s);
-        if (chunk < 2 * tile) chunk = 2 * tile;
     }
     chunk = (chunk + tile - 1) / tile * tile;
-    return chunk;
+    return {nw, chunk};
 }
 
 int cu_count(int device) {
@@ -157,6 +174,11 @@ size_t ftm_kv_cache_bytes(int batch, int n_kv_heads, int max_seq_len, int head_d
 int ftm_set_split_chunk(int positions) {
     if (positions < 0) return -1;
     return g_split_chunk.exchange(positions);
+}
+
+int ftm_set_workgroup_waves(int waves) {
+    if (waves != 0 && waves != 4 && waves != 16) return -1;
+    return g_waves.exchange(waves);
 }
 
 void ftm_release_workspaces(void) {
@@ -297,9 +319,9 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
     p.n_hg = n_hg;
     p.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
 
-    const int tile = ftm::tile_rows(kv_dtype, head_dim, gtile);
     const int units = batch * n_kv_heads * n_hg;
-    p.chunk = choose_chunk(units, step, tile, cu_count(device));
+    const Shape shape = choose_shape(kv_dtype, head_dim, gtile, units, step, cu_count(device));
+    p.chunk = shape.chunk;
     p.S = (step + p.chunk - 1) / p.chunk;
     p.direct = p.S == 1;
     if (!p.direct) {
@@ -313,7 +335,7 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
 
     auto ev = timing_slot(0);
     if (ev.first) (void)hipEventRecord(ev.first, stream);
-    he = ftm::launch_attention(p, kv_dtype, head_dim, gtile, stream);
+    he = ftm::launch_attention(p, kv_dtype, head_dim, gtile, shape.nw, stream);
     if (ev.second) (void)hipEventRecord(ev.second, stream);
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(he));
     if (!p.direct) {

@@ -34,10 +34,12 @@ struct Params {
 
 // Group tile (query heads served by one pass over a KV head) for G heads.
 int group_tile(int G);
-// Positions one workgroup covers per iteration of its streaming loop.
-int tile_rows(int kv, int head_dim, int group_tile);
+// Positions one workgroup of `nw` waves covers per streaming iteration.
+int tile_rows(int kv, int head_dim, int group_tile, int nw);
+// Whether the 16-wave workgroup is built for this cache type and group tile.
+bool wide_ok(int kv, int group_tile);
 
-hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, hipStream_t s);
+hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, int nw, hipStream_t s);
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);
 
 }  // namespace ftm

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import Callable, Optional, Tuple
 
 import torch
 
@@ -25,7 +25,7 @@ _ACT = {FTM_F32: torch.float32, FTM_F16: torch.float16, FTM_BF16: torch.bfloat16
 
 # Every symbol include/ftm.h declares.
 EXPORTS = ("ftm_decode_mha", "ftm_kv_cache_bytes", "ftm_last_error", "ftm_version",
-           "ftm_set_split_chunk", "ftm_release_workspaces", "ftm_timing_enable",
+           "ftm_set_split_chunk", "ftm_set_workgroup_waves", "ftm_release_workspaces", "ftm_timing_enable",
            "ftm_timing_disable", "ftm_timing_read")
 
 
@@ -46,6 +46,8 @@ def _load() -> ctypes.CDLL:
     lib.ftm_version.restype = ctypes.c_char_p
     lib.ftm_set_split_chunk.argtypes = [i32]
     lib.ftm_set_split_chunk.restype = i32
+    lib.ftm_set_workgroup_waves.argtypes = [i32]
+    lib.ftm_set_workgroup_waves.restype = i32
     lib.ftm_release_workspaces.argtypes = []
     lib.ftm_release_workspaces.restype = None
     lib.ftm_timing_enable.argtypes = [i32]
@@ -75,6 +77,10 @@ def ftm_kv_cache_bytes(batch: int, n_kv_heads: int, max_seq_len: int, head_dim: 
 
 def ftm_set_split_chunk(positions: int) -> int:
     return int(lib.ftm_set_split_chunk(positions))
+
+
+def ftm_set_workgroup_waves(waves: int) -> int:
+    return int(lib.ftm_set_workgroup_waves(waves))
 
 
 def ftm_release_workspaces() -> None:
@@ -114,15 +120,7 @@ def ftm_decode_mha_raw(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, ba
                                   kv_scales, out, stream))
 
 
-def ftm_decode_mha(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-                   qkv_bias: Optional[torch.Tensor], k_cache: torch.Tensor, v_cache: torch.Tensor,
-                   seq_lens: Optional[torch.Tensor], step: int, out: torch.Tensor,
-                   kv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
-    """One decode step (see include/ftm.h).  Shapes: q/out [B, H, D],
-    k_new/v_new [B, Hkv, D], k_cache/v_cache [B, Hkv, Lmax, D],
-    qkv_bias [(H + 2 Hkv) D] or None, seq_lens int32 [B] or None,
-    kv_scales fp32 [2, B, Hkv, Lmax] for an int8 cache.  Caches and scales
-    are updated in place; out is written."""
+def _marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step, out, kv_scales, stream):
     if k_cache.dim() != 4 or q.dim() != 3:
         raise ValueError("q must be [B, H, D] and k_cache [B, Hkv, Lmax, D]")
     B, H, D = q.shape
@@ -152,7 +150,37 @@ def ftm_decode_mha(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
             raise ValueError(f"{name} is on {t.device}, the cache on {dev}")
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.ftm_decode_mha(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_cache),
-                            _ptr(v_cache), _ptr(seq_lens), B, Lmax, int(step), H, Hkv, D, kv,
-                            _ptr(kv_scales), _ptr(out), ctypes.c_void_p(stream))
-    _check(rc)
+    return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_cache), _ptr(v_cache),
+            _ptr(seq_lens), B, Lmax, int(step), H, Hkv, D, kv, _ptr(kv_scales), _ptr(out),
+            ctypes.c_void_p(stream))
+
+
+def ftm_decode_mha(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   qkv_bias: Optional[torch.Tensor], k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   seq_lens: Optional[torch.Tensor], step: int, out: torch.Tensor,
+                   kv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One decode step (see include/ftm.h).  Shapes: q/out [B, H, D],
+    k_new/v_new [B, Hkv, D], k_cache/v_cache [B, Hkv, Lmax, D],
+    qkv_bias [(H + 2 Hkv) D] or None, seq_lens int32 [B] or None,
+    kv_scales fp32 [2, B, Hkv, Lmax] for an int8 cache.  Caches and scales
+    are updated in place; out is written."""
+    _check(lib.ftm_decode_mha(*_marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens,
+                                        step, out, kv_scales, stream)))
+
+
+def ftm_decode_mha_prepared(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step, out,
+                            kv_scales=None, stream=None) -> Callable[[], None]:
+    """Checks and marshals the arguments once and returns a callable that
+    issues the same ftm_decode_mha call, for loops that repeat a call on
+    fixed buffers.  The tensors must stay alive and in place."""
+    args = _marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step, out, kv_scales,
+                    stream)
+    keep = (q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, kv_scales)
+    f = lib.ftm_decode_mha
+
+    def call() -> None:
+        rc = f(*args)
+        if rc != 0:
+            raise RuntimeError(f"libftm status {rc}: {ftm_last_error()}")
+    call.tensors = keep
+    return call

@@ -132,9 +132,17 @@ const char* ftm_version(void);
  * independent partial softmax states per chunk, merged by a combine
  * kernel; [pptc.cn/news/144085] section 2.2 on running softmax statistics).
  * 0 restores the automatic choice.  Values are rounded up to the kernel's
- * tile; a chunk of max_seq_len or more forces the single-pass kernel.
+ * tile; a chunk of `step` or more gives a single pass with no combine.
  * Process-wide; returns the previous setting, or -1 for a negative value. */
 int ftm_set_split_chunk(int positions);
+
+/* Waves per workgroup of the attention pass: 4 or 16; 0 restores the
+ * automatic choice (16 when there are fewer (sequence, KV head) units than
+ * twice the CU count and the 16-wave shape is built, else 4).  The 16-wave
+ * shape is built for passes of one query head over fp32, fp16 and bf16
+ * caches; elsewhere 4 is used whatever is set.  Process-wide; returns the
+ * previous setting, or -1 for another value. */
+int ftm_set_workgroup_waves(int waves);
 
 /* Frees every workspace the library holds (all devices and streams).  The
  * caller must make sure no call of this library is still running. */

@@ -57,7 +57,7 @@ def check(case, out, ref, tag="", tol=None):
 
 
 def run_and_compare(ftm, case, chunk=0, device="cuda", poison=True, with_bias=True,
-                    with_lens=True, lens=None, mutate=None, tag="", tol=None):
+                    with_lens=True, lens=None, mutate=None, tag="", tol=None, waves=0):
     """Full comparison at a size the oracle finishes quickly."""
     inp = W.make_inputs(case, "cpu", poison=poison, lens=lens)
     if mutate:
@@ -70,11 +70,13 @@ def run_and_compare(ftm, case, chunk=0, device="cuda", poison=True, with_bias=Tr
     ref_out, _ = run_oracle(oracle, case, npi, n_threads=8)
     g = {k: (v.to(device) if torch.is_tensor(v) else v) for k, v in inp.items()}
     ftm.ftm_set_split_chunk(chunk)
+    ftm.ftm_set_workgroup_waves(waves)
     try:
         out = gpu_call(ftm, g, case, with_bias, with_lens)
         torch.cuda.synchronize()
     finally:
         ftm.ftm_set_split_chunk(0)
+        ftm.ftm_set_workgroup_waves(0)
     # caches: every byte equals the oracle's (appended rows bit-exact, the
     # rest untouched); NaN-poisoned rows compare as bytes too
     assert to_np(g["k_cache"], case.kv_dtype).tobytes() == npi["k_cache"].tobytes(), f"{tag}: k_cache"
@@ -100,6 +102,40 @@ GRID = [(kv, D, H, Hkv) for kv in ("f32", "f16", "bf16", "i8") for D in (64, 128
 def test_parity_grid(ftm, kv, D, H, Hkv):
     case = small(kv, D=D, H=H, Hkv=Hkv, seed=11 + D + H * 3 + Hkv)
     run_and_compare(ftm, case, tag=f"{kv} D{D} H{H}/{Hkv}")
+
+
+WIDE = [(kv, D, H, Hkv, chunk) for kv in ("f32", "f16", "bf16", "i8") for D in (64, 128)
+        for (H, Hkv) in ((4, 4), (8, 4)) for chunk in (0, 256)]
+
+
+@pytest.mark.parametrize("kv,D,H,Hkv,chunk", WIDE)
+def test_parity_wide_workgroups(ftm, kv, D, H, Hkv, chunk):
+    """The 16-wave workgroup (one or two query heads per pass), single pass
+    and split."""
+    case = small(kv, D=D, H=H, Hkv=Hkv, seed=21 + D + H + Hkv + chunk)
+    run_and_compare(ftm, case, chunk=chunk, waves=16, tag=f"wide {kv} D{D} H{H}/{Hkv} c{chunk}")
+
+
+@pytest.mark.parametrize("waves", [4, 16])
+def test_parity_forced_narrow_and_wide_on_7b_shape(ftm, waves):
+    """The 7B-shaped layer (fp16, 32 heads x 128) at a shorter context, both
+    workgroup shapes."""
+    case = W.Case("7b-short", 8, 32, 32, 128, "f16", ctx=640, max_seq_len=640,
+                  value_scale=1 / np.sqrt(128), seed=22)
+    run_and_compare(ftm, case, waves=waves, tag=f"7b-short waves{waves}")
+
+
+def test_prepared_call_matches_plain_call(ftm):
+    case = small("bf16", B=2, H=8, Hkv=2, Lmax=900, lens=(500, 900), seed=23)
+    inp = W.make_inputs(case, "cuda")
+    a = gpu_call(ftm, inp, case)
+    out = torch.empty_like(a)
+    call = ftm.ftm_decode_mha_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"],
+                                       inp["k_cache"], inp["v_cache"], inp["seq_lens"], inp["step"],
+                                       out, inp.get("kv_scales"))
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(bits(a), bits(out))
 
 
 @pytest.mark.parametrize("G", [3, 5, 12, 16])
