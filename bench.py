@@ -167,14 +167,19 @@ def main():
             call(k)
             k += 1
     torch.cuda.synchronize()
-    # timed region 1: the whole path, nothing else on the stream
+    # timed region 1: the whole path, nothing else on the stream; a HIP event
+    # pair on the launch stream brackets the region
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    r0.record(stream)
     for _ in range(args.steps):
         for _l in range(layers):
             call(k)
             k += 1
+    r1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    region_gpu_ms = r0.elapsed_time(r1)
     # timed region 2: the same steps with a HIP event pair recorded around
     # every kernel launch, on the launch stream, for per-kernel durations
     ftm.ftm_timing_enable(args.steps * layers + 8)
@@ -192,13 +197,23 @@ def main():
     elapsed = t1 - t0
     ms_step = elapsed * 1e3 / args.steps
     gbs = kv_step * args.steps / elapsed / 1e9
-    avg_att_us = ms_att * 1e3 / max(n_att, 1)
+    per_launch_us = ms_att * 1e3 / max(n_att, 1)
+    if n_cmb == 0:
+        # one kernel per step: its average duration is the event-bracketed
+        # region time over the launches (an event pair around every launch
+        # adds its own dispatch and release time, a few us)
+        avg_att_us = region_gpu_ms * 1e3 / (args.steps * layers)
+        timing = "events bracketing timed region 1 / launches (one kernel per step)"
+    else:
+        avg_att_us = per_launch_us
+        timing = "event pair around every attention launch in timed region 2"
     achieved = kv_layer / (avg_att_us * 1e-6) / 1e9
     traffic = read_traffic(args.config)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
             "kernel": "attention_kernel", "avg_launch_us": round(avg_att_us, 2),
+            "avg_launch_us_per_launch_events": round(per_launch_us, 2), "timing": timing,
             "launches": n_att, "algorithmic_bytes_per_launch": kv_layer}
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
