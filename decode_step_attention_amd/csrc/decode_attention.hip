@@ -24,6 +24,8 @@
 // .../2131745] section 2.1).  Scores never leave registers.
 #include "ftm_internal.hpp"
 
+#include <cstdlib>
+
 namespace ftm {
 namespace {
 
@@ -33,6 +35,8 @@ constexpr int kWaves = 4;                 // waves per combine workgroup
 constexpr int kThreads = 64 * kWaves;
 // Buffer descriptor word 3 for raw (untyped) buffer access on the gfx9 family.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the K/V stream: non-temporal (every byte is used once).
+constexpr int kStream = 2;
 constexpr float kNegInf = -__builtin_inff();
 
 // ---------------------------------------------------------------------------
@@ -322,21 +326,21 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
     auto issue_k = [&](int base) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, 0);
+            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
         if constexpr (I8) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                ksc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (base + u * RPI + r) * 4, 0, 0));
+                ksc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (base + u * RPI + r) * 4, 0, kStream));
         }
     };
     auto issue_v = [&](int base) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, 0);
+            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
         if constexpr (I8) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                vsc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, (base + u * RPI + r) * 4, 0, 0));
+                vsc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, (base + u * RPI + r) * 4, 0, kStream));
         }
     };
 
@@ -533,6 +537,535 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped-query pass on the matrix cores, for fp16/bf16 caches with 4 or 8
+// query heads per KV head.  Both products are small dense contractions and
+// run as MFMA, heads padded to 16:
+//  * S^T = K . Q^T with v_mfma_f32_16x16x32: each lane's 16-byte slice of a
+//    K row is its A operand as loaded (no conversion, no cross-lane sum).
+//    The fp32 query (bias added, log2(e)/sqrt(D) folded in) is the B
+//    operand as two halves, hi = round(q) and lo = round(q - hi), whose
+//    products accumulate in fp32: about 16 (bf16) or 22 (fp16) bits of q.
+//  * O += P . V with v_mfma_f32_16x16x16: S^T leaves each lane holding four
+//    consecutive positions of one head, which is exactly the A-operand
+//    layout of P, so the weights need no shuffle; they enter as hi/lo
+//    halves too.  V must be read down its columns, so every V tile goes
+//    through a per-wave LDS buffer whose row pitch (D*2 + 8 bytes) puts the
+//    four rows one operand reads on distinct banks.
+// The softmax runs on the S^T tile: lane (g, n) holds head n at positions
+// 4g..4g+3 of each 16-position tile.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int KV> struct Mfma;
+template <> struct Mfma<KV_BF16> {
+    typedef bf16x8 vec8;
+    typedef s16x4 vec4;
+    __device__ static vec8 bits8(const u32x4 w) { return __builtin_bit_cast(vec8, w); }
+    __device__ static vec4 bits4(const u32x2 w) { return __builtin_bit_cast(vec4, w); }
+    __device__ static void split8(const float* x, vec8& hi, vec8& lo) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const __bf16 h = (__bf16)x[i];
+            hi[i] = h;
+            lo[i] = (__bf16)(x[i] - (float)h);
+        }
+    }
+    __device__ static void split4(const float* x, vec4& hi, vec4& lo) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const __bf16 h = (__bf16)x[i];
+            hi[i] = __builtin_bit_cast(short, h);
+            lo[i] = __builtin_bit_cast(short, (__bf16)(x[i] - (float)h));
+        }
+    }
+    __device__ static f32x4 mma32(const vec8 a, const vec8 b, const f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static f32x4 mma16(const vec4 a, const vec4 b, const f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<KV_F16> {
+    typedef f16x8 vec8;
+    typedef f16x4 vec4;
+    __device__ static vec8 bits8(const u32x4 w) { return __builtin_bit_cast(vec8, w); }
+    __device__ static vec4 bits4(const u32x2 w) { return __builtin_bit_cast(vec4, w); }
+    __device__ static void split8(const float* x, vec8& hi, vec8& lo) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const _Float16 h = (_Float16)x[i];
+            hi[i] = h;
+            lo[i] = (_Float16)(x[i] - (float)h);
+        }
+    }
+    __device__ static void split4(const float* x, vec4& hi, vec4& lo) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const _Float16 h = (_Float16)x[i];
+            hi[i] = h;
+            lo[i] = (_Float16)(x[i] - (float)h);
+        }
+    }
+    __device__ static f32x4 mma32(const vec8 a, const vec8 b, const f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static f32x4 mma16(const vec4 a, const vec4 b, const f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Orders this wave's LDS accesses: everything issued before has completed.
+__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Device-coherent accesses for data handed between workgroups on different
+// XCDs (relaxed atomics at agent scope: written through to, and read from,
+// the device coherence point).
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's stores have been acknowledged.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Largest batch the balanced schedule handles (its per-sequence work
+// offsets live in LDS); larger batches take the vector-ALU pass.
+constexpr int kGqaMaxBatch = 1024;
+
+// One segment [pos0, pos1) of one unit (sequence b, KV head j, head group
+// hgi) streamed by the whole workgroup.  On return the workgroup's merged
+// state sits in LDS: n_states softmax states (m, l, o[HP][D]), one per wave
+// plus the appended row's when the segment holds it.
+template <int KV, int D, int HP, int NT, int NW>
+__device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* smem, float (*sm_m)[HP],
+                                           float (*sm_l)[HP], int b, int j, int hgi, int L,
+                                           int pos0, int pos1) {
+    using MF = Mfma<KV>;
+    typedef typename MF::vec8 vec8;
+    typedef typename MF::vec4 vec4;
+    constexpr int ROW_BYTES = D * 2;
+    constexpr int KK = D / 32;              // S^T: MFMA steps over the head dim
+    constexpr int DT = D / 16;              // O: 16-column tiles
+    constexpr int EPL = 8;                  // V: elements per lane per load
+    constexpr int LPR = D / EPL;            // V: lanes per row
+    constexpr int RPI = 64 / LPR;           // V: rows per wave-wide load
+    constexpr int VL = 16 / RPI;            // V: loads per 16-position tile
+    constexpr int WAVE_ROWS = 16 * NT;
+    constexpr int BLOCK_ROWS = NW * WAVE_ROWS;
+    constexpr int VPITCH = ROW_BYTES + 8;   // bytes per V row in LDS
+    constexpr int V_BYTES = WAVE_ROWS * VPITCH;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;                // MFMA layout: k-slot group, position quad
+    const int n = lane & 15;                // MFMA layout: K row / head column / V column
+    const int r = lane / LPR;               // V load layout: row slot
+    const int c = lane % LPR;               // V load layout: 16-byte column slice
+    const int h0 = j * p.G + hgi * HP;
+    const int heads_here = min(HP, p.G - hgi * HP);
+    const int stream_end = min(pos1, L - 1);
+    const bool owns_new = pos1 == L;
+
+    const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;
+    const uint32_t valid_bytes = (uint32_t)max(stream_end, 0) * ROW_BYTES;
+    const auto krs = make_rsrc((const char*)p.k_cache + row0 * ROW_BYTES, valid_bytes);
+    const auto vrs = make_rsrc((const char*)p.v_cache + row0 * ROW_BYTES, valid_bytes);
+    unsigned char* vtile = smem + wave * V_BYTES;
+
+    u32x4 kr[NT][KK], vr[NT][VL];
+    // K: lane (g, n) reads row n of the tile, 16-byte pieces kk*4 + g (one
+    // wave-wide load covers 64 contiguous bytes of each of 16 rows)
+    auto issue_k = [&](int base) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                kr[t][kk] = __builtin_amdgcn_raw_buffer_load_b128(
+                    krs, (base + t * 16 + n) * ROW_BYTES + (kk * 4 + g) * 16, 0, kStream);
+    };
+    auto issue_v = [&](int base) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int u = 0; u < VL; ++u)
+                vr[t][u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    vrs, (base + t * 16 + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
+    };
+
+    int base = pos0 + wave * WAVE_ROWS;
+    issue_k(base);
+    issue_v(base);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // query as the B operand of S^T: column n = head h0 + n (zero past the
+    // group), k-slots of step kk = elements (kk*4 + g)*8 .. +8, the same
+    // permutation of the head dim the K loads use
+    vec8 qhi[KK], qlo[KK];
+    {
+        const int hq = min(h0 + n, p.H - 1);
+        float x[KK][8];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            load_act<KV, 8>(p.q, ((size_t)b * p.H + hq) * D + (kk * 4 + g) * 8, x[kk]);
+        if (p.bias) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                float bx[8];
+                load_act<KV, 8>(p.bias, (size_t)hq * D + (kk * 4 + g) * 8, bx);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[kk][e] = x[kk][e] + bx[e];
+            }
+        }
+        const bool ok = n < heads_here;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[kk][e] = ok ? x[kk][e] * p.qscale : 0.0f;
+            MF::split8(x[kk], qhi[kk], qlo[kk]);
+        }
+    }
+
+    float m = kNegInf;                      // head n: running max (same in all four quads)
+    float l = 0.0f;                         // head n: this lane's share of the sum
+    f32x4 acc[DT];                          // O[head 4g+i][16*tn + n]
+#pragma unroll
+    for (int tn = 0; tn < DT; ++tn) acc[tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (; base < stream_end; base += BLOCK_ROWS) {
+        // S^T tiles: row = position 4g+i of the tile, column = head n
+        f32x4 st[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            st[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const vec8 kb = MF::bits8(kr[t][kk]);
+                st[t] = MF::mma32(kb, qhi[kk], st[t]);
+                st[t] = MF::mma32(kb, qlo[kk], st[t]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(base + BLOCK_ROWS);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // V rows into this wave's LDS tile (8-byte stores: the pitch is 8 mod 16)
+        lds_wave_fence();
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int u = 0; u < VL; ++u) {
+                u32x2* dst = (u32x2*)(vtile + (t * 16 + u * RPI + r) * VPITCH + c * 16);
+                dst[0] = u32x2{vr[t][u][0], vr[t][u][1]};
+                dst[1] = u32x2{vr[t][u][2], vr[t][u][3]};
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(base + BLOCK_ROWS);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // online softmax per head (column n), over the 4*NT positions of this
+        // lane and the three other quads of the column
+        float s[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s[t][i] = base + t * 16 + 4 * g + i < stream_end ? st[t][i] : kNegInf;
+        float mt = s[0][0];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[t][i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float ms = mn == kNegInf ? 0.0f : mn;
+        const float alpha = fast_exp2(m - ms);
+        m = mn;
+        float ls = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[t][i] = fast_exp2(s[t][i] - ms);
+                ls += s[t][i];
+            }
+        l = l * alpha + ls;
+        // P as the A operand of O += P.V: row = head n, k = positions 4g+i
+        vec4 ph[NT], pl[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) MF::split4(s[t], ph[t], pl[t]);
+        // rescale O rows (heads 4g+i) by their heads' factors
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha, 4 * g + i);
+#pragma unroll
+            for (int tn = 0; tn < DT; ++tn) acc[tn][i] *= ai;
+        }
+        lds_wave_fence();
+        // P.V: B operand = V[position 4g+i][16*tn + n], read down the tile's columns
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const unsigned char* col = vtile + (t * 16 + 4 * g) * VPITCH + n * 2;
+#pragma unroll
+            for (int tn = 0; tn < DT; ++tn) {
+                const unsigned char* q0 = col + tn * 32;
+                const uint32_t e0 = *(const uint16_t*)(q0);
+                const uint32_t e1 = *(const uint16_t*)(q0 + VPITCH);
+                const uint32_t e2 = *(const uint16_t*)(q0 + 2 * VPITCH);
+                const uint32_t e3 = *(const uint16_t*)(q0 + 3 * VPITCH);
+                const vec4 vb = MF::bits4(u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
+                acc[tn] = MF::mma16(ph[t], vb, acc[tn]);
+                acc[tn] = MF::mma16(pl[t], vb, acc[tn]);
+            }
+        }
+    }
+
+    // l over the four quads of the column
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    __syncthreads();                        // every wave is done with its V tile
+    float* sm_o = (float*)smem;             // [NW + 1][HP][D]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * g + i;
+        if (h < HP) {
+#pragma unroll
+            for (int tn = 0; tn < DT; ++tn) sm_o[(wave * HP + h) * D + tn * 16 + n] = acc[tn][i];
+        }
+    }
+    if (g == 0 && n < HP) {
+        sm_m[wave][n] = m;
+        sm_l[wave][n] = l;
+    }
+
+    // the appended row: stored by wave 0, and kept as one more softmax state
+    if (owns_new && wave == 0) {
+        const int pnew = L - 1;
+        const size_t src_row = (size_t)b * p.Hkv + j;
+        float kx[EPL], vx[EPL], ks, vs;
+        u32x4 kpk, vpk;
+        make_new_row<KV, D, EPL, LPR>(p, p.k_new, p.H + j, src_row, c, kx, ks, kpk);
+        make_new_row<KV, D, EPL, LPR>(p, p.v_new, p.H + p.Hkv + j, src_row, c, vx, vs, vpk);
+        if (hgi == 0 && r == 0) {
+            *(u32x4*)((char*)p.k_cache + (row0 + pnew) * ROW_BYTES + c * 16) = kpk;
+            *(u32x4*)((char*)p.v_cache + (row0 + pnew) * ROW_BYTES + c * 16) = vpk;
+        }
+#pragma unroll
+        for (int h = 0; h < HP; ++h) {
+            const int hq = min(h0 + h, p.H - 1);
+            float qx[EPL];
+            load_act<KV, EPL>(p.q, ((size_t)b * p.H + hq) * D + c * EPL, qx);
+            if (p.bias) {
+                float bx[EPL];
+                load_act<KV, EPL>(p.bias, (size_t)hq * D + c * EPL, bx);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) qx[e] = qx[e] + bx[e];
+            }
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) d = fmaf(qx[e] * p.qscale, kx[e], d);
+            d = group_sum<LPR>(d);
+            if (r == 0) {
+                if (c == 0) {
+                    sm_m[NW][h] = d;
+                    sm_l[NW][h] = 1.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) sm_o[(NW * HP + h) * D + c * EPL + e] = vx[e];
+            }
+        }
+    }
+    __syncthreads();
+    return owns_new ? NW + 1 : NW;
+}
+
+// Grouped-query pass with a balanced schedule.  The work of a step is the
+// concatenation over units u = (b, j, hgi) of L_b positions each; workgroup
+// i takes the slice [i*W, (i+1)*W) of it, W = max(ceil(total / grid),
+// seg_min) rounded to 16, whatever the lengths, so every workgroup streams
+// the same number of rows.  A slice crossing units is several segments.
+// Each segment's state is written to the unit's partial slot; the last
+// workgroup to finish a unit (an atomic count per unit, device-scope
+// fences around it) merges the unit's partials into `out` and clears the
+// count for the next call.  A unit inside one segment writes `out` directly.
+template <int KV, int D, int HP, int NT, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+gqa_kernel(const Params p) {
+    using A = Act<KV>;
+    constexpr int NTH = 64 * NW;
+    constexpr int V_BYTES = 16 * NT * (D * 2 + 8);
+    constexpr int O_BYTES = (NW + 1) * HP * D * 4;
+    static_assert(HP == 4 || HP == 8, "4 or 8 heads per pass");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[cmax(NW * V_BYTES, O_BYTES)];
+    __shared__ float sm_m[NW + 1][HP];      // slot NW: the appended row
+    __shared__ float sm_l[NW + 1][HP];
+    __shared__ int sm_pref[kGqaMaxBatch + 1];   // work offset of each sequence
+    __shared__ int sm_last;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int upb = p.Hkv * p.n_hg;         // units per sequence
+
+    // per-sequence work (valid length * units), then its exclusive prefix
+    for (int i = threadIdx.x; i < p.B; i += NTH) {
+        const int Lb = p.seq_lens ? p.seq_lens[i] : p.step;
+        sm_pref[i + 1] = (Lb >= 1 && Lb <= p.step) ? Lb * upb : 0;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int carry = 0;
+        for (int base = 0; base < p.B; base += 64) {
+            const int idx = base + lane;
+            int v = idx < p.B ? sm_pref[idx + 1] : 0;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(v, off);
+                if (lane >= off) v += t;
+            }
+            if (idx < p.B) sm_pref[idx + 1] = carry + v;
+            carry += __shfl(v, 63);
+        }
+        if (lane == 0) sm_pref[0] = 0;
+    }
+    __syncthreads();
+
+    // NaN rows for sequences whose length is invalid (no append for them)
+    for (int bb = blockIdx.x; bb < p.B; bb += gridDim.x) {
+        if (sm_pref[bb + 1] == sm_pref[bb])
+            for (int idx = threadIdx.x; idx < p.H * D; idx += NTH)
+                A::st(p.out, (size_t)bb * p.H * D + idx, __builtin_nanf(""));
+    }
+    const int total = sm_pref[p.B];
+    if (total == 0) return;
+    int W = (total + gridDim.x - 1) / gridDim.x;
+    W = max((W + 15) / 16 * 16, p.seg_min);
+    int st = blockIdx.x * W;
+    const int en = min(st + W, total);
+
+    float* sm_o = (float*)smem;
+    while (st < en) {
+        // the sequence holding work offset st: largest b with pref[b] <= st
+        int lo = 0, hi = p.B;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sm_pref[mid] <= st) lo = mid;
+            else hi = mid;
+        }
+        const int b = lo;
+        const int L = (sm_pref[b + 1] - sm_pref[b]) / upb;
+        const int off = st - sm_pref[b];
+        const int ub = off / L;             // unit within the sequence: j * n_hg + hgi
+        const int pos0 = off - ub * L;
+        const int pos1 = min(L, pos0 + (en - st));
+        const int j = ub / p.n_hg;
+        const int hgi = ub - j * p.n_hg;
+        const int h0 = j * p.G + hgi * HP;
+        const int heads_here = min(HP, p.G - hgi * HP);
+        const int unit = b * upb + ub;
+        const int wu = sm_pref[b] + ub * L;     // work offset of the unit
+        const int first = wu / W;
+        const int nseg = (wu + L - 1) / W - first + 1;
+        const int seg = blockIdx.x - first;
+
+        const int n_states = gqa_segment<KV, D, HP, NT, NW>(p, smem, sm_m, sm_l, b, j, hgi, L, pos0, pos1);
+
+        // merge this workgroup's states; write out, or the unit's partial slot
+        for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
+            const int h = idx / D;
+            const int d = idx - h * D;
+            if (h >= heads_here) continue;
+            float M = sm_m[0][h];
+            for (int w = 1; w < n_states; ++w) M = fmaxf(M, sm_m[w][h]);
+            const float ms = M == kNegInf ? 0.0f : M;
+            float lsum = 0.0f, o = 0.0f;
+            for (int w = 0; w < n_states; ++w) {
+                const float a = fast_exp2(sm_m[w][h] - ms);
+                lsum += a * sm_l[w][h];
+                o += a * sm_o[(w * HP + h) * D + d];
+            }
+            if (nseg == 1) {
+                A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o / lsum);
+            } else {
+                const size_t slot = ((size_t)unit * p.seg_max + seg) * HP + h;
+                coherent_store(&p.ws_o[slot * D + d], o);
+                if (d == 0) {
+                    coherent_store(&p.ws_ml[slot * 2], M);
+                    coherent_store(&p.ws_ml[slot * 2 + 1], lsum);
+                }
+            }
+        }
+        if (nseg > 1) {
+            // partials are written through to the device coherence point; once
+            // every thread's stores are acknowledged the unit's count goes up,
+            // and the workgroup that completes it reads the partials back
+            // coherently.  No cache-wide writeback or invalidate is needed.
+            wait_stores();
+            __syncthreads();
+            if (threadIdx.x == 0)
+                sm_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == nseg - 1;
+            __syncthreads();
+            if (sm_last) {
+                // one parallel round for the slices' (m, l), kept in LDS as
+                // rescale factors; then each output sums its slices with
+                // independent loads
+                const size_t slot0 = (size_t)unit * p.seg_max * HP;
+                float* sm_a = (float*)smem;         // [seg_max][HP] weights 2^(m_k - M)
+                float* sm_ls = sm_a + p.seg_max * HP;   // [HP] 1 / sum_k 2^(m_k - M) l_k
+                float* sm_ms = sm_ls + HP;              // [seg_max][HP] raw m_k, then l_k
+                for (int t = threadIdx.x; t < nseg * HP; t += NTH) {
+                    sm_ms[t] = coherent_load(&p.ws_ml[(slot0 + t) * 2]);
+                    sm_a[t] = coherent_load(&p.ws_ml[(slot0 + t) * 2 + 1]);
+                }
+                __syncthreads();
+                if (threadIdx.x < HP) {
+                    const int h = threadIdx.x;
+                    float M = kNegInf;
+                    for (int k = 0; k < nseg; ++k) M = fmaxf(M, sm_ms[k * HP + h]);
+                    float lsum = 0.0f;
+                    for (int k = 0; k < nseg; ++k) {
+                        const float a = fast_exp2(sm_ms[k * HP + h] - M);
+                        lsum += a * sm_a[k * HP + h];
+                        sm_ms[k * HP + h] = a;
+                    }
+                    sm_ls[h] = 1.0f / lsum;
+                }
+                __syncthreads();
+                for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
+                    const int h = idx / D;
+                    const int d = idx - h * D;
+                    if (h >= heads_here) continue;
+                    float o = 0.0f;
+                    int k = 0;
+                    for (; k + 4 <= nseg; k += 4) {
+                        float v[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = coherent_load(&p.ws_o[(slot0 + (size_t)(k + q) * HP + h) * D + d]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) o += sm_ms[(k + q) * HP + h] * v[q];
+                    }
+                    for (; k < nseg; ++k) o += sm_ms[k * HP + h] * coherent_load(&p.ws_o[(slot0 + (size_t)k * HP + h) * D + d]);
+                    A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o * sm_ls[h]);
+                }
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();                    // LDS is reused by the next segment
+        st += pos1 - pos0;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Combine: one wave per (b, h).  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // ---------------------------------------------------------------------------
 template <int KV, int D>
@@ -576,9 +1109,22 @@ constexpr int unroll_for(int gt) { return gt <= 2 ? 8 : 4; }
 // of the fp32/fp16/bf16 caches fit without spilling.
 constexpr bool wide_built(int kv, int gt) { return gt == 1 && kv != KV_I8; }
 
+constexpr int kGqaTiles = 2;   // 16-position tiles per wave per iteration
+constexpr int kGqaWaves = 4;
+constexpr int kGqaBlocksPerCu = 2;   // resident at up to 256 registers per lane
+
+template <int KV, int D, int HP>
+hipError_t launch_gqa_t(const Params& p, hipStream_t s) {
+    hipLaunchKernelGGL((gqa_kernel<KV, D, HP, kGqaTiles, kGqaWaves>), dim3(p.S), dim3(64 * kGqaWaves), 0, s, p);
+    return hipGetLastError();
+}
+
 template <int KV, int D, int GT>
 hipError_t launch_attention_t(const Params& p, int nw, hipStream_t s) {
     dim3 grid(p.S, p.Hkv * p.n_hg, p.B);
+    if constexpr ((KV == KV_F16 || KV == KV_BF16) && (GT == 4 || GT == 8)) {
+        if (p.balanced) return launch_gqa_t<KV, D, GT>(p, s);
+    }
     constexpr int U = unroll_for(GT);
     if constexpr (wide_built(KV, GT)) {
         if (nw == 16) {
@@ -625,6 +1171,19 @@ int group_tile(int G) {
     int t = 1;
     while (t < G) t <<= 1;
     return t;
+}
+
+int gqa_blocks_per_cu() {
+    const char* e = std::getenv("FTM_GQA_BLOCKS_PER_CU");
+    const int v = e ? std::atoi(e) : 0;
+    return v > 0 && v <= 16 ? v : kGqaBlocksPerCu;
+}
+
+bool use_gqa_mfma(int kv, int gtile, int batch) {
+    if (!((kv == KV_F16 || kv == KV_BF16) && (gtile == 4 || gtile == 8))) return false;
+    if (batch > kGqaMaxBatch) return false;
+    const char* e = std::getenv("FTM_GQA_VALU");
+    return !(e && *e == '1');
 }
 
 int tile_rows(int kv, int head_dim, int gtile, int nw) {

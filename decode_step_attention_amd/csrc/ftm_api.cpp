@@ -4,6 +4,7 @@
 // decode_attention.hip.
 #include "ftm.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdio>
@@ -31,13 +32,18 @@ int fail(int status, const std::string& msg) {
 // recycled instead of allocated per layer).
 // ---------------------------------------------------------------------------
 struct Workspace {
-    void* ptr = nullptr;
+    void* ptr = nullptr;        // split partials
     size_t bytes = 0;
+    int* counters = nullptr;    // per-unit counts of the balanced schedule, zero between calls
+    size_t n_counters = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
+// Partials buffer of at least `bytes` and, when n_counters > 0, a zeroed
+// counter array of at least that many ints, for (device, stream).
+int get_workspace(int device, hipStream_t stream, size_t bytes, size_t n_counters, void** out,
+                  int** counters) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& w = g_ws[{device, stream}];
     if (w.bytes < bytes) {
@@ -59,7 +65,27 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
         }
         w.bytes = grow;
     }
+    if (w.n_counters < n_counters) {
+        if (w.counters) {
+            hipError_t e = hipFree(w.counters);
+            w.counters = nullptr;
+            w.n_counters = 0;
+            if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipFree: ") + hipGetErrorString(e));
+        }
+        size_t grow = n_counters + n_counters / 4 + 64;
+        hipError_t e = hipMalloc(&w.counters, grow * sizeof(int));
+        if (e == hipSuccess) e = hipMemset(w.counters, 0, grow * sizeof(int));
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            if (w.counters) (void)hipFree(w.counters);
+            w.counters = nullptr;
+            (void)hipGetLastError();
+            return fail(FTM_ERR_OUT_OF_MEMORY, std::string("counter array: ") + hipGetErrorString(e));
+        }
+        w.n_counters = grow;
+    }
     *out = w.ptr;
+    if (counters) *counters = w.counters;
     return FTM_OK;
 }
 
@@ -192,6 +218,15 @@ void ftm_release_workspaces(void) {
             (void)hipSetDevice(cur);
         }
     }
+    for (auto& kv : g_ws) {
+        if (kv.second.counters) {
+            int cur = 0;
+            (void)hipGetDevice(&cur);
+            (void)hipSetDevice(kv.first.first);
+            (void)hipFree(kv.second.counters);
+            (void)hipSetDevice(cur);
+        }
+    }
     g_ws.clear();
 }
 
@@ -320,17 +355,40 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
     p.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
 
     const int units = batch * n_kv_heads * n_hg;
-    const Shape shape = choose_shape(kv_dtype, head_dim, gtile, units, step, cu_count(device));
-    p.chunk = shape.chunk;
-    p.S = (step + p.chunk - 1) / p.chunk;
-    p.direct = p.S == 1;
-    if (!p.direct) {
-        const size_t n_part = (size_t)batch * n_heads * p.S;
+    const bool balanced = ftm::use_gqa_mfma(kv_dtype, gtile, batch) &&
+                          (long long)batch * step * n_kv_heads * n_hg < (1LL << 31);
+    Shape shape{4, 0};
+    p.balanced = balanced;
+    if (balanced) {
+        // grouped heads on the matrix cores: a fixed grid sharing the total
+        // work evenly; partial slots per unit, merged in the same launch
+        p.S = cu_count(device) * ftm::gqa_blocks_per_cu();
+        p.chunk = 0;
+        p.direct = 0;
+        // slices of at least 256 positions, and at most 200 slots per unit
+        // (the merge keeps a unit's slice statistics in LDS)
+        p.seg_min = std::max(256, (step + 198) / 199);
+        p.seg_max = (step + p.seg_min - 1) / p.seg_min + 1;
+        const size_t slots = (size_t)units * p.seg_max * gtile;
         void* ws = nullptr;
-        int st = get_workspace(device, stream, n_part * (head_dim + 2) * sizeof(float), &ws);
+        int st = get_workspace(device, stream, slots * (head_dim + 2) * sizeof(float), units, &ws,
+                               &p.counters);
         if (st != FTM_OK) return st;
         p.ws_o = (float*)ws;
-        p.ws_ml = p.ws_o + n_part * head_dim;
+        p.ws_ml = p.ws_o + slots * head_dim;
+    } else {
+        shape = choose_shape(kv_dtype, head_dim, gtile, units, step, cu_count(device));
+        p.chunk = shape.chunk;
+        p.S = (step + p.chunk - 1) / p.chunk;
+        p.direct = p.S == 1;
+        if (!p.direct) {
+            const size_t n_part = (size_t)batch * n_heads * p.S;
+            void* ws = nullptr;
+            int st = get_workspace(device, stream, n_part * (head_dim + 2) * sizeof(float), 0, &ws, nullptr);
+            if (st != FTM_OK) return st;
+            p.ws_o = (float*)ws;
+            p.ws_ml = p.ws_o + n_part * head_dim;
+        }
     }
 
     auto ev = timing_slot(0);
@@ -338,7 +396,7 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
     he = ftm::launch_attention(p, kv_dtype, head_dim, gtile, shape.nw, stream);
     if (ev.second) (void)hipEventRecord(ev.second, stream);
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(he));
-    if (!p.direct) {
+    if (!balanced && !p.direct) {
         auto ev2 = timing_slot(1);
         if (ev2.first) (void)hipEventRecord(ev2.first, stream);
         he = ftm::launch_combine(p, kv_dtype, head_dim, stream);

@@ -30,12 +30,24 @@ struct Params {
     int S;                  // chunks per sequence at length `step`
     int direct;             // 1: single pass writes `out`; 0: write partials
     float qscale;           // log2(e) / sqrt(D), folded into the query
+    // balanced grouped-query schedule (grid of S workgroups)
+    int balanced;           // 1: grouped-query pass on the matrix cores
+    int* counters;          // [units] finished-segment counts, zero between calls
+    int seg_min;            // shortest slice a workgroup takes, in positions
+    int seg_max;            // partial slots per unit
 };
 
 // Group tile (query heads served by one pass over a KV head) for G heads.
 int group_tile(int G);
-// Positions one workgroup of `nw` waves covers per streaming iteration.
+// Positions one workgroup of `nw` waves of the vector-ALU pass covers per
+// streaming iteration.
 int tile_rows(int kv, int head_dim, int group_tile, int nw);
+// Whether a pass of `group_tile` heads over this cache type runs on the
+// matrix cores with the balanced schedule (fp16/bf16 caches, 4 or 8 heads,
+// batch <= 1024; FTM_GQA_VALU=1 turns it off).
+bool use_gqa_mfma(int kv, int group_tile, int batch);
+// Workgroups per CU of the grouped-query pass.
+int gqa_blocks_per_cu();
 // Whether the 16-wave workgroup is built for this cache type and group tile.
 bool wide_ok(int kv, int group_tile);
 
