@@ -182,6 +182,11 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
     return v;
 }
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -638,37 +643,50 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 
 // Largest batch the balanced schedule handles (its per-sequence work
 // offsets live in LDS); larger batches take the vector-ALU pass.
-constexpr int kGqaMaxBatch = 1024;
+constexpr int kGqaMaxBatch = 256;
+
+// LDS layout of the grouped-query pass, per wave: a K tile and a V tile of
+// 16 positions, row pitches chosen so that the operand reads hit distinct
+// banks: K rows are read 16 B at a time across 16 rows (pitch = row + 16 B),
+// V is read down its columns by the transposing read, 4 rows x 32 B per
+// 16-lane group (pitch = row + 32 B).  The query operand (hi and lo halves
+// for 16 padded heads) is shared by the workgroup, with the K pitch.
+template <int D> struct GqaLds {
+    static constexpr int ROW = D * 2;
+    static constexpr int KPITCH = ROW + 16;
+    static constexpr int VPITCH = ROW + 32;
+    static constexpr int WAVE = 16 * KPITCH + 16 * VPITCH;
+    static constexpr int QBYTES = 2 * 16 * KPITCH;
+};
 
 // One segment [pos0, pos1) of one unit (sequence b, KV head j, head group
 // hgi) streamed by the whole workgroup.  On return the workgroup's merged
 // state sits in LDS: n_states softmax states (m, l, o[HP][D]), one per wave
 // plus the appended row's when the segment holds it.
-template <int KV, int D, int HP, int NT, int NW>
-__device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* smem, float (*sm_m)[HP],
-                                           float (*sm_l)[HP], int b, int j, int hgi, int L,
-                                           int pos0, int pos1) {
+template <int KV, int D, int HP, int NW>
+__device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles, unsigned char* qbuf,
+                                           float (*sm_m)[HP], float (*sm_l)[HP], int b, int j,
+                                           int hgi, int L, int pos0, int pos1) {
     using MF = Mfma<KV>;
+    using LD = GqaLds<D>;
     typedef typename MF::vec8 vec8;
     typedef typename MF::vec4 vec4;
+    constexpr int NTH = 64 * NW;
     constexpr int ROW_BYTES = D * 2;
     constexpr int KK = D / 32;              // S^T: MFMA steps over the head dim
     constexpr int DT = D / 16;              // O: 16-column tiles
-    constexpr int EPL = 8;                  // V: elements per lane per load
-    constexpr int LPR = D / EPL;            // V: lanes per row
-    constexpr int RPI = 64 / LPR;           // V: rows per wave-wide load
-    constexpr int VL = 16 / RPI;            // V: loads per 16-position tile
-    constexpr int WAVE_ROWS = 16 * NT;
-    constexpr int BLOCK_ROWS = NW * WAVE_ROWS;
-    constexpr int VPITCH = ROW_BYTES + 8;   // bytes per V row in LDS
-    constexpr int V_BYTES = WAVE_ROWS * VPITCH;
+    constexpr int EPL = 8;                  // loads: elements per lane
+    constexpr int LPR = D / EPL;            // loads: lanes per row
+    constexpr int RPI = 64 / LPR;           // loads: rows per wave-wide load
+    constexpr int VL = 16 / RPI;            // loads per 16-position tile, each of K and V
+    constexpr int BLOCK_ROWS = NW * 16;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;                // MFMA layout: k-slot group, position quad
     const int n = lane & 15;                // MFMA layout: K row / head column / V column
-    const int r = lane / LPR;               // V load layout: row slot
-    const int c = lane % LPR;               // V load layout: 16-byte column slice
+    const int r = lane / LPR;               // load layout: row slot
+    const int c = lane % LPR;               // load layout: 16-byte column slice
     const int h0 = j * p.G + hgi * HP;
     const int heads_here = min(HP, p.G - hgi * HP);
     const int stream_end = min(pos1, L - 1);
@@ -678,60 +696,48 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* smem,
     const uint32_t valid_bytes = (uint32_t)max(stream_end, 0) * ROW_BYTES;
     const auto krs = make_rsrc((const char*)p.k_cache + row0 * ROW_BYTES, valid_bytes);
     const auto vrs = make_rsrc((const char*)p.v_cache + row0 * ROW_BYTES, valid_bytes);
-    unsigned char* vtile = smem + wave * V_BYTES;
+    unsigned char* ktile = tiles + wave * LD::WAVE;
+    unsigned char* vtile = ktile + 16 * LD::KPITCH;
 
-    u32x4 kr[NT][KK], vr[NT][VL];
-    // K: lane (g, n) reads row n of the tile, 16-byte pieces kk*4 + g (one
-    // wave-wide load covers 64 contiguous bytes of each of 16 rows)
-    auto issue_k = [&](int base) {
+    // K and V rows in the load layout: one wave-wide load is RPI whole rows
+    u32x4 kr[VL], vr[VL];
+    auto issue = [&](int base) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                kr[t][kk] = __builtin_amdgcn_raw_buffer_load_b128(
-                    krs, (base + t * 16 + n) * ROW_BYTES + (kk * 4 + g) * 16, 0, kStream);
+        for (int u = 0; u < VL; ++u) {
+            const int off = (base + u * RPI + r) * ROW_BYTES + c * 16;
+            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStream);
+            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStream);
+        }
     };
-    auto issue_v = [&](int base) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int u = 0; u < VL; ++u)
-                vr[t][u] = __builtin_amdgcn_raw_buffer_load_b128(
-                    vrs, (base + t * 16 + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
-    };
-
-    int base = pos0 + wave * WAVE_ROWS;
-    issue_k(base);
-    issue_v(base);
+    int base = pos0 + wave * 16;
+    issue(base);
     __builtin_amdgcn_sched_barrier(0);
 
-    // query as the B operand of S^T: column n = head h0 + n (zero past the
-    // group), k-slots of step kk = elements (kk*4 + g)*8 .. +8, the same
-    // permutation of the head dim the K loads use
-    vec8 qhi[KK], qlo[KK];
-    {
-        const int hq = min(h0 + n, p.H - 1);
-        float x[KK][8];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            load_act<KV, 8>(p.q, ((size_t)b * p.H + hq) * D + (kk * 4 + g) * 8, x[kk]);
-        if (p.bias) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
+    // query operand of S^T, shared by the workgroup: column n = head h0 + n
+    // (zero past the group), hi and lo halves, in the K tile's layout; one
+    // 16-byte piece of one head per thread
+    for (int idx = threadIdx.x; idx < 16 * LPR; idx += NTH) {
+        const int col = idx / LPR;
+        const int pc = idx - col * LPR;
+        float x[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        if (col < heads_here) {
+            const size_t h = (size_t)h0 + col;
+            load_act<KV, 8>(p.q, ((size_t)b * p.H + h) * D + pc * 8, x);
+            if (p.bias) {
                 float bx[8];
-                load_act<KV, 8>(p.bias, (size_t)hq * D + (kk * 4 + g) * 8, bx);
+                load_act<KV, 8>(p.bias, h * D + pc * 8, bx);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[kk][e] = x[kk][e] + bx[e];
+                for (int e = 0; e < 8; ++e) x[e] = x[e] + bx[e];
             }
-        }
-        const bool ok = n < heads_here;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[kk][e] = ok ? x[kk][e] * p.qscale : 0.0f;
-            MF::split8(x[kk], qhi[kk], qlo[kk]);
+            for (int e = 0; e < 8; ++e) x[e] *= p.qscale;
         }
+        vec8 hi, lo;
+        MF::split8(x, hi, lo);
+        *(vec8*)(qbuf + col * LD::KPITCH + pc * 16) = hi;
+        *(vec8*)(qbuf + 16 * LD::KPITCH + col * LD::KPITCH + pc * 16) = lo;
     }
+    __syncthreads();
 
     float m = kNegInf;                      // head n: running max (same in all four quads)
     float l = 0.0f;                         // head n: this lane's share of the sum
@@ -740,49 +746,38 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* smem,
     for (int tn = 0; tn < DT; ++tn) acc[tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (; base < stream_end; base += BLOCK_ROWS) {
-        // S^T tiles: row = position 4g+i of the tile, column = head n
-        f32x4 st[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            st[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const vec8 kb = MF::bits8(kr[t][kk]);
-                st[t] = MF::mma32(kb, qhi[kk], st[t]);
-                st[t] = MF::mma32(kb, qlo[kk], st[t]);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        issue_k(base + BLOCK_ROWS);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // V rows into this wave's LDS tile (8-byte stores: the pitch is 8 mod 16)
+        // stage this tile in LDS, then send the next tile's loads out
         lds_wave_fence();
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int u = 0; u < VL; ++u) {
-                u32x2* dst = (u32x2*)(vtile + (t * 16 + u * RPI + r) * VPITCH + c * 16);
-                dst[0] = u32x2{vr[t][u][0], vr[t][u][1]};
-                dst[1] = u32x2{vr[t][u][2], vr[t][u][3]};
-            }
+        for (int u = 0; u < VL; ++u) {
+            *(u32x4*)(ktile + (u * RPI + r) * LD::KPITCH + c * 16) = kr[u];
+            *(u32x4*)(vtile + (u * RPI + r) * LD::VPITCH + c * 16) = vr[u];
+        }
         __builtin_amdgcn_sched_barrier(0);
-        issue_v(base + BLOCK_ROWS);
+        issue(base + BLOCK_ROWS);
         __builtin_amdgcn_sched_barrier(0);
+        lds_wave_fence();
 
-        // online softmax per head (column n), over the 4*NT positions of this
-        // lane and the three other quads of the column
-        float s[NT][4];
+        // S^T: row = position 4g+i of the tile, column = head n
+        f32x4 st = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int kk = 0; kk < KK; ++kk) {
+            const int piece = (kk * 4 + g) * 16;
+            const vec8 ka = MF::bits8(*(const u32x4*)(ktile + n * LD::KPITCH + piece));
+            const vec8 qh = MF::bits8(*(const u32x4*)(qbuf + n * LD::KPITCH + piece));
+            const vec8 ql = MF::bits8(*(const u32x4*)(qbuf + 16 * LD::KPITCH + n * LD::KPITCH + piece));
+            st = MF::mma32(ka, qh, st);
+            st = MF::mma32(ka, ql, st);
+            // one step's operands live at a time (registers hold the next
+            // tile's loads and the accumulators)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // online softmax per head (column n) over the positions of the tile
+        float s[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s[t][i] = base + t * 16 + 4 * g + i < stream_end ? st[t][i] : kNegInf;
-        float mt = s[0][0];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[t][i]);
+        for (int i = 0; i < 4; ++i) s[i] = base + 4 * g + i < stream_end ? st[i] : kNegInf;
+        float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mn = fmaxf(m, mt);
@@ -791,48 +786,39 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* smem,
         m = mn;
         float ls = 0.0f;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[t][i] = fast_exp2(s[t][i] - ms);
-                ls += s[t][i];
-            }
+        for (int i = 0; i < 4; ++i) {
+            s[i] = fast_exp2(s[i] - ms);
+            ls += s[i];
+        }
         l = l * alpha + ls;
         // P as the A operand of O += P.V: row = head n, k = positions 4g+i
-        vec4 ph[NT], pl[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) MF::split4(s[t], ph[t], pl[t]);
-        // rescale O rows (heads 4g+i) by their heads' factors
+        vec4 ph, pl;
+        MF::split4(s, ph, pl);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float ai = __shfl(alpha, 4 * g + i);
 #pragma unroll
             for (int tn = 0; tn < DT; ++tn) acc[tn][i] *= ai;
         }
-        lds_wave_fence();
-        // P.V: B operand = V[position 4g+i][16*tn + n], read down the tile's columns
+        // B operand V[position 4g+i][16*tn + n]: one transposing read per
+        // 16 columns; lane n of group g names row 4g + n/4, columns 4(n%4)..+3
+        const unsigned char* vrow = vtile + (4 * g + (n >> 2)) * LD::VPITCH + (n & 3) * 8;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const unsigned char* col = vtile + (t * 16 + 4 * g) * VPITCH + n * 2;
-#pragma unroll
-            for (int tn = 0; tn < DT; ++tn) {
-                const unsigned char* q0 = col + tn * 32;
-                const uint32_t e0 = *(const uint16_t*)(q0);
-                const uint32_t e1 = *(const uint16_t*)(q0 + VPITCH);
-                const uint32_t e2 = *(const uint16_t*)(q0 + 2 * VPITCH);
-                const uint32_t e3 = *(const uint16_t*)(q0 + 3 * VPITCH);
-                const vec4 vb = MF::bits4(u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
-                acc[tn] = MF::mma16(ph[t], vb, acc[tn]);
-                acc[tn] = MF::mma16(pl[t], vb, acc[tn]);
-            }
+        for (int tn = 0; tn < DT; ++tn) {
+            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vrow + tn * 32));
+            const vec4 vb = __builtin_bit_cast(vec4, t);
+            acc[tn] = MF::mma16(ph, vb, acc[tn]);
+            acc[tn] = MF::mma16(pl, vb, acc[tn]);
+            if (tn & 1) __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // l over the four quads of the column
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    __syncthreads();                        // every wave is done with its V tile
-    float* sm_o = (float*)smem;             // [NW + 1][HP][D]
+    __syncthreads();                        // every wave is done with its tiles
+    float* sm_o = (float*)tiles;            // [NW + 1][HP][D]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * g + i;
@@ -887,45 +873,59 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* smem,
     return owns_new ? NW + 1 : NW;
 }
 
-// Grouped-query pass with a balanced schedule.  The work of a step is the
-// concatenation over units u = (b, j, hgi) of L_b positions each; workgroup
-// i takes the slice [i*W, (i+1)*W) of it, W = max(ceil(total / grid),
-// seg_min) rounded to 16, whatever the lengths, so every workgroup streams
-// the same number of rows.  A slice crossing units is several segments.
-// Each segment's state is written to the unit's partial slot; the last
-// workgroup to finish a unit (an atomic count per unit, device-scope
-// fences around it) merges the unit's partials into `out` and clears the
-// count for the next call.  A unit inside one segment writes `out` directly.
-template <int KV, int D, int HP, int NT, int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
-gqa_kernel(const Params p) {
+// Grouped-query pass with a balanced schedule.  The work of a step is L_b
+// positions for each unit u = (b, j, hgi).  With W = max(seg_min,
+// ceil(total / target)) the units of sequence b are cut into
+// n_b = max(1, round(L_b / W)) near-equal pieces, one workgroup per piece,
+// so every workgroup streams about W rows whatever the lengths, and each
+// streams a single piece (one prologue, one epilogue).  The grid has
+// target + units workgroups, at least the number of pieces; the rest exit.
+// A unit in one piece writes `out` directly.  Otherwise each piece writes
+// its state to the unit's partial slot, and the last piece to finish (an
+// atomic count per unit) merges the slots into `out` and clears the count
+// for the next call.  Partials move between XCDs as device-coherent
+// accesses, so no cache-wide writeback or invalidate is needed.
+template <int KV, int D, int HP, int NW>
+__global__ void __launch_bounds__(64 * NW) gqa_kernel(const Params p) {
     using A = Act<KV>;
+    using LD = GqaLds<D>;
     constexpr int NTH = 64 * NW;
-    constexpr int V_BYTES = 16 * NT * (D * 2 + 8);
     constexpr int O_BYTES = (NW + 1) * HP * D * 4;
     static_assert(HP == 4 || HP == 8, "4 or 8 heads per pass");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[cmax(NW * V_BYTES, O_BYTES)];
+    // per-wave tiles while streaming; the merge buffers afterwards
+    __shared__ __attribute__((aligned(16))) unsigned char smem[cmax(NW * LD::WAVE, O_BYTES)];
+    __shared__ __attribute__((aligned(16))) unsigned char qbuf[LD::QBYTES];
     __shared__ float sm_m[NW + 1][HP];      // slot NW: the appended row
     __shared__ float sm_l[NW + 1][HP];
-    __shared__ int sm_pref[kGqaMaxBatch + 1];   // work offset of each sequence
+    __shared__ int sm_pref[kGqaMaxBatch + 1];   // first piece of each sequence
+    __shared__ int sm_len[kGqaMaxBatch];
     __shared__ int sm_last;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int upb = p.Hkv * p.n_hg;         // units per sequence
+    const int target = gridDim.x - p.B * upb;
 
-    // per-sequence work (valid length * units), then its exclusive prefix
+    // valid lengths, total work, slice length W, pieces per unit n_b and
+    // their exclusive prefix (in workgroups)
     for (int i = threadIdx.x; i < p.B; i += NTH) {
         const int Lb = p.seq_lens ? p.seq_lens[i] : p.step;
-        sm_pref[i + 1] = (Lb >= 1 && Lb <= p.step) ? Lb * upb : 0;
+        sm_len[i] = (Lb >= 1 && Lb <= p.step) ? Lb : 0;
     }
     __syncthreads();
     if (wave == 0) {
+        int tot = 0;
+        for (int base = 0; base < p.B; base += 64) tot += base + lane < p.B ? sm_len[base + lane] : 0;
+        tot = __builtin_amdgcn_readfirstlane(wave_sum_int(tot));
+        const long long total = (long long)tot * upb;
+        int W = (int)((total + target - 1) / max(target, 1));
+        W = max(W, p.seg_min);
         int carry = 0;
         for (int base = 0; base < p.B; base += 64) {
             const int idx = base + lane;
-            int v = idx < p.B ? sm_pref[idx + 1] : 0;
+            const int Lb = idx < p.B ? sm_len[idx] : 0;
+            int v = Lb > 0 ? max(1, (Lb + W / 2) / W) * upb : 0;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int t = __shfl_up(v, off);
@@ -940,129 +940,115 @@ gqa_kernel(const Params p) {
 
     // NaN rows for sequences whose length is invalid (no append for them)
     for (int bb = blockIdx.x; bb < p.B; bb += gridDim.x) {
-        if (sm_pref[bb + 1] == sm_pref[bb])
+        if (sm_len[bb] == 0)
             for (int idx = threadIdx.x; idx < p.H * D; idx += NTH)
                 A::st(p.out, (size_t)bb * p.H * D + idx, __builtin_nanf(""));
     }
-    const int total = sm_pref[p.B];
-    if (total == 0) return;
-    int W = (total + gridDim.x - 1) / gridDim.x;
-    W = max((W + 15) / 16 * 16, p.seg_min);
-    int st = blockIdx.x * W;
-    const int en = min(st + W, total);
+    const int blk = blockIdx.x;
+    if (blk >= sm_pref[p.B]) return;
 
-    float* sm_o = (float*)smem;
-    while (st < en) {
-        // the sequence holding work offset st: largest b with pref[b] <= st
-        int lo = 0, hi = p.B;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (sm_pref[mid] <= st) lo = mid;
-            else hi = mid;
-        }
-        const int b = lo;
-        const int L = (sm_pref[b + 1] - sm_pref[b]) / upb;
-        const int off = st - sm_pref[b];
-        const int ub = off / L;             // unit within the sequence: j * n_hg + hgi
-        const int pos0 = off - ub * L;
-        const int pos1 = min(L, pos0 + (en - st));
-        const int j = ub / p.n_hg;
-        const int hgi = ub - j * p.n_hg;
-        const int h0 = j * p.G + hgi * HP;
-        const int heads_here = min(HP, p.G - hgi * HP);
-        const int unit = b * upb + ub;
-        const int wu = sm_pref[b] + ub * L;     // work offset of the unit
-        const int first = wu / W;
-        const int nseg = (wu + L - 1) / W - first + 1;
-        const int seg = blockIdx.x - first;
-
-        const int n_states = gqa_segment<KV, D, HP, NT, NW>(p, smem, sm_m, sm_l, b, j, hgi, L, pos0, pos1);
-
-        // merge this workgroup's states; write out, or the unit's partial slot
-        for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
-            const int h = idx / D;
-            const int d = idx - h * D;
-            if (h >= heads_here) continue;
-            float M = sm_m[0][h];
-            for (int w = 1; w < n_states; ++w) M = fmaxf(M, sm_m[w][h]);
-            const float ms = M == kNegInf ? 0.0f : M;
-            float lsum = 0.0f, o = 0.0f;
-            for (int w = 0; w < n_states; ++w) {
-                const float a = fast_exp2(sm_m[w][h] - ms);
-                lsum += a * sm_l[w][h];
-                o += a * sm_o[(w * HP + h) * D + d];
-            }
-            if (nseg == 1) {
-                A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o / lsum);
-            } else {
-                const size_t slot = ((size_t)unit * p.seg_max + seg) * HP + h;
-                coherent_store(&p.ws_o[slot * D + d], o);
-                if (d == 0) {
-                    coherent_store(&p.ws_ml[slot * 2], M);
-                    coherent_store(&p.ws_ml[slot * 2 + 1], lsum);
-                }
-            }
-        }
-        if (nseg > 1) {
-            // partials are written through to the device coherence point; once
-            // every thread's stores are acknowledged the unit's count goes up,
-            // and the workgroup that completes it reads the partials back
-            // coherently.  No cache-wide writeback or invalidate is needed.
-            wait_stores();
-            __syncthreads();
-            if (threadIdx.x == 0)
-                sm_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT) == nseg - 1;
-            __syncthreads();
-            if (sm_last) {
-                // one parallel round for the slices' (m, l), kept in LDS as
-                // rescale factors; then each output sums its slices with
-                // independent loads
-                const size_t slot0 = (size_t)unit * p.seg_max * HP;
-                float* sm_a = (float*)smem;         // [seg_max][HP] weights 2^(m_k - M)
-                float* sm_ls = sm_a + p.seg_max * HP;   // [HP] 1 / sum_k 2^(m_k - M) l_k
-                float* sm_ms = sm_ls + HP;              // [seg_max][HP] raw m_k, then l_k
-                for (int t = threadIdx.x; t < nseg * HP; t += NTH) {
-                    sm_ms[t] = coherent_load(&p.ws_ml[(slot0 + t) * 2]);
-                    sm_a[t] = coherent_load(&p.ws_ml[(slot0 + t) * 2 + 1]);
-                }
-                __syncthreads();
-                if (threadIdx.x < HP) {
-                    const int h = threadIdx.x;
-                    float M = kNegInf;
-                    for (int k = 0; k < nseg; ++k) M = fmaxf(M, sm_ms[k * HP + h]);
-                    float lsum = 0.0f;
-                    for (int k = 0; k < nseg; ++k) {
-                        const float a = fast_exp2(sm_ms[k * HP + h] - M);
-                        lsum += a * sm_a[k * HP + h];
-                        sm_ms[k * HP + h] = a;
-                    }
-                    sm_ls[h] = 1.0f / lsum;
-                }
-                __syncthreads();
-                for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
-                    const int h = idx / D;
-                    const int d = idx - h * D;
-                    if (h >= heads_here) continue;
-                    float o = 0.0f;
-                    int k = 0;
-                    for (; k + 4 <= nseg; k += 4) {
-                        float v[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) v[q] = coherent_load(&p.ws_o[(slot0 + (size_t)(k + q) * HP + h) * D + d]);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) o += sm_ms[(k + q) * HP + h] * v[q];
-                    }
-                    for (; k < nseg; ++k) o += sm_ms[k * HP + h] * coherent_load(&p.ws_o[(slot0 + (size_t)k * HP + h) * D + d]);
-                    A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o * sm_ls[h]);
-                }
-                if (threadIdx.x == 0)
-                    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();                    // LDS is reused by the next segment
-        st += pos1 - pos0;
+    // this workgroup's piece: sequence b with pref[b] <= blk < pref[b+1]
+    int lo = 0, hi = p.B;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm_pref[mid] <= blk) lo = mid;
+        else hi = mid;
     }
+    const int b = lo;
+    const int L = sm_len[b];
+    const int nseg = (sm_pref[b + 1] - sm_pref[b]) / upb;
+    const int local = blk - sm_pref[b];
+    const int ub = local / nseg;            // unit within the sequence: j * n_hg + hgi
+    const int seg = local - ub * nseg;
+    const int pos0 = (int)((long long)seg * L / nseg);
+    const int pos1 = (int)((long long)(seg + 1) * L / nseg);
+    const int j = ub / p.n_hg;
+    const int hgi = ub - j * p.n_hg;
+    const int h0 = j * p.G + hgi * HP;
+    const int heads_here = min(HP, p.G - hgi * HP);
+    const int unit = b * upb + ub;
+
+    const int n_states = gqa_segment<KV, D, HP, NW>(p, smem, qbuf, sm_m, sm_l, b, j, hgi, L, pos0, pos1);
+    float* sm_o = (float*)smem;
+
+    // merge this workgroup's states; write out, or the unit's partial slot
+    for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        if (h >= heads_here) continue;
+        float M = sm_m[0][h];
+        for (int w = 1; w < n_states; ++w) M = fmaxf(M, sm_m[w][h]);
+        const float ms = M == kNegInf ? 0.0f : M;
+        float lsum = 0.0f, o = 0.0f;
+        for (int w = 0; w < n_states; ++w) {
+            const float a = fast_exp2(sm_m[w][h] - ms);
+            lsum += a * sm_l[w][h];
+            o += a * sm_o[(w * HP + h) * D + d];
+        }
+        if (nseg == 1) {
+            A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o / lsum);
+        } else {
+            const size_t slot = ((size_t)unit * p.seg_max + seg) * HP + h;
+            coherent_store(&p.ws_o[slot * D + d], o);
+            if (d == 0) {
+                coherent_store(&p.ws_ml[slot * 2], M);
+                coherent_store(&p.ws_ml[slot * 2 + 1], lsum);
+            }
+        }
+    }
+    if (nseg == 1) return;
+    // partials are written through to the device coherence point; once every
+    // thread's stores are acknowledged the unit's count goes up, and the
+    // workgroup that completes it reads the partials back coherently
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        sm_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == nseg - 1;
+    __syncthreads();
+    if (!sm_last) return;
+    // one parallel round for the pieces' (m, l), kept in LDS as rescale
+    // factors; then each output sums its pieces with independent loads
+    const size_t slot0 = (size_t)unit * p.seg_max * HP;
+    float* sm_a = (float*)smem;             // [seg_max][HP]: l_k, then the weights 2^(m_k - M)
+    float* sm_ls = sm_a + p.seg_max * HP;   // [HP]: 1 / sum_k 2^(m_k - M) l_k
+    float* sm_ms = sm_ls + HP;              // [seg_max][HP]: m_k
+    for (int t = threadIdx.x; t < nseg * HP; t += NTH) {
+        sm_ms[t] = coherent_load(&p.ws_ml[(slot0 + t) * 2]);
+        sm_a[t] = coherent_load(&p.ws_ml[(slot0 + t) * 2 + 1]);
+    }
+    __syncthreads();
+    if (threadIdx.x < HP) {
+        const int h = threadIdx.x;
+        float M = kNegInf;
+        for (int k = 0; k < nseg; ++k) M = fmaxf(M, sm_ms[k * HP + h]);
+        float lsum = 0.0f;
+        for (int k = 0; k < nseg; ++k) {
+            const float a = fast_exp2(sm_ms[k * HP + h] - M);
+            lsum += a * sm_a[k * HP + h];
+            sm_a[k * HP + h] = a;
+        }
+        sm_ls[h] = 1.0f / lsum;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        if (h >= heads_here) continue;
+        float o = 0.0f;
+        int k = 0;
+        for (; k + 4 <= nseg; k += 4) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = coherent_load(&p.ws_o[(slot0 + (size_t)(k + q) * HP + h) * D + d]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o += sm_a[(k + q) * HP + h] * v[q];
+        }
+        for (; k < nseg; ++k) o += sm_a[k * HP + h] * coherent_load(&p.ws_o[(slot0 + (size_t)k * HP + h) * D + d]);
+        A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o * sm_ls[h]);
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1109,13 +1095,12 @@ constexpr int unroll_for(int gt) { return gt <= 2 ? 8 : 4; }
 // of the fp32/fp16/bf16 caches fit without spilling.
 constexpr bool wide_built(int kv, int gt) { return gt == 1 && kv != KV_I8; }
 
-constexpr int kGqaTiles = 2;   // 16-position tiles per wave per iteration
 constexpr int kGqaWaves = 4;
-constexpr int kGqaBlocksPerCu = 2;   // resident at up to 256 registers per lane
+constexpr int kGqaBlocksPerCu = 2;   // target pieces per CU (3 fit: about 47 KiB of LDS and 140 registers each)
 
 template <int KV, int D, int HP>
 hipError_t launch_gqa_t(const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((gqa_kernel<KV, D, HP, kGqaTiles, kGqaWaves>), dim3(p.S), dim3(64 * kGqaWaves), 0, s, p);
+    hipLaunchKernelGGL((gqa_kernel<KV, D, HP, kGqaWaves>), dim3(p.S), dim3(64 * kGqaWaves), 0, s, p);
     return hipGetLastError();
 }
 

@@ -362,11 +362,12 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
     if (balanced) {
         // grouped heads on the matrix cores: a fixed grid sharing the total
         // work evenly; partial slots per unit, merged in the same launch
-        p.S = cu_count(device) * ftm::gqa_blocks_per_cu();
+        // target pieces (about W rows each) plus one spare per unit for rounding
+        p.S = cu_count(device) * ftm::gqa_blocks_per_cu() + units;
         p.chunk = 0;
         p.direct = 0;
-        // slices of at least 256 positions, and at most 200 slots per unit
-        // (the merge keeps a unit's slice statistics in LDS)
+        // pieces of at least 256 positions, and at most 200 per unit (the
+        // merge keeps a unit's piece statistics in LDS)
         p.seg_min = std::max(256, (step + 198) / 199);
         p.seg_max = (step + p.seg_min - 1) / p.seg_min + 1;
         const size_t slots = (size_t)units * p.seg_max * gtile;

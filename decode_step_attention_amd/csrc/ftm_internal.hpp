@@ -44,7 +44,7 @@ int group_tile(int G);
 int tile_rows(int kv, int head_dim, int group_tile, int nw);
 // Whether a pass of `group_tile` heads over this cache type runs on the
 // matrix cores with the balanced schedule (fp16/bf16 caches, 4 or 8 heads,
-// batch <= 1024; FTM_GQA_VALU=1 turns it off).
+// batch <= 256; FTM_GQA_VALU=1 turns it off).
 bool use_gqa_mfma(int kv, int group_tile, int batch);
 // Workgroups per CU of the grouped-query pass.
 int gqa_blocks_per_cu();
