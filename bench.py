@@ -41,10 +41,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(config: str):
-    """HBM bytes per launch of the attention kernel from the committed
+def dominant_kernel(case: W.Case) -> str:
+    """The kernel that streams the cache for this workload: grouped heads
+    (3 or more per KV head) over fp16/bf16 caches run on the matrix cores
+    (batch up to 256), everything else on the vector-ALU pass."""
+    if (case.kv_dtype in ("f16", "bf16") and case.group >= 3 and case.batch <= 256
+            and os.environ.get("FTM_GQA_VALU") != "1"):
+        return "gqa_kernel"
+    return "attention_kernel"
+
+
+def read_traffic(kernel: str, config: str):
+    """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_attention_{config}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{config}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -208,11 +218,12 @@ def main():
         avg_att_us = per_launch_us
         timing = "event pair around every attention launch in timed region 2"
     achieved = kv_layer / (avg_att_us * 1e-6) / 1e9
-    traffic = read_traffic(args.config)
+    kernel = dominant_kernel(case)
+    traffic = read_traffic(kernel, args.config)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
-            "kernel": "attention_kernel", "avg_launch_us": round(avg_att_us, 2),
+            "kernel": kernel, "avg_launch_us": round(avg_att_us, 2),
             "avg_launch_us_per_launch_events": round(per_launch_us, 2), "timing": timing,
             "launches": n_att, "algorithmic_bytes_per_launch": kv_layer}
     result = {

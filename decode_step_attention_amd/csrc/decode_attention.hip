@@ -327,15 +327,23 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
     const auto vsrs = make_rsrc(I8 ? p.kv_scales + plane + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
 
     u32x4 kr[U], vr[U];
-    float ksc[U], vsc[U];
+    // INT8 scales: the WAVE_ROWS scales of an iteration are contiguous, so
+    // lane l loads the scale of row l (one coalesced load per 64 rows) and
+    // the lanes holding a row fetch it with a cross-lane read at use
+    constexpr int NS = (WAVE_ROWS + 63) / 64;
+    float ks_all[NS], vs_all[NS];
+    // lanes past the iteration's rows point outside the descriptor: no fetch
+    auto scale_off = [&](int base, int i) {
+        return i * 64 + lane < WAVE_ROWS ? (base + i * 64 + lane) * 4 : 0x7fffffff;
+    };
     auto issue_k = [&](int base) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
         if constexpr (I8) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                ksc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, (base + u * RPI + r) * 4, 0, kStream));
+            for (int i = 0; i < NS; ++i)
+                ks_all[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, scale_off(base, i), 0, kStream));
         }
     };
     auto issue_v = [&](int base) {
@@ -344,9 +352,13 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
             vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
         if constexpr (I8) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                vsc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, (base + u * RPI + r) * 4, 0, kStream));
+            for (int i = 0; i < NS; ++i)
+                vs_all[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, scale_off(base, i), 0, kStream));
         }
+    };
+    // scale of row u*RPI + r of this iteration (64 is a multiple of RPI)
+    auto row_scale = [&](const float* all, int u) {
+        return __shfl(all[(u * RPI) / 64], (u * RPI) % 64 + r);
     };
 
     // the first K/V loads go out before the query is read, so their latency
@@ -393,13 +405,15 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
             float x[EPL];
             E::unpack(kr[u], x);
             const bool valid = base + u * RPI + r < stream_end;
+            float ksu = 1.0f;
+            if constexpr (I8) ksu = row_scale(ks_all, u);
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
                 float d = 0.0f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) d = fmaf(qv[g][e], x[e], d);
                 d = group_sum<LPR>(d);
-                if constexpr (I8) d *= ksc[u];
+                if constexpr (I8) d *= ksu;
                 s[g][u] = valid ? d : kNegInf;
             }
         }
@@ -431,10 +445,12 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
         for (int u = 0; u < U; ++u) {
             float x[EPL];
             E::unpack(vr[u], x);
+            float vsu = 1.0f;
+            if constexpr (I8) vsu = row_scale(vs_all, u);
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
                 float w = s[g][u];
-                if constexpr (I8) w *= vsc[u];
+                if constexpr (I8) w *= vsu;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(w, x[e], o[g][e]);
             }
