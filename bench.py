@@ -9,7 +9,10 @@ workload.  Inputs are seeded synthetic tensors already resident in HBM; the
 layer caches rotate so that the working set exceeds the 256 MB last-level
 cache.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config 7b]
+    python bench.py [--steps K] [--warmup W] [--config 7b] [--graph]
+
+--graph records each step's calls once into a HIP graph (ftm_graph_*) and
+times graph replays instead of one library call per layer.
 """
 from __future__ import annotations
 
@@ -80,6 +83,7 @@ def cpu_baseline(case, inputs, lens, budget_s: float):
     act, kvd = case.act_dtype, case.kv_dtype
     per_seq = case.n_kv_heads * 2 * case.max_seq_len * case.head_dim * W.ELEM_BYTES[kvd]
     nb = int(max(1, min(case.batch, (512 << 20) // per_seq)))
+    paged = case.page_size > 0
 
     def host(t, dt):
         t = t.detach().contiguous().cpu()
@@ -90,9 +94,15 @@ def cpu_baseline(case, inputs, lens, budget_s: float):
     kn = host(inp["k_new"][:nb], act)
     vn = host(inp["v_new"][:nb], act)
     bias = host(inp["bias"], act)
-    kc0 = host(inp["k_cache"][:nb], kvd)
-    vc0 = host(inp["v_cache"][:nb], kvd)
-    sc0 = host(inp["kv_scales"][:, :nb], "f32") if kvd == "i8" else None
+    if paged:
+        kc0 = host(inp["k_pages"], kvd)
+        vc0 = host(inp["v_pages"], kvd)
+        table = host(inp["block_table"][:nb], "i32")
+        sc0 = host(inp["kv_scales"], "f32") if kvd == "i8" else None
+    else:
+        kc0 = host(inp["k_cache"][:nb], kvd)
+        vc0 = host(inp["v_cache"][:nb], kvd)
+        sc0 = host(inp["kv_scales"][:, :nb], "f32") if kvd == "i8" else None
     sl = np.ascontiguousarray(lens[:nb].astype(np.int32))
     step = int(sl.max())
     sample_bytes = int(W.kv_bytes(case.with_(batch=nb), sl.tolist()))
@@ -102,7 +112,11 @@ def cpu_baseline(case, inputs, lens, budget_s: float):
         kc, vc = kc0.copy(), vc0.copy()
         sc = sc0.copy() if sc0 is not None else None
         t0 = time.perf_counter()
-        oracle.decode_mha(q, kn, vn, bias, kc, vc, sl, step, H, Hkv, D, kvd, sc, n_threads=ncores)
+        if paged:
+            oracle.decode_mha_paged(q, kn, vn, bias, kc, vc, table, sl, step, H, Hkv, D, kvd, sc,
+                                    n_threads=ncores)
+        else:
+            oracle.decode_mha(q, kn, vn, bias, kc, vc, sl, step, H, Hkv, D, kvd, sc, n_threads=ncores)
         dt = time.perf_counter() - t0
         best = min(best, dt)
         total += dt
@@ -121,6 +135,8 @@ def main():
     ap.add_argument("--config", default="7b", choices=sorted(W.CASES))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0 skips it)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a HIP graph instead of one call per layer")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -137,21 +153,30 @@ def main():
     rotate = max(case.rotate, layers)
     lens = W.seq_lens(case)
     print(f"# {describe(case)}; {rotate} cache sets; generating inputs", file=sys.stderr, flush=True)
-    inputs = [W.make_inputs(case, dev, layer=i, poison=False, lens=lens) for i in range(rotate)]
+    make = W.make_paged_inputs if case.page_size else W.make_inputs
+    inputs = [make(case, dev, layer=i, poison=False, lens=lens) for i in range(rotate)]
     outs = [torch.empty((case.batch, case.n_heads, case.head_dim),
                         dtype=W.TORCH_DTYPES[case.act_dtype], device=dev) for _ in range(2)]
     step = int(lens.max())
     lens_np = lens.numpy()
     kv_layer = W.kv_bytes(case, lens_np.tolist())
     kv_step = kv_layer * layers
-    stream = torch.cuda.current_stream(dev)
+    # graph capture needs a created stream (the null stream cannot be captured)
+    stream = torch.cuda.Stream(dev) if args.graph else torch.cuda.current_stream(dev)
 
     # one prepared call per (cache set, output buffer): the per-step host work
     # is a single C call, so the GPU is never waiting on Python
-    calls = [[ftm.ftm_decode_mha_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"],
-                                          inp["k_cache"], inp["v_cache"], inp["seq_lens"], step,
-                                          outs[o], inp.get("kv_scales"), stream=stream.cuda_stream)
-              for o in range(2)] for inp in inputs]
+    def prepare(inp, out):
+        if case.page_size:
+            return ftm.ftm_decode_mha_paged_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"],
+                                                     inp["k_pages"], inp["v_pages"], inp["block_table"],
+                                                     inp["seq_lens"], step, out, inp.get("kv_scales"),
+                                                     stream=stream.cuda_stream)
+        return ftm.ftm_decode_mha_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"],
+                                           inp["k_cache"], inp["v_cache"], inp["seq_lens"], step,
+                                           out, inp.get("kv_scales"), stream=stream.cuda_stream)
+
+    calls = [[prepare(inp, outs[o]) for o in range(2)] for inp in inputs]
 
     def call(i):
         calls[i % rotate][i & 1]()
@@ -177,33 +202,71 @@ def main():
             call(k)
             k += 1
     torch.cuda.synchronize()
+
+    # kernels one step launches (the attention pass, plus the combine when
+    # the sequences are split)
+    ftm.ftm_timing_enable(layers + 8)
+    for _l in range(layers):
+        call(k)
+        k += 1
+    torch.cuda.synchronize()
+    kernels_per_step = ftm.ftm_timing_read(0)[0] + ftm.ftm_timing_read(1)[0]
+    ftm.ftm_timing_disable()
+
+    graphs = []
+    if args.graph:
+        # one graph per distinct step: the step's layer calls on its cache
+        # sets, captured after the warm-up has sized the stream's workspace
+        n_graphs = max(1, rotate // layers)
+        for gi in range(n_graphs):
+            ftm.ftm_graph_begin(stream.cuda_stream)
+            try:
+                for lyr in range(layers):
+                    calls[(gi * layers + lyr) % rotate][0]()
+            finally:
+                graphs.append(ftm.ftm_graph_end(stream.cuda_stream))
+        for gi in range(min(args.warmup, len(graphs) * 4)):
+            ftm.ftm_graph_launch(graphs[gi % len(graphs)], stream.cuda_stream)
+        torch.cuda.synchronize()
+
+    def run_step(i):
+        nonlocal k
+        if graphs:
+            ftm.ftm_graph_launch(graphs[i % len(graphs)], stream.cuda_stream)
+            return
+        for _l in range(layers):
+            call(k)
+            k += 1
+
     # timed region 1: the whole path, nothing else on the stream; a HIP event
     # pair on the launch stream brackets the region
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     r0.record(stream)
-    for _ in range(args.steps):
-        for _l in range(layers):
-            call(k)
-            k += 1
+    for i in range(args.steps):
+        run_step(i)
     r1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     region_gpu_ms = r0.elapsed_time(r1)
-    # timed region 2: the same steps with a HIP event pair recorded around
-    # every kernel launch, on the launch stream, for per-kernel durations
-    ftm.ftm_timing_enable(args.steps * layers + 8)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        for _l in range(layers):
-            call(k)
-            k += 1
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    n_att, ms_att = ftm.ftm_timing_read(0)
-    n_cmb, ms_cmb = ftm.ftm_timing_read(1)
-    ftm.ftm_timing_disable()
+    n_att = n_cmb = 0
+    ms_att = ms_cmb = 0.0
+    t2 = t3 = 0.0
+    if not graphs:
+        # timed region 2: the same steps with a HIP event pair recorded around
+        # every kernel launch, on the launch stream, for per-kernel durations
+        ftm.ftm_timing_enable(args.steps * layers + 8)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for i in range(args.steps):
+            run_step(i)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        n_att, ms_att = ftm.ftm_timing_read(0)
+        n_cmb, ms_cmb = ftm.ftm_timing_read(1)
+        ftm.ftm_timing_disable()
+    for g in graphs:
+        ftm.ftm_graph_destroy(g)
     elapsed = t1 - t0
     ms_step = elapsed * 1e3 / args.steps
     gbs = kv_step * args.steps / elapsed / 1e9
@@ -213,7 +276,8 @@ def main():
         # region time over the launches (an event pair around every launch
         # adds its own dispatch and release time, a few us)
         avg_att_us = region_gpu_ms * 1e3 / (args.steps * layers)
-        timing = "events bracketing timed region 1 / launches (one kernel per step)"
+        timing = ("events bracketing timed region 1 (graph replays) / layer launches" if graphs
+                  else "events bracketing timed region 1 / launches (one kernel per step)")
     else:
         avg_att_us = per_launch_us
         timing = "event pair around every attention launch in timed region 2"
@@ -225,7 +289,8 @@ def main():
             "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
             "kernel": kernel, "avg_launch_us": round(avg_att_us, 2),
             "avg_launch_us_per_launch_events": round(per_launch_us, 2), "timing": timing,
-            "launches": n_att, "algorithmic_bytes_per_launch": kv_layer}
+            "launches": n_att if n_att else args.steps * layers,
+            "algorithmic_bytes_per_launch": kv_layer}
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -234,11 +299,15 @@ def main():
         "config": {"workload": describe(case), "batch": case.batch, "n_heads": case.n_heads,
                    "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim,
                    "context": step, "kv_dtype": case.kv_dtype, "act_dtype": case.act_dtype,
-                   "layers_per_step": layers, "cache_sets_rotated": rotate},
+                   "layers_per_step": layers, "cache_sets_rotated": rotate,
+                   "cache_layout": f"paged, {case.page_size}-token pages" if case.page_size else "contiguous",
+                   "launch": "HIP graph replay per step" if graphs else "one library call per layer"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(case.batch * args.steps / elapsed, 1),
         "kv_bytes_per_step": kv_step,
-        "ms_per_step_with_kernel_events": round((t3 - t2) * 1e3 / args.steps, 5),
+        "ms_per_step_with_kernel_events": round((t3 - t2) * 1e3 / args.steps, 5) if not graphs else None,
+        "kernels_per_step": kernels_per_step,
+        "gpu_ms_per_step": round(region_gpu_ms / args.steps, 5),
         "combine_avg_launch_us": round(ms_cmb * 1e3 / n_cmb, 2) if n_cmb else None,
         "device_copy_GBs": round(copy_gbs, 1),
         "roofline": roof,

@@ -206,6 +206,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0, n, kRsrcWord3);
 }
 
+// Paged cache: position `pos` of (sequence b, KV head j) is row pos mod P of
+// page tbl[pos / P] of a [n_pages, Hkv, P, row] pool (P a power of two; tbl
+// is sequence b's block-table row).  Descriptor starting at the row of
+// `pos` (wave-uniform) and covering the rows of its page that lie below
+// `end`: empty when pos >= end, zeros and `bad` set when the table names a
+// page outside the pool.  Branch-free: the table index is clamped to the
+// last page below `end`, so the entry read always lies in the row.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* pool, int row_bytes,
+                                                            const int32_t* tbl, const Params& p,
+                                                            int j, int pos, int end, bool& bad) {
+    const int sh = p.page_shift;
+    const int idx = min(pos >> sh, max(end - 1, 0) >> sh);
+    const int page = tbl[idx];
+    const int in_page = pos & ((1 << sh) - 1);
+    const bool valid = (unsigned)page < (unsigned)p.n_pages;
+    int rows = min(end - pos, (1 << sh) - in_page);
+    rows = rows > 0 ? rows : 0;
+    bad |= rows > 0 && !valid;
+    rows = valid ? rows : 0;
+    const size_t row = (((size_t)(valid ? page : 0) * p.Hkv + j) << sh) + in_page;
+    return make_rsrc((const char*)pool + row * row_bytes, (uint32_t)rows * (uint32_t)row_bytes);
+}
+
+// Where the appended row of (b, j) at position pnew lives: its row index in
+// the cache (or pool) and the element offset of the V plane of the INT8
+// scales.  Paged: false when the table names a page outside the pool.
+template <bool PG>
+__device__ __forceinline__ bool new_row_index(const Params& p, int b, int j, int pnew, size_t& row,
+                                              size_t& scale_plane) {
+    if constexpr (PG) {
+        const int page = p.block_table[(size_t)b * p.max_pages + (pnew >> p.page_shift)];
+        row = (((size_t)page * p.Hkv + j) << p.page_shift) + (pnew & ((1 << p.page_shift) - 1));
+        scale_plane = ((size_t)p.n_pages * p.Hkv) << p.page_shift;
+        return (unsigned)page < (unsigned)p.n_pages;
+    } else {
+        row = ((size_t)b * p.Hkv + j) * p.Lmax + pnew;
+        scale_plane = (size_t)p.B * p.Hkv * p.Lmax;
+        return true;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // The new row: x = fl32(new + bias), stored as the cache type.  `stored`
 // receives what the cache now holds, as fp32 (INT8: the code), `scale` the
@@ -270,7 +311,7 @@ __device__ __forceinline__ void make_new_row(const Params& p, const void* src, i
 // clipped by the buffer descriptor (they return zeros and fetch nothing), so
 // the prefetch after the last iteration costs issue slots only.
 // ---------------------------------------------------------------------------
-template <int KV, int D, int GT, int U, int NW>
+template <int KV, int D, int GT, int U, int NW, bool PG>
 __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
     using E = Elem<KV>;
     using A = Act<KV>;
@@ -289,7 +330,7 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
     __shared__ float sm_o[NW][GT][D];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane / LPR;               // row slot of this lane
     const int c = lane % LPR;               // 16-byte column slice of the row
     const int chunk = blockIdx.x;
@@ -316,49 +357,65 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
     const int stream_end = min(c1, L - 1);  // the new row L-1 comes from registers
     const bool owns_new = c1 == L;
 
-    const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;   // row 0 of this (b, j)
-    const char* kbase = (const char*)p.k_cache + row0 * ROW_BYTES;
-    const char* vbase = (const char*)p.v_cache + row0 * ROW_BYTES;
-    const uint32_t valid_bytes = (uint32_t)max(stream_end, 0) * ROW_BYTES;
-    const auto krs = make_rsrc(kbase, valid_bytes);
-    const auto vrs = make_rsrc(vbase, valid_bytes);
-    const size_t plane = (size_t)p.B * p.Hkv * p.Lmax;       // INT8 scale plane
-    const auto ksrs = make_rsrc(I8 ? p.kv_scales + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
-    const auto vsrs = make_rsrc(I8 ? p.kv_scales + plane + row0 : nullptr, I8 ? max(stream_end, 0) * 4 : 0);
+    // contiguous cache: one descriptor per stream over rows [0, stream_end)
+    // of this (b, j); paged: one per page, built where the rows are loaded
+    const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;   // contiguous: row 0 of this (b, j)
+    const uint32_t valid_bytes = PG ? 0u : (uint32_t)max(stream_end, 0) * ROW_BYTES;
+    const auto krs = make_rsrc(PG ? nullptr : (const char*)p.k_cache + row0 * ROW_BYTES, valid_bytes);
+    const auto vrs = make_rsrc(PG ? nullptr : (const char*)p.v_cache + row0 * ROW_BYTES, valid_bytes);
+    const size_t plane = PG ? ((size_t)p.n_pages * p.Hkv) << p.page_shift
+                            : (size_t)p.B * p.Hkv * p.Lmax;  // INT8 scale plane
+    const bool flat_i8 = I8 && !PG;
+    const auto ksrs = make_rsrc(flat_i8 ? p.kv_scales + row0 : nullptr, flat_i8 ? max(stream_end, 0) * 4 : 0);
+    const auto vsrs = make_rsrc(flat_i8 ? p.kv_scales + plane + row0 : nullptr, flat_i8 ? max(stream_end, 0) * 4 : 0);
+    const int32_t* tbl = PG ? p.block_table + (size_t)b * p.max_pages : nullptr;
+    bool bad = false;                       // paged: the table named a page outside the pool
 
     u32x4 kr[U], vr[U];
-    // INT8 scales: the WAVE_ROWS scales of an iteration are contiguous, so
-    // lane l loads the scale of row l (one coalesced load per 64 rows) and
-    // the lanes holding a row fetch it with a cross-lane read at use
-    constexpr int NS = (WAVE_ROWS + 63) / 64;
+    // INT8 scales, contiguous cache: the WAVE_ROWS scales of an iteration
+    // are contiguous, so lane l loads the scale of row l (one coalesced load
+    // per 64 rows) and the lanes holding a row fetch it with a cross-lane
+    // read at use.  Paged: the lanes of a row load its scale from the row's
+    // page, one load per RPI rows.
+    constexpr int NS = PG ? U : (WAVE_ROWS + 63) / 64;
     float ks_all[NS], vs_all[NS];
     // lanes past the iteration's rows point outside the descriptor: no fetch
     auto scale_off = [&](int base, int i) {
         return i * 64 + lane < WAVE_ROWS ? (base + i * 64 + lane) * 4 : 0x7fffffff;
     };
-    auto issue_k = [&](int base) {
+    // rows base + u*RPI .. + RPI-1 lie in one page (P >= 16 >= RPI, both
+    // powers of two, base a multiple of RPI)
+    auto issue_stream = [&](const void* pool, const __amdgpu_buffer_rsrc_t& rs,
+                            const __amdgpu_buffer_rsrc_t& srs, size_t splane, u32x4* dst,
+                            float* sdst, int base) {
+        if constexpr (PG) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
-        if constexpr (I8) {
+            for (int u = 0; u < U; ++u) {
+                const int pos = base + u * RPI;
+                const auto prs = page_rsrc(pool, ROW_BYTES, tbl, p, j, pos, stream_end, bad);
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(prs, r * ROW_BYTES + c * 16, 0, kStream);
+                if constexpr (I8) {
+                    const auto pss = page_rsrc(p.kv_scales + splane, 4, tbl, p, j, pos, stream_end, bad);
+                    sdst[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pss, r * 4, 0, kStream));
+                }
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < NS; ++i)
-                ks_all[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, scale_off(base, i), 0, kStream));
+            for (int u = 0; u < U; ++u)
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
+            if constexpr (I8) {
+#pragma unroll
+                for (int i = 0; i < NS; ++i)
+                    sdst[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, scale_off(base, i), 0, kStream));
+            }
         }
     };
-    auto issue_v = [&](int base) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (base + u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
-        if constexpr (I8) {
-#pragma unroll
-            for (int i = 0; i < NS; ++i)
-                vs_all[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, scale_off(base, i), 0, kStream));
-        }
-    };
+    auto issue_k = [&](int base) { issue_stream(p.k_cache, krs, ksrs, 0, kr, ks_all, base); };
+    auto issue_v = [&](int base) { issue_stream(p.v_cache, vrs, vsrs, plane, vr, vs_all, base); };
     // scale of row u*RPI + r of this iteration (64 is a multiple of RPI)
     auto row_scale = [&](const float* all, int u) {
-        return __shfl(all[(u * RPI) / 64], (u * RPI) % 64 + r);
+        if constexpr (PG) return all[u];
+        else return __shfl(all[(u * RPI) / 64], (u * RPI) % 64 + r);
     };
 
     // the first K/V loads go out before the query is read, so their latency
@@ -468,13 +525,16 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
         u32x4 kpk, vpk;
         make_new_row<KV, D, EPL, LPR>(p, p.k_new, p.H + j, src_row, c, kx, ks, kpk);
         make_new_row<KV, D, EPL, LPR>(p, p.v_new, p.H + p.Hkv + j, src_row, c, vx, vs, vpk);
-        if (hgi == 0 && r == 0) {
-            *(u32x4*)((char*)p.k_cache + (row0 + pnew) * ROW_BYTES + c * 16) = kpk;
-            *(u32x4*)((char*)p.v_cache + (row0 + pnew) * ROW_BYTES + c * 16) = vpk;
+        size_t nrow, splane;
+        const bool ok = new_row_index<PG>(p, b, j, pnew, nrow, splane);
+        if (!ok) bad = true;
+        if (ok && hgi == 0 && r == 0) {
+            *(u32x4*)((char*)p.k_cache + nrow * ROW_BYTES + c * 16) = kpk;
+            *(u32x4*)((char*)p.v_cache + nrow * ROW_BYTES + c * 16) = vpk;
             if constexpr (I8) {
                 if (c == 0) {
-                    p.kv_scales[row0 + pnew] = ks;
-                    p.kv_scales[plane + row0 + pnew] = vs;
+                    p.kv_scales[nrow] = ks;
+                    p.kv_scales[splane + nrow] = vs;
                 }
             }
         }
@@ -496,6 +556,13 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
                 m[g] = mn;
             }
         }
+    }
+
+    // a page outside the pool makes the result NaN (the sum carries it
+    // through every merge)
+    if (bad) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) l[g] = __builtin_nanf("");
     }
 
     // merge the row slots of each wave
@@ -679,7 +746,7 @@ template <int D> struct GqaLds {
 // hgi) streamed by the whole workgroup.  On return the workgroup's merged
 // state sits in LDS: n_states softmax states (m, l, o[HP][D]), one per wave
 // plus the appended row's when the segment holds it.
-template <int KV, int D, int HP, int NW>
+template <int KV, int D, int HP, int NW, bool PG>
 __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles, unsigned char* qbuf,
                                            float (*sm_m)[HP], float (*sm_l)[HP], int b, int j,
                                            int hgi, int L, int pos0, int pos1) {
@@ -698,7 +765,7 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
     constexpr int BLOCK_ROWS = NW * 16;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;                // MFMA layout: k-slot group, position quad
     const int n = lane & 15;                // MFMA layout: K row / head column / V column
     const int r = lane / LPR;               // load layout: row slot
@@ -708,21 +775,37 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
     const int stream_end = min(pos1, L - 1);
     const bool owns_new = pos1 == L;
 
+    // contiguous cache: one descriptor per stream over rows [0, stream_end)
+    // of this (b, j); paged: one per 16-position tile (tiles start at
+    // multiples of 16 and never straddle a page, P >= 16)
     const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;
-    const uint32_t valid_bytes = (uint32_t)max(stream_end, 0) * ROW_BYTES;
-    const auto krs = make_rsrc((const char*)p.k_cache + row0 * ROW_BYTES, valid_bytes);
-    const auto vrs = make_rsrc((const char*)p.v_cache + row0 * ROW_BYTES, valid_bytes);
+    const uint32_t valid_bytes = PG ? 0u : (uint32_t)max(stream_end, 0) * ROW_BYTES;
+    const auto krs = make_rsrc(PG ? nullptr : (const char*)p.k_cache + row0 * ROW_BYTES, valid_bytes);
+    const auto vrs = make_rsrc(PG ? nullptr : (const char*)p.v_cache + row0 * ROW_BYTES, valid_bytes);
+    const int32_t* tbl = PG ? p.block_table + (size_t)b * p.max_pages : nullptr;
+    bool bad = false;                       // paged: the table named a page outside the pool
     unsigned char* ktile = tiles + wave * LD::WAVE;
     unsigned char* vtile = ktile + 16 * LD::KPITCH;
 
     // K and V rows in the load layout: one wave-wide load is RPI whole rows
     u32x4 kr[VL], vr[VL];
     auto issue = [&](int base) {
+        if constexpr (PG) {
+            const auto kps = page_rsrc(p.k_cache, ROW_BYTES, tbl, p, j, base, stream_end, bad);
+            const auto vps = page_rsrc(p.v_cache, ROW_BYTES, tbl, p, j, base, stream_end, bad);
 #pragma unroll
-        for (int u = 0; u < VL; ++u) {
-            const int off = (base + u * RPI + r) * ROW_BYTES + c * 16;
-            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStream);
-            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStream);
+            for (int u = 0; u < VL; ++u) {
+                const int off = (u * RPI + r) * ROW_BYTES + c * 16;
+                kr[u] = __builtin_amdgcn_raw_buffer_load_b128(kps, off, 0, kStream);
+                vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vps, off, 0, kStream);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < VL; ++u) {
+                const int off = (base + u * RPI + r) * ROW_BYTES + c * 16;
+                kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStream);
+                vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStream);
+            }
         }
     };
     int base = pos0 + wave * 16;
@@ -845,7 +928,7 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
     }
     if (g == 0 && n < HP) {
         sm_m[wave][n] = m;
-        sm_l[wave][n] = l;
+        sm_l[wave][n] = bad ? __builtin_nanf("") : l;   // a page outside the pool: NaN result
     }
 
     // the appended row: stored by wave 0, and kept as one more softmax state
@@ -856,9 +939,11 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
         u32x4 kpk, vpk;
         make_new_row<KV, D, EPL, LPR>(p, p.k_new, p.H + j, src_row, c, kx, ks, kpk);
         make_new_row<KV, D, EPL, LPR>(p, p.v_new, p.H + p.Hkv + j, src_row, c, vx, vs, vpk);
-        if (hgi == 0 && r == 0) {
-            *(u32x4*)((char*)p.k_cache + (row0 + pnew) * ROW_BYTES + c * 16) = kpk;
-            *(u32x4*)((char*)p.v_cache + (row0 + pnew) * ROW_BYTES + c * 16) = vpk;
+        size_t nrow, splane;
+        const bool ok = new_row_index<PG>(p, b, j, pnew, nrow, splane);
+        if (ok && hgi == 0 && r == 0) {
+            *(u32x4*)((char*)p.k_cache + nrow * ROW_BYTES + c * 16) = kpk;
+            *(u32x4*)((char*)p.v_cache + nrow * ROW_BYTES + c * 16) = vpk;
         }
 #pragma unroll
         for (int h = 0; h < HP; ++h) {
@@ -878,7 +963,7 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
             if (r == 0) {
                 if (c == 0) {
                     sm_m[NW][h] = d;
-                    sm_l[NW][h] = 1.0f;
+                    sm_l[NW][h] = ok ? 1.0f : __builtin_nanf("");
                 }
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) sm_o[(NW * HP + h) * D + c * EPL + e] = vx[e];
@@ -901,7 +986,7 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
 // atomic count per unit) merges the slots into `out` and clears the count
 // for the next call.  Partials move between XCDs as device-coherent
 // accesses, so no cache-wide writeback or invalidate is needed.
-template <int KV, int D, int HP, int NW>
+template <int KV, int D, int HP, int NW, bool PG>
 __global__ void __launch_bounds__(64 * NW) gqa_kernel(const Params p) {
     using A = Act<KV>;
     using LD = GqaLds<D>;
@@ -976,15 +1061,16 @@ __global__ void __launch_bounds__(64 * NW) gqa_kernel(const Params p) {
     const int local = blk - sm_pref[b];
     const int ub = local / nseg;            // unit within the sequence: j * n_hg + hgi
     const int seg = local - ub * nseg;
-    const int pos0 = (int)((long long)seg * L / nseg);
-    const int pos1 = (int)((long long)(seg + 1) * L / nseg);
+    // piece boundaries on multiples of 16 (a tile never straddles a page)
+    const int pos0 = seg == 0 ? 0 : (int)((long long)seg * L / nseg) & ~15;
+    const int pos1 = seg == nseg - 1 ? L : (int)((long long)(seg + 1) * L / nseg) & ~15;
     const int j = ub / p.n_hg;
     const int hgi = ub - j * p.n_hg;
     const int h0 = j * p.G + hgi * HP;
     const int heads_here = min(HP, p.G - hgi * HP);
     const int unit = b * upb + ub;
 
-    const int n_states = gqa_segment<KV, D, HP, NW>(p, smem, qbuf, sm_m, sm_l, b, j, hgi, L, pos0, pos1);
+    const int n_states = gqa_segment<KV, D, HP, NW, PG>(p, smem, qbuf, sm_m, sm_l, b, j, hgi, L, pos0, pos1);
     float* sm_o = (float*)smem;
 
     // merge this workgroup's states; write out, or the unit's partial slot
@@ -1114,46 +1200,47 @@ constexpr bool wide_built(int kv, int gt) { return gt == 1 && kv != KV_I8; }
 constexpr int kGqaWaves = 4;
 constexpr int kGqaBlocksPerCu = 2;   // target pieces per CU (3 fit: about 47 KiB of LDS and 140 registers each)
 
-template <int KV, int D, int HP>
+template <int KV, int D, int HP, bool PG>
 hipError_t launch_gqa_t(const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((gqa_kernel<KV, D, HP, kGqaWaves>), dim3(p.S), dim3(64 * kGqaWaves), 0, s, p);
+    hipLaunchKernelGGL((gqa_kernel<KV, D, HP, kGqaWaves, PG>), dim3(p.S), dim3(64 * kGqaWaves), 0, s, p);
     return hipGetLastError();
 }
 
-template <int KV, int D, int GT>
+template <int KV, int D, int GT, bool PG>
 hipError_t launch_attention_t(const Params& p, int nw, hipStream_t s) {
     dim3 grid(p.S, p.Hkv * p.n_hg, p.B);
     if constexpr ((KV == KV_F16 || KV == KV_BF16) && (GT == 4 || GT == 8)) {
-        if (p.balanced) return launch_gqa_t<KV, D, GT>(p, s);
+        if (p.balanced) return launch_gqa_t<KV, D, GT, PG>(p, s);
     }
     constexpr int U = unroll_for(GT);
     if constexpr (wide_built(KV, GT)) {
         if (nw == 16) {
-            hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 16>), grid, dim3(64 * 16), 0, s, p);
+            hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 16, PG>), grid, dim3(64 * 16), 0, s, p);
             return hipGetLastError();
         }
     }
     if (nw != 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 4>), grid, dim3(64 * 4), 0, s, p);
+    hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 4, PG>), grid, dim3(64 * 4), 0, s, p);
     return hipGetLastError();
 }
 
-template <int KV, int D>
+template <int KV, int D, bool PG>
 hipError_t dispatch_gt(const Params& p, int gt, int nw, hipStream_t s) {
     switch (gt) {
-    case 1: return launch_attention_t<KV, D, 1>(p, nw, s);
-    case 2: return launch_attention_t<KV, D, 2>(p, nw, s);
-    case 4: return launch_attention_t<KV, D, 4>(p, nw, s);
-    case 8: return launch_attention_t<KV, D, 8>(p, nw, s);
+    case 1: return launch_attention_t<KV, D, 1, PG>(p, nw, s);
+    case 2: return launch_attention_t<KV, D, 2, PG>(p, nw, s);
+    case 4: return launch_attention_t<KV, D, 4, PG>(p, nw, s);
+    case 8: return launch_attention_t<KV, D, 8, PG>(p, nw, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int KV>
 hipError_t dispatch_d(const Params& p, int d, int gt, int nw, hipStream_t s) {
+    const bool pg = p.block_table != nullptr;
     switch (d) {
-    case 64: return dispatch_gt<KV, 64>(p, gt, nw, s);
-    case 128: return dispatch_gt<KV, 128>(p, gt, nw, s);
+    case 64: return pg ? dispatch_gt<KV, 64, true>(p, gt, nw, s) : dispatch_gt<KV, 64, false>(p, gt, nw, s);
+    case 128: return pg ? dispatch_gt<KV, 128, true>(p, gt, nw, s) : dispatch_gt<KV, 128, false>(p, gt, nw, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -36,21 +36,39 @@ struct Workspace {
     size_t bytes = 0;
     int* counters = nullptr;    // per-unit counts of the balanced schedule, zero between calls
     size_t n_counters = 0;
+    bool captured = false;      // a graph may hold these buffers: retire them, never free
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Buffers replaced while a captured graph may still use them; freed only
+// by ftm_release_workspaces.
+std::vector<std::pair<int, void*>> g_retired;
+
+// Frees `ptr`, or keeps it for ftm_release_workspaces when a graph may use it.
+hipError_t drop_buffer(int device, void* ptr, bool captured) {
+    if (captured) {
+        g_retired.push_back({device, ptr});
+        return hipSuccess;
+    }
+    return hipFree(ptr);
+}
 
 // Partials buffer of at least `bytes` and, when n_counters > 0, a zeroed
 // counter array of at least that many ints, for (device, stream).
-int get_workspace(int device, hipStream_t stream, size_t bytes, size_t n_counters, void** out,
-                  int** counters) {
+int get_workspace(int device, hipStream_t stream, size_t bytes, size_t n_counters, bool capturing,
+                  void** out, int** counters) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& w = g_ws[{device, stream}];
+    if (capturing && (w.bytes < bytes || w.n_counters < n_counters))
+        return fail(FTM_ERR_INVALID_ARG,
+                    "the stream is being captured and its workspace would have to grow: make one "
+                    "call of this shape on this stream before capturing");
+    if (capturing) w.captured = true;
     if (w.bytes < bytes) {
         if (w.ptr) {
             // hipFree waits for the device, so work still using the old
             // buffer has finished before it goes away
-            hipError_t e = hipFree(w.ptr);
+            hipError_t e = drop_buffer(device, w.ptr, w.captured);
             w.ptr = nullptr;
             w.bytes = 0;
             if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipFree: ") + hipGetErrorString(e));
@@ -67,7 +85,7 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t n_counter
     }
     if (w.n_counters < n_counters) {
         if (w.counters) {
-            hipError_t e = hipFree(w.counters);
+            hipError_t e = drop_buffer(device, w.counters, w.captured);
             w.counters = nullptr;
             w.n_counters = 0;
             if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipFree: ") + hipGetErrorString(e));
@@ -175,7 +193,27 @@ int cu_count(int device) {
     return n;
 }
 
+// Validated arguments of one decode step, contiguous or paged.
+struct Call {
+    const void *q, *k_new, *v_new, *qkv_bias;
+    void *k_cache, *v_cache;
+    const int32_t* seq_lens;
+    int batch, capacity, step, n_heads, n_kv_heads, head_dim, kv_dtype;
+    float* kv_scales;
+    void* out;
+    hipStream_t stream;
+    // paged
+    const int32_t* block_table;
+    int page_shift, max_pages, n_pages;
+};
+
 }  // namespace
+
+// A captured sequence of calls, instantiated for replay.
+struct ftm_graph_s {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
 
 extern "C" {
 
@@ -227,6 +265,14 @@ void ftm_release_workspaces(void) {
             (void)hipSetDevice(cur);
         }
     }
+    for (auto& r : g_retired) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(r.first);
+        (void)hipFree(r.second);
+        (void)hipSetDevice(cur);
+    }
+    g_retired.clear();
     g_ws.clear();
 }
 
@@ -279,22 +325,26 @@ int ftm_timing_read(int kind, int* launches, double* total_ms) {
     return FTM_OK;
 }
 
-int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
-                   void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
-                   int max_seq_len, int step, int n_heads, int n_kv_heads, int head_dim,
-                   int kv_dtype, float* kv_scales, void* out, void* stream_ptr) {
-    // ---- host-side checks: nothing is enqueued on failure ----
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both layouts; nothing is enqueued on failure.
+int check_common(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                 const void* k_cache, const void* v_cache, const int32_t* seq_lens, int batch,
+                 int capacity, int step, int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
+                 const float* kv_scales, const void* out, const char* capacity_name) {
     if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
         return fail(FTM_ERR_INVALID_ARG, "a required pointer (q, k_new, v_new, k_cache, v_cache, out) is NULL");
-    if (batch < 1 || max_seq_len < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
-        return fail(FTM_ERR_INVALID_ARG, "batch, max_seq_len, n_heads, n_kv_heads and head_dim must be >= 1");
+    if (batch < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
+        return fail(FTM_ERR_INVALID_ARG, "batch, n_heads, n_kv_heads and head_dim must be >= 1");
     if (n_heads % n_kv_heads != 0)
         return fail(FTM_ERR_INVALID_ARG, "n_heads (" + std::to_string(n_heads) +
                                              ") is not a multiple of n_kv_heads (" +
                                              std::to_string(n_kv_heads) + ")");
-    if (step < 1 || step > max_seq_len)
-        return fail(FTM_ERR_INVALID_ARG, "step " + std::to_string(step) + " outside [1, max_seq_len=" +
-                                             std::to_string(max_seq_len) + "]");
+    if (step < 1 || step > capacity)
+        return fail(FTM_ERR_INVALID_ARG, "step " + std::to_string(step) + " outside [1, " + capacity_name +
+                                             "=" + std::to_string(capacity) + "]");
     if (kv_dtype < FTM_F32 || kv_dtype > FTM_I8)
         return fail(FTM_ERR_INVALID_ARG, "unknown kv_dtype " + std::to_string(kv_dtype));
     if ((kv_dtype == FTM_I8) != (kv_scales != nullptr))
@@ -315,48 +365,69 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
     const int n_hg = (G + gtile - 1) / gtile;
     if ((long)n_kv_heads * n_hg > 65535 || batch > 65535)
         return fail(FTM_ERR_UNSUPPORTED, "grid too large: n_kv_heads * head groups and batch must be <= 65535");
-    const size_t elem = kv_dtype == FTM_F32 ? 4 : (kv_dtype == FTM_I8 ? 1 : 2);
-    if ((size_t)max_seq_len * head_dim * elem > 0x7fffffffu)
-        return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
+    return FTM_OK;
+}
 
-    hipStream_t stream = (hipStream_t)stream_ptr;
+size_t elem_bytes(int kv_dtype) { return kv_dtype == FTM_F32 ? 4 : (kv_dtype == FTM_I8 ? 1 : 2); }
+
+int decode_impl(const Call& a) {
+    hipStream_t stream = a.stream;
     int device = 0;
     hipError_t he = hipGetDevice(&device);
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
+    // under stream capture nothing may allocate, synchronise or record
+    // timing events: the workspace must already be large enough
+    bool capturing = false;
+    if (stream) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        he = hipStreamIsCapturing(stream, &cs);
+        if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipStreamIsCapturing: ") + hipGetErrorString(he));
+        capturing = cs != hipStreamCaptureStatusNone;
+    }
 
-    if (env_int("FTM_VALIDATE", 0) && seq_lens) {
-        std::vector<int32_t> h(batch);
-        he = hipMemcpyAsync(h.data(), seq_lens, sizeof(int32_t) * batch, hipMemcpyDeviceToHost, stream);
+    if (env_int("FTM_VALIDATE", 0) && a.seq_lens) {
+        if (capturing)
+            return fail(FTM_ERR_INVALID_ARG, "FTM_VALIDATE reads seq_lens on the host and cannot run under stream capture");
+        std::vector<int32_t> h(a.batch);
+        he = hipMemcpyAsync(h.data(), a.seq_lens, sizeof(int32_t) * a.batch, hipMemcpyDeviceToHost, stream);
         if (he == hipSuccess) he = hipStreamSynchronize(stream);
         if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("FTM_VALIDATE copy: ") + hipGetErrorString(he));
-        for (int b = 0; b < batch; ++b)
-            if (h[b] < 1 || h[b] > step)
+        for (int b = 0; b < a.batch; ++b)
+            if (h[b] < 1 || h[b] > a.step)
                 return fail(FTM_ERR_INVALID_ARG, "seq_lens[" + std::to_string(b) + "] = " +
                                                      std::to_string(h[b]) + " outside [1, step]");
     }
 
+    const int G = a.n_heads / a.n_kv_heads;
+    const int gtile = ftm::group_tile(G);
+    const int n_hg = (G + gtile - 1) / gtile;
     ftm::Params p{};
-    p.q = q;
-    p.k_new = k_new;
-    p.v_new = v_new;
-    p.bias = qkv_bias;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.seq_lens = seq_lens;
-    p.kv_scales = kv_scales;
-    p.out = out;
-    p.B = batch;
-    p.Lmax = max_seq_len;
-    p.step = step;
-    p.H = n_heads;
-    p.Hkv = n_kv_heads;
+    p.q = a.q;
+    p.k_new = a.k_new;
+    p.v_new = a.v_new;
+    p.bias = a.qkv_bias;
+    p.k_cache = a.k_cache;
+    p.v_cache = a.v_cache;
+    p.seq_lens = a.seq_lens;
+    p.kv_scales = a.kv_scales;
+    p.out = a.out;
+    p.B = a.batch;
+    p.Lmax = a.capacity;
+    p.step = a.step;
+    p.H = a.n_heads;
+    p.Hkv = a.n_kv_heads;
     p.G = G;
     p.n_hg = n_hg;
-    p.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    p.qscale = (float)(1.4426950408889634 / std::sqrt((double)a.head_dim));
+    p.block_table = a.block_table;
+    p.page_shift = a.page_shift;
+    p.max_pages = a.max_pages;
+    p.n_pages = a.n_pages;
 
-    const int units = batch * n_kv_heads * n_hg;
-    const bool balanced = ftm::use_gqa_mfma(kv_dtype, gtile, batch) &&
-                          (long long)batch * step * n_kv_heads * n_hg < (1LL << 31);
+    const int kv_dtype = a.kv_dtype, head_dim = a.head_dim;
+    const int units = a.batch * a.n_kv_heads * n_hg;
+    const bool balanced = ftm::use_gqa_mfma(kv_dtype, gtile, a.batch) &&
+                          (long long)a.batch * a.step * a.n_kv_heads * n_hg < (1LL << 31);
     Shape shape{4, 0};
     p.balanced = balanced;
     if (balanced) {
@@ -368,43 +439,136 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
         p.direct = 0;
         // pieces of at least 256 positions, and at most 200 per unit (the
         // merge keeps a unit's piece statistics in LDS)
-        p.seg_min = std::max(256, (step + 198) / 199);
-        p.seg_max = (step + p.seg_min - 1) / p.seg_min + 1;
+        p.seg_min = std::max(256, (a.step + 198) / 199);
+        p.seg_max = (a.step + p.seg_min - 1) / p.seg_min + 1;
         const size_t slots = (size_t)units * p.seg_max * gtile;
         void* ws = nullptr;
-        int st = get_workspace(device, stream, slots * (head_dim + 2) * sizeof(float), units, &ws,
-                               &p.counters);
+        int st = get_workspace(device, stream, slots * (head_dim + 2) * sizeof(float), units, capturing,
+                               &ws, &p.counters);
         if (st != FTM_OK) return st;
         p.ws_o = (float*)ws;
         p.ws_ml = p.ws_o + slots * head_dim;
     } else {
-        shape = choose_shape(kv_dtype, head_dim, gtile, units, step, cu_count(device));
+        shape = choose_shape(kv_dtype, head_dim, gtile, units, a.step, cu_count(device));
         p.chunk = shape.chunk;
-        p.S = (step + p.chunk - 1) / p.chunk;
+        p.S = (a.step + p.chunk - 1) / p.chunk;
         p.direct = p.S == 1;
         if (!p.direct) {
-            const size_t n_part = (size_t)batch * n_heads * p.S;
+            const size_t n_part = (size_t)a.batch * a.n_heads * p.S;
             void* ws = nullptr;
-            int st = get_workspace(device, stream, n_part * (head_dim + 2) * sizeof(float), 0, &ws, nullptr);
+            int st = get_workspace(device, stream, n_part * (head_dim + 2) * sizeof(float), 0, capturing,
+                                   &ws, nullptr);
             if (st != FTM_OK) return st;
             p.ws_o = (float*)ws;
             p.ws_ml = p.ws_o + n_part * head_dim;
         }
     }
 
-    auto ev = timing_slot(0);
+    auto ev = capturing ? std::pair<hipEvent_t, hipEvent_t>{nullptr, nullptr} : timing_slot(0);
     if (ev.first) (void)hipEventRecord(ev.first, stream);
     he = ftm::launch_attention(p, kv_dtype, head_dim, gtile, shape.nw, stream);
     if (ev.second) (void)hipEventRecord(ev.second, stream);
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(he));
     if (!balanced && !p.direct) {
-        auto ev2 = timing_slot(1);
+        auto ev2 = capturing ? std::pair<hipEvent_t, hipEvent_t>{nullptr, nullptr} : timing_slot(1);
         if (ev2.first) (void)hipEventRecord(ev2.first, stream);
         he = ftm::launch_combine(p, kv_dtype, head_dim, stream);
         if (ev2.second) (void)hipEventRecord(ev2.second, stream);
         if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("combine launch: ") + hipGetErrorString(he));
     }
     g_last_error.clear();
+    return FTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                   void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
+                   int max_seq_len, int step, int n_heads, int n_kv_heads, int head_dim,
+                   int kv_dtype, float* kv_scales, void* out, void* stream_ptr) {
+    if (max_seq_len < 1) return fail(FTM_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+    int st = check_common(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len,
+                          step, n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales, out, "max_seq_len");
+    if (st != FTM_OK) return st;
+    if ((size_t)max_seq_len * head_dim * elem_bytes(kv_dtype) > 0x7fffffffu)
+        return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
+    Call a{q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len, step, n_heads,
+           n_kv_heads, head_dim, kv_dtype, kv_scales, out, (hipStream_t)stream_ptr, nullptr, 0, 0, 0};
+    return decode_impl(a);
+}
+
+int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                         void* k_pages, void* v_pages, const int32_t* block_table, int n_pages,
+                         int page_size, int max_pages_per_seq, const int32_t* seq_lens, int batch,
+                         int step, int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
+                         float* kv_scales, void* out, void* stream_ptr) {
+    if (!block_table) return fail(FTM_ERR_INVALID_ARG, "block_table is NULL");
+    if (((uintptr_t)block_table & 3u) != 0) return fail(FTM_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    if (n_pages < 1 || max_pages_per_seq < 1)
+        return fail(FTM_ERR_INVALID_ARG, "n_pages and max_pages_per_seq must be >= 1");
+    if (page_size < 16 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0)
+        return fail(FTM_ERR_INVALID_ARG, "page_size " + std::to_string(page_size) +
+                                             " must be a power of two in [16, 65536]");
+    const long long cap = (long long)max_pages_per_seq * page_size;
+    if (cap > 0x7fffffffLL)
+        return fail(FTM_ERR_UNSUPPORTED, "max_pages_per_seq * page_size must stay below 2^31");
+    int st = check_common(q, k_new, v_new, qkv_bias, k_pages, v_pages, seq_lens, batch, (int)cap, step,
+                          n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales, out,
+                          "max_pages_per_seq * page_size");
+    if (st != FTM_OK) return st;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    Call a{q, k_new, v_new, qkv_bias, k_pages, v_pages, seq_lens, batch, (int)cap, step, n_heads,
+           n_kv_heads, head_dim, kv_dtype, kv_scales, out, (hipStream_t)stream_ptr, block_table, shift,
+           max_pages_per_seq, n_pages};
+    return decode_impl(a);
+}
+
+int ftm_graph_begin(void* stream) {
+    if (!stream) return fail(FTM_ERR_INVALID_ARG, "the null stream cannot be captured: pass a created stream");
+    hipError_t e = hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+    g_last_error.clear();
+    return FTM_OK;
+}
+
+int ftm_graph_end(void* stream, ftm_graph* graph) {
+    if (!stream || !graph) return fail(FTM_ERR_INVALID_ARG, "ftm_graph_end: stream and graph must be non-NULL");
+    *graph = nullptr;
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture((hipStream_t)stream, &g);
+    if (e != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return fail(FTM_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    }
+    hipGraphExec_t x = nullptr;
+    e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return fail(FTM_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    }
+    *graph = new ftm_graph_s{g, x};
+    g_last_error.clear();
+    return FTM_OK;
+}
+
+int ftm_graph_launch(ftm_graph graph, void* stream) {
+    if (!graph) return fail(FTM_ERR_INVALID_ARG, "ftm_graph_launch: graph is NULL");
+    hipError_t e = hipGraphLaunch(graph->exec, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipGraphLaunch: ") + hipGetErrorString(e));
+    g_last_error.clear();
+    return FTM_OK;
+}
+
+int ftm_graph_destroy(ftm_graph graph) {
+    if (!graph) return FTM_OK;
+    hipError_t e1 = hipGraphExecDestroy(graph->exec);
+    hipError_t e2 = hipGraphDestroy(graph->graph);
+    delete graph;
+    if (e1 != hipSuccess || e2 != hipSuccess)
+        return fail(FTM_ERR_HIP, std::string("graph destroy: ") + hipGetErrorString(e1 != hipSuccess ? e1 : e2));
     return FTM_OK;
 }
 

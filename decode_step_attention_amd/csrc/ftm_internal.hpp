@@ -17,10 +17,10 @@ struct Params {
     const void* k_new;      // [B, Hkv, D] act
     const void* v_new;      // [B, Hkv, D] act
     const void* bias;       // [(H + 2 Hkv) D] act or null
-    void* k_cache;          // [B, Hkv, Lmax, D] kv
-    void* v_cache;          // [B, Hkv, Lmax, D] kv
+    void* k_cache;          // [B, Hkv, Lmax, D] kv; paged: [n_pages, Hkv, P, D]
+    void* v_cache;          // same layout as k_cache
     const int32_t* seq_lens;// [B] or null
-    float* kv_scales;       // [2, B, Hkv, Lmax] (INT8) or null
+    float* kv_scales;       // [2, B, Hkv, Lmax] (INT8) or null; paged: [2, n_pages, Hkv, P]
     void* out;              // [B, H, D] act
     float* ws_o;            // [B, H, S, D]  un-normalised partial outputs
     float* ws_ml;           // [B, H, S, 2]  partial (max, sum), log2 domain
@@ -35,6 +35,11 @@ struct Params {
     int* counters;          // [units] finished-segment counts, zero between calls
     int seg_min;            // shortest slice a workgroup takes, in positions
     int seg_max;            // partial slots per unit
+    // paged cache (block_table null: contiguous [B, Hkv, Lmax, D] cache)
+    const int32_t* block_table;   // [B, max_pages]: page of positions [i P, (i+1) P)
+    int page_shift;         // log2(P), P >= 16
+    int max_pages;          // block-table row length
+    int n_pages;            // pages in the pool
 };
 
 // Group tile (query heads served by one pass over a KV head) for G heads.

@@ -24,9 +24,10 @@ _ACT = {FTM_F32: torch.float32, FTM_F16: torch.float16, FTM_BF16: torch.bfloat16
         FTM_I8: torch.float16}
 
 # Every symbol include/ftm.h declares.
-EXPORTS = ("ftm_decode_mha", "ftm_kv_cache_bytes", "ftm_last_error", "ftm_version",
-           "ftm_set_split_chunk", "ftm_set_workgroup_waves", "ftm_release_workspaces", "ftm_timing_enable",
-           "ftm_timing_disable", "ftm_timing_read")
+EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_kv_cache_bytes", "ftm_last_error",
+           "ftm_version", "ftm_set_split_chunk", "ftm_set_workgroup_waves", "ftm_release_workspaces",
+           "ftm_graph_begin", "ftm_graph_end", "ftm_graph_launch", "ftm_graph_destroy",
+           "ftm_timing_enable", "ftm_timing_disable", "ftm_timing_read")
 
 
 def _load() -> ctypes.CDLL:
@@ -38,6 +39,17 @@ def _load() -> ctypes.CDLL:
     lib.ftm_decode_mha.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                    i32, vp, vp, vp]
     lib.ftm_decode_mha.restype = i32
+    lib.ftm_decode_mha_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i32,
+                                         i32, i32, i32, i32, vp, vp, vp]
+    lib.ftm_decode_mha_paged.restype = i32
+    lib.ftm_graph_begin.argtypes = [vp]
+    lib.ftm_graph_begin.restype = i32
+    lib.ftm_graph_end.argtypes = [vp, ctypes.POINTER(vp)]
+    lib.ftm_graph_end.restype = i32
+    lib.ftm_graph_launch.argtypes = [vp, vp]
+    lib.ftm_graph_launch.restype = i32
+    lib.ftm_graph_destroy.argtypes = [vp]
+    lib.ftm_graph_destroy.restype = i32
     lib.ftm_kv_cache_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.ftm_kv_cache_bytes.restype = ctypes.c_size_t
     lib.ftm_last_error.argtypes = []
@@ -120,25 +132,7 @@ def ftm_decode_mha_raw(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, ba
                                   kv_scales, out, stream))
 
 
-def _marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step, out, kv_scales, stream):
-    if k_cache.dim() != 4 or q.dim() != 3:
-        raise ValueError("q must be [B, H, D] and k_cache [B, Hkv, Lmax, D]")
-    B, H, D = q.shape
-    _, Hkv, Lmax, _ = k_cache.shape
-    kv = _TORCH_TO_KV.get(k_cache.dtype)
-    if kv is None:
-        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
-    act = _ACT[kv]
-    dev = k_cache.device
-    tensors = {"q": (q, act, (B, H, D)), "k_new": (k_new, act, (B, Hkv, D)),
-               "v_new": (v_new, act, (B, Hkv, D)), "k_cache": (k_cache, k_cache.dtype, (B, Hkv, Lmax, D)),
-               "v_cache": (v_cache, k_cache.dtype, (B, Hkv, Lmax, D)), "out": (out, act, (B, H, D))}
-    if qkv_bias is not None:
-        tensors["qkv_bias"] = (qkv_bias, act, ((H + 2 * Hkv) * D,))
-    if seq_lens is not None:
-        tensors["seq_lens"] = (seq_lens, torch.int32, (B,))
-    if kv_scales is not None:
-        tensors["kv_scales"] = (kv_scales, torch.float32, (2, B, Hkv, Lmax))
+def _check_tensors(tensors, dev) -> None:
     for name, (t, dt, shape) in tensors.items():
         if t.dtype != dt:
             raise TypeError(f"{name}: dtype {t.dtype}, expected {dt}")
@@ -148,11 +142,62 @@ def _marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step, out, k
             raise ValueError(f"{name} must be contiguous")
         if t.device != dev:
             raise ValueError(f"{name} is on {t.device}, the cache on {dev}")
+
+
+def _step_tensors(q, k_new, v_new, qkv_bias, k_cache, seq_lens, out):
+    """Checks of the per-step tensors shared by both cache layouts."""
+    if k_cache.dim() != 4 or q.dim() != 3:
+        raise ValueError("q must be [B, H, D] and the cache 4-dimensional")
+    B, H, D = q.shape
+    Hkv = k_cache.shape[1]
+    kv = _TORCH_TO_KV.get(k_cache.dtype)
+    if kv is None:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    act = _ACT[kv]
+    tensors = {"q": (q, act, (B, H, D)), "k_new": (k_new, act, (B, Hkv, D)),
+               "v_new": (v_new, act, (B, Hkv, D)), "out": (out, act, (B, H, D))}
+    if qkv_bias is not None:
+        tensors["qkv_bias"] = (qkv_bias, act, ((H + 2 * Hkv) * D,))
+    if seq_lens is not None:
+        tensors["seq_lens"] = (seq_lens, torch.int32, (B,))
+    return B, H, Hkv, D, kv, tensors
+
+
+def _stream_ptr(stream, dev):
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    return ctypes.c_void_p(stream)
+
+
+def _marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step, out, kv_scales, stream):
+    B, H, Hkv, D, kv, tensors = _step_tensors(q, k_new, v_new, qkv_bias, k_cache, seq_lens, out)
+    Lmax = k_cache.shape[2]
+    tensors["k_cache"] = (k_cache, k_cache.dtype, (B, Hkv, Lmax, D))
+    tensors["v_cache"] = (v_cache, k_cache.dtype, (B, Hkv, Lmax, D))
+    if kv_scales is not None:
+        tensors["kv_scales"] = (kv_scales, torch.float32, (2, B, Hkv, Lmax))
+    _check_tensors(tensors, k_cache.device)
     return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_cache), _ptr(v_cache),
             _ptr(seq_lens), B, Lmax, int(step), H, Hkv, D, kv, _ptr(kv_scales), _ptr(out),
-            ctypes.c_void_p(stream))
+            _stream_ptr(stream, k_cache.device))
+
+
+def _marshal_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, step, out,
+                   kv_scales, stream):
+    B, H, Hkv, D, kv, tensors = _step_tensors(q, k_new, v_new, qkv_bias, k_pages, seq_lens, out)
+    n_pages, _, P, _ = k_pages.shape
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages_per_seq]")
+    max_pages = block_table.shape[1]
+    tensors["k_pages"] = (k_pages, k_pages.dtype, (n_pages, Hkv, P, D))
+    tensors["v_pages"] = (v_pages, k_pages.dtype, (n_pages, Hkv, P, D))
+    tensors["block_table"] = (block_table, torch.int32, (B, max_pages))
+    if kv_scales is not None:
+        tensors["kv_scales"] = (kv_scales, torch.float32, (2, n_pages, Hkv, P))
+    _check_tensors(tensors, k_pages.device)
+    return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_pages), _ptr(v_pages),
+            _ptr(block_table), n_pages, P, max_pages, _ptr(seq_lens), B, int(step), H, Hkv, D, kv,
+            _ptr(kv_scales), _ptr(out), _stream_ptr(stream, k_pages.device))
 
 
 def ftm_decode_mha(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -168,6 +213,15 @@ def ftm_decode_mha(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                                         step, out, kv_scales, stream)))
 
 
+def _prepared(f, args, keep) -> Callable[[], None]:
+    def call() -> None:
+        rc = f(*args)
+        if rc != 0:
+            raise RuntimeError(f"libftm status {rc}: {ftm_last_error()}")
+    call.tensors = keep
+    return call
+
+
 def ftm_decode_mha_prepared(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step, out,
                             kv_scales=None, stream=None) -> Callable[[], None]:
     """Checks and marshals the arguments once and returns a callable that
@@ -176,11 +230,48 @@ def ftm_decode_mha_prepared(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_len
     args = _marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step, out, kv_scales,
                     stream)
     keep = (q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, kv_scales)
-    f = lib.ftm_decode_mha
+    return _prepared(lib.ftm_decode_mha, args, keep)
 
-    def call() -> None:
-        rc = f(*args)
-        if rc != 0:
-            raise RuntimeError(f"libftm status {rc}: {ftm_last_error()}")
-    call.tensors = keep
-    return call
+
+def ftm_decode_mha_paged(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                         qkv_bias: Optional[torch.Tensor], k_pages: torch.Tensor,
+                         v_pages: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: Optional[torch.Tensor], step: int, out: torch.Tensor,
+                         kv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One decode step over a paged cache (see include/ftm.h).  Shapes:
+    k_pages/v_pages [n_pages, Hkv, P, D], block_table int32 [B, max_pages],
+    kv_scales fp32 [2, n_pages, Hkv, P] for an int8 cache; the rest as for
+    ftm_decode_mha."""
+    _check(lib.ftm_decode_mha_paged(*_marshal_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages,
+                                                    block_table, seq_lens, step, out, kv_scales,
+                                                    stream)))
+
+
+def ftm_decode_mha_paged_prepared(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table,
+                                  seq_lens, step, out, kv_scales=None,
+                                  stream=None) -> Callable[[], None]:
+    """ftm_decode_mha_paged with the arguments marshalled once."""
+    args = _marshal_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, step,
+                          out, kv_scales, stream)
+    keep = (q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, kv_scales)
+    return _prepared(lib.ftm_decode_mha_paged, args, keep)
+
+
+def ftm_graph_begin(stream: int) -> None:
+    """Starts capturing `stream` (a created stream's handle, not 0)."""
+    _check(lib.ftm_graph_begin(ctypes.c_void_p(stream)))
+
+
+def ftm_graph_end(stream: int) -> int:
+    """Ends the capture and returns the instantiated graph's handle."""
+    g = ctypes.c_void_p(None)
+    _check(lib.ftm_graph_end(ctypes.c_void_p(stream), ctypes.byref(g)))
+    return g.value
+
+
+def ftm_graph_launch(graph: int, stream: int) -> None:
+    _check(lib.ftm_graph_launch(ctypes.c_void_p(graph), ctypes.c_void_p(stream)))
+
+
+def ftm_graph_destroy(graph: Optional[int]) -> None:
+    _check(lib.ftm_graph_destroy(ctypes.c_void_p(graph)))

@@ -31,7 +31,7 @@ TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
 
 _TAGS = {"q": 1, "k_new": 2, "v_new": 3, "bias": 4, "k_cache": 5, "v_cache": 6,
-         "k_scale": 7, "v_scale": 8, "lens": 9}
+         "k_scale": 7, "v_scale": 8, "lens": 9, "pages": 10}
 
 
 def act_dtype(kv_dtype: str) -> str:
@@ -49,7 +49,9 @@ class Case:
     ``value_scale``: standard deviation of every drawn real value.
     ``int8_code_gain``: prefilled INT8 rows hold codes round(gain * N(0,1))
     clamped to +-127, with a per-row scale of (1 +- 5%) / gain, so that the
-    dequantised values are again about N(0,1) * value_scale-free."""
+    dequantised values are again about N(0,1) * value_scale-free.
+    ``page_size``: 0 for the contiguous [B, Hkv, Lmax, D] cache, else the
+    tokens per page of a paged cache (``make_paged_inputs``)."""
     name: str
     batch: int
     n_heads: int
@@ -64,6 +66,7 @@ class Case:
     rotate: int = 1
     seed: int = 1000
     int8_code_gain: float = 127.0 / 3.0
+    page_size: int = 0
 
     @property
     def act_dtype(self) -> str:
@@ -91,6 +94,11 @@ CASES: Dict[str, Case] = {
     "int8": Case("int8", 64, 40, 40, 128, "i8", ctx=4096, max_seq_len=4096,
                  value_scale=1.0, rotate=2, seed=1004),
 }
+# The same layer shapes over a paged cache of 256-token pages (the page size
+# [intelliparadigm.com .../2131745] section 5.1 gives as its example), pages
+# handed out in a seeded random order.
+CASES["7b_paged"] = CASES["7b"].with_(name="7b_paged", page_size=256)
+CASES["gqa_paged"] = CASES["gqa"].with_(name="gqa_paged", page_size=256)
 
 
 def _gen(case: Case, tag: str, layer: int, device) -> torch.Generator:
@@ -178,6 +186,63 @@ def make_inputs(case: Case, device="cpu", layer: int = 0, poison: bool = True,
     t["seq_lens"] = L.to(device)
     t["step"] = int(L.max())
     return t
+
+
+def to_paged(t: Dict[str, torch.Tensor], case: Case, page_size: int, layer: int = 0,
+             poison: bool = True) -> Dict[str, torch.Tensor]:
+    """Moves the contiguous cache of ``make_inputs`` into a page pool.
+
+    Sequence b takes ceil(L_b / P) pages, enough for positions [0, L_b); the
+    pool holds those plus max(1, B / 4) spare pages, all handed out in a
+    seeded random order.  Adds ``k_pages``/``v_pages`` [n_pages, Hkv, P, D],
+    ``block_table`` int32 [B, ceil(Lmax / P)] (-1 past a sequence's pages)
+    and, for INT8, ``kv_scales`` [2, n_pages, Hkv, P]; removes the
+    contiguous cache.  Rows the pool holds that no position maps to are NaN
+    (NaN scales for INT8) with ``poison``, else zero."""
+    P = page_size
+    k, v = t.pop("k_cache"), t.pop("v_cache")
+    B, Hkv, Lmax, D = k.shape
+    dev = k.device
+    L = t["seq_lens"].cpu().tolist()
+    max_pages = (Lmax + P - 1) // P
+    need = [min(max(0, (int(x) + P - 1) // P), max_pages) for x in L]
+    n_pages = sum(need) + max(1, B // 4)
+    perm = torch.randperm(n_pages, generator=_gen(case, "pages", layer, "cpu")).tolist()
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    fill = float("nan") if poison else 0.0
+    i8 = case.kv_dtype == "i8"
+    kp = torch.empty((n_pages, Hkv, P, D), dtype=k.dtype, device=dev)
+    vp = torch.empty_like(kp)
+    if i8:
+        kp.zero_()
+        vp.zero_()
+        sc = t.pop("kv_scales")
+        sp = torch.full((2, n_pages, Hkv, P), fill, dtype=torch.float32, device=dev)
+    else:
+        kp.fill_(fill)
+        vp.fill_(fill)
+    n = 0
+    for b in range(B):
+        for i in range(need[b]):
+            pg = perm[n]
+            n += 1
+            table[b, i] = pg
+            lo, hi = i * P, min((i + 1) * P, Lmax)
+            kp[pg, :, :hi - lo] = k[b, :, lo:hi]
+            vp[pg, :, :hi - lo] = v[b, :, lo:hi]
+            if i8:
+                sp[:, pg, :, :hi - lo] = sc[:, b, :, lo:hi]
+    t["k_pages"], t["v_pages"] = kp, vp
+    t["block_table"] = table.to(dev)
+    if i8:
+        t["kv_scales"] = sp
+    return t
+
+
+def make_paged_inputs(case: Case, device="cpu", layer: int = 0, poison: bool = True,
+                      lens: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """``make_inputs`` with the cache in a page pool of ``case.page_size``."""
+    return to_paged(make_inputs(case, device, layer, poison, lens), case, case.page_size, layer, poison)
 
 
 def kv_bytes(case: Case, lens: Optional[List[int]] = None) -> int:

@@ -113,6 +113,81 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new,
                    int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
                    float* kv_scales, void* out, void* stream);
 
+/*
+ * ftm_decode_mha_paged -- the same decode step over a paged KV cache.
+ *
+ * The cache is cut into fixed-size pages that sequences take as needed,
+ * as in virtual memory ([intelliparadigm.com .../2131745] section 5.1: a
+ * cache split into pages of a fixed number of tokens; [framerc.cn/news/
+ * 4453289] section 3.2: fixed-size blocks allocated on demand instead of
+ * one maximum-length buffer per sequence).  Position i of sequence b lives
+ * in page block_table[b][i / page_size], at row i % page_size.
+ *
+ * Shapes (row-major, contiguous; P = page_size):
+ *   k_pages, v_pages [n_pages, n_kv_heads, P, D]  kv_dtype, read, and the
+ *             row of position seq_lens[b]-1 of every (b, KV head) written
+ *   block_table [batch, max_pages_per_seq] int32 device array: page indices
+ *             in [0, n_pages); only the entries of pages holding positions
+ *             below seq_lens[b] are read
+ *   kv_scales [2, n_pages, n_kv_heads, P] fp32, INT8 caches only (K scales
+ *             first), read and written like the rows they scale
+ *   every other argument as for ftm_decode_mha, with max_pages_per_seq * P
+ *             in the role of max_seq_len (step <= max_pages_per_seq * P).
+ * Arithmetic, the append rule and the results are those of ftm_decode_mha
+ * on the cache the table describes.  page_size must be a power of two in
+ * [16, 65536]; k_pages and v_pages 16-byte aligned, block_table 4 bytes.
+ *
+ * The caller owns the pool and the table.  Pages that two sequences share,
+ * or that one sequence lists twice, are the caller's to keep consistent:
+ * the call writes one row per (sequence, KV head) and reads the others
+ * concurrently.  A sequence whose table names a page outside [0, n_pages)
+ * at a position it reads gets NaN output rows; when that page is the one
+ * of the new row, the row is not appended (no host synchronisation is
+ * needed to see the error).  Other errors as for ftm_decode_mha, plus
+ * FTM_ERR_INVALID_ARG for a NULL or misaligned block_table, n_pages or
+ * max_pages_per_seq below 1, or another page_size.
+ * ftm_kv_cache_bytes(n_pages, n_kv_heads, page_size, head_dim, kv_dtype)
+ * gives the pool's bytes.
+ */
+int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new,
+                         const void* qkv_bias, void* k_pages, void* v_pages,
+                         const int32_t* block_table, int n_pages, int page_size,
+                         int max_pages_per_seq, const int32_t* seq_lens, int batch, int step,
+                         int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
+                         float* kv_scales, void* out, void* stream);
+
+/* ---- HIP graphs ----------------------------------------------------------
+ * A decode step of a model is one call per layer on fixed buffers; its
+ * kernel launches can be recorded once and replayed as one graph launch, so
+ * that launch overhead stops dominating small shapes ([lmnt.cn/news/219530]
+ * section 5.3 and [lpnh.cn/news/2765398] section 1.2: the count of kernel
+ * launches per decode step is a cost of its own; [pptc.cn/news/144085]
+ * section 2.3).
+ *
+ * ftm_graph_begin starts capturing `stream` (a created stream, not the null
+ * stream; capture mode thread-local).  The ftm_decode_mha and
+ * ftm_decode_mha_paged calls that follow on that stream and host thread are
+ * recorded, not run.  They allocate nothing: each needs a workspace that an
+ * earlier call of the same or a larger shape on the same stream has already
+ * grown, or it fails with FTM_ERR_INVALID_ARG and records nothing (the
+ * capture stays valid).  FTM_VALIDATE and kernel timing do not apply while
+ * capturing.  ftm_graph_end stops the capture and instantiates the graph
+ * into *graph (NULL on failure).  ftm_graph_launch replays it on any stream:
+ * the same kernels on the same pointers, reading the buffers' contents at
+ * replay time.  Replays of one graph, and calls on the stream it was
+ * captured on, share that stream's workspace: do not run them concurrently.
+ * A workspace a graph was captured with stays allocated when a later call
+ * needs a larger one, so graphs stay valid until ftm_release_workspaces,
+ * after which they must not be replayed.
+ * ftm_graph_destroy frees the graph (NULL is accepted).  All return FTM_OK
+ * or FTM_ERR_INVALID_ARG / FTM_ERR_HIP with ftm_last_error() set.
+ */
+typedef struct ftm_graph_s* ftm_graph;
+int ftm_graph_begin(void* stream);
+int ftm_graph_end(void* stream, ftm_graph* graph);
+int ftm_graph_launch(ftm_graph graph, void* stream);
+int ftm_graph_destroy(ftm_graph graph);
+
 /* Bytes of one layer's K and V cache (plus INT8 scales) for the layout
  * above: 2 * batch * n_kv_heads * max_seq_len * (head_dim * elem + scale),
  * scale = 4 bytes for INT8, 0 otherwise.  Sizing as in
@@ -145,7 +220,8 @@ int ftm_set_split_chunk(int positions);
 int ftm_set_workgroup_waves(int waves);
 
 /* Frees every workspace the library holds (all devices and streams).  The
- * caller must make sure no call of this library is still running. */
+ * caller must make sure no call of this library is still running, and must
+ * not replay graphs captured before the release. */
 void ftm_release_workspaces(void);
 
 /* ---- kernel timing -------------------------------------------------------

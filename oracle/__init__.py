@@ -116,6 +116,70 @@ def decode_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, step,
     return out, probs
 
 
+def decode_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, step,
+                     n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales=None,
+                     n_threads=1) -> np.ndarray:
+    """One decode step over a paged cache; appends into k_pages/v_pages/kv_scales
+    in place and returns out[B,H,D] float64.
+
+    Paging is address translation only ([intelliparadigm.com
+    .../2131745] section 5.1: the cache cut into fixed-size pages;
+    [framerc.cn/news/4453289] section 3.2: blocks taken on demand, located
+    through a table as in virtual memory): position i of sequence b is row
+    i mod P of page block_table[b, i // P].  The step is therefore the
+    contiguous step above on the cache that the table describes: this
+    function gathers that cache, runs ``decode_mha`` on it and writes the
+    one appended row per (b, KV head) back to its page.
+
+    Contract for a table entry outside [0, n_pages) among the pages of
+    positions [0, L_b): the sequence's output rows are NaN, and its new row
+    is appended only if the new row's own page is valid.
+
+    Layouts: k_pages/v_pages [n_pages, Hkv, P, D], block_table int32
+    [B, max_pages], kv_scales float32 [2, n_pages, Hkv, P] (INT8 only)."""
+    n_pages, Hkv, P, D = k_pages.shape
+    B, max_pages = block_table.shape
+    if Hkv != n_kv_heads or D != head_dim or v_pages.shape != k_pages.shape:
+        raise ValueError("page pool shape does not match n_kv_heads / head_dim")
+    cap = max_pages * P
+    lens = (np.full(B, step, dtype=np.int64) if seq_lens is None
+            else np.asarray(seq_lens, dtype=np.int64))
+    tbl = np.asarray(block_table, dtype=np.int64)
+    ok_entry = (tbl >= 0) & (tbl < n_pages)
+    page_of = np.where(ok_entry, tbl, 0)
+
+    def gather(pool):
+        # [B, max_pages, Hkv, P, ...] -> [B, Hkv, max_pages * P, ...]
+        g = pool[page_of]
+        g = np.swapaxes(g, 1, 2)
+        return np.ascontiguousarray(g.reshape((B, Hkv, cap) + pool.shape[3:]))
+
+    kc, vc = gather(k_pages), gather(v_pages)
+    sc = None
+    if kv_scales is not None:
+        sc = np.ascontiguousarray(np.stack([gather(kv_scales[0]), gather(kv_scales[1])]))
+    out, _ = decode_mha(q, k_new, v_new, qkv_bias, kc, vc,
+                        None if seq_lens is None else np.ascontiguousarray(seq_lens, dtype=np.int32),
+                        step, n_heads, n_kv_heads, head_dim, kv_dtype, sc, n_threads=n_threads)
+    for b in range(B):
+        L = int(lens[b])
+        if L < 1 or L > step:
+            continue                        # the contiguous step already wrote NaN, no append
+        pages_used = (L - 1) // P + 1
+        if not ok_entry[b, :pages_used].all():
+            out[b] = np.nan
+        last = (L - 1) // P
+        if not ok_entry[b, last]:
+            continue
+        pg, row = int(tbl[b, last]), (L - 1) % P
+        k_pages[pg, :, row] = kc[b, :, L - 1]
+        v_pages[pg, :, row] = vc[b, :, L - 1]
+        if kv_scales is not None:
+            kv_scales[0, pg, :, row] = sc[0, b, :, L - 1]
+            kv_scales[1, pg, :, row] = sc[1, b, :, L - 1]
+    return out
+
+
 def f16_bits_to_double(bits: int) -> float:
     return _load().orc_f16_bits_to_double(bits)
 

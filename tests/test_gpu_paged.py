@@ -1,0 +1,219 @@
+"""GPU parity of the paged-cache entry point (ftm_decode_mha_paged) through
+the C ABI.
+
+Every case is checked three ways on the same seeded inputs:
+  * against the paged oracle: the pools (and INT8 scale pools) must equal
+    the oracle's bytewise, and out must meet the same bar as the contiguous
+    path (max-abs 1e-5 fp32, 2e-3 otherwise, row-rel 1e-5 / 1e-2);
+  * against the contiguous GPU entry point on the cache the block table
+    describes: out must be bitwise identical, since only the addressing
+    differs and the work split depends on the lengths alone;
+  * with a table naming pages outside the pool: NaN rows, and the append
+    made exactly when the new row's page is valid, as the oracle does.
+Pages are handed out in a seeded random order, with spare pages that no
+position maps to; rows the step must not read hold NaN."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_step_attention_amd import workloads as W
+from tests.helpers import out_to_f64, to_np
+from tests.test_gpu_parity import bits, check, gpu_call, small, sub_problem
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ftm():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from decode_step_attention_amd import ftm as m
+    yield m
+    m.ftm_set_split_chunk(0)
+    m.ftm_set_workgroup_waves(0)
+
+
+def paged_np(pg, kvd):
+    act = W.act_dtype(kvd)
+    r = {k: to_np(pg[k], act) for k in ("q", "k_new", "v_new", "bias")}
+    r["k_pages"] = to_np(pg["k_pages"], kvd)
+    r["v_pages"] = to_np(pg["v_pages"], kvd)
+    r["block_table"] = pg["block_table"].cpu().numpy().astype(np.int32)
+    r["seq_lens"] = pg["seq_lens"].cpu().numpy().astype(np.int32)
+    r["kv_scales"] = to_np(pg["kv_scales"], "f32") if "kv_scales" in pg else None
+    return r
+
+
+def gpu_paged(ftm, g, case):
+    out = torch.empty((case.batch, case.n_heads, case.head_dim),
+                      dtype=W.TORCH_DTYPES[case.act_dtype], device=g["q"].device)
+    ftm.ftm_decode_mha_paged(g["q"], g["k_new"], g["v_new"], g["bias"], g["k_pages"], g["v_pages"],
+                             g["block_table"], g["seq_lens"], g["step"], out, g.get("kv_scales"))
+    return out
+
+
+def run_paged(ftm, case, P, chunk=0, waves=0, lens=None, mutate=None, contiguous=True, tag=""):
+    inp = W.make_inputs(case, "cpu", poison=True, lens=lens)
+    contig = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    pg = W.to_paged(inp, case, P, poison=True)
+    if mutate:
+        mutate(pg)
+    npp = paged_np(pg, case.kv_dtype)
+    ref = oracle.decode_mha_paged(npp["q"], npp["k_new"], npp["v_new"], npp["bias"],
+                                  npp["k_pages"], npp["v_pages"], npp["block_table"],
+                                  npp["seq_lens"], pg["step"], case.n_heads, case.n_kv_heads,
+                                  case.head_dim, case.kv_dtype, npp["kv_scales"], n_threads=8)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in pg.items()}
+    gc = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in contig.items()}
+    ftm.ftm_set_split_chunk(chunk)
+    ftm.ftm_set_workgroup_waves(waves)
+    try:
+        print(f"[{tag}] paged call", flush=True)
+        out = gpu_paged(ftm, g, case)
+        torch.cuda.synchronize()
+        out_c = gpu_call(ftm, gc, case) if contiguous else None
+        torch.cuda.synchronize()
+    finally:
+        ftm.ftm_set_split_chunk(0)
+        ftm.ftm_set_workgroup_waves(0)
+    kvd = case.kv_dtype
+    assert to_np(g["k_pages"], kvd).tobytes() == npp["k_pages"].tobytes(), f"{tag}: k_pages"
+    assert to_np(g["v_pages"], kvd).tobytes() == npp["v_pages"].tobytes(), f"{tag}: v_pages"
+    if kvd == "i8":
+        assert to_np(g["kv_scales"], "f32").tobytes() == npp["kv_scales"].tobytes(), f"{tag}: scales"
+    check(case, out, ref, tag)
+    if contiguous:
+        assert torch.equal(bits(out), bits(out_c)), f"{tag}: paged and contiguous outputs differ"
+    return out, ref
+
+
+# ---- every kernel path, several page sizes -------------------------------
+PATHS = [
+    # kv, D, H, Hkv, P, chunk, waves
+    ("f16", 128, 8, 8, 16, 0, 0),       # one head per pass, 16-wave workgroups
+    ("f16", 128, 8, 8, 256, 0, 0),
+    ("f16", 128, 8, 8, 64, 256, 4),     # split into chunks + combine, 4-wave
+    ("bf16", 64, 8, 8, 32, 0, 16),
+    ("f32", 64, 8, 8, 16, 0, 0),
+    ("f32", 128, 8, 8, 128, 384, 4),
+    ("f16", 128, 8, 4, 32, 0, 0),       # two heads per pass
+    ("i8", 128, 8, 8, 16, 0, 0),        # INT8, scales from the pages
+    ("i8", 64, 8, 8, 128, 256, 0),
+    ("i8", 128, 8, 2, 64, 0, 0),        # INT8, four heads per pass
+    ("i8", 128, 8, 1, 16, 0, 0),        # INT8, eight heads per pass
+    ("bf16", 128, 8, 1, 16, 0, 0),      # grouped heads on the matrix cores
+    ("bf16", 128, 8, 2, 256, 0, 0),
+    ("f16", 64, 8, 1, 64, 0, 0),
+    ("f16", 128, 16, 2, 16, 0, 0),
+]
+
+
+@pytest.mark.parametrize("kv,D,H,Hkv,P,chunk,waves", PATHS)
+def test_paged_parity(ftm, kv, D, H, Hkv, P, chunk, waves):
+    case = small(kv, D=D, H=H, Hkv=Hkv, seed=41 + D + H + Hkv + P)
+    run_paged(ftm, case, P, chunk=chunk, waves=waves,
+              tag=f"paged {kv} D{D} H{H}/{Hkv} P{P} c{chunk} w{waves}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+def test_paged_grouped_heads_vector_path(ftm, monkeypatch, kv):
+    monkeypatch.setenv("FTM_GQA_VALU", "1")
+    case = small(kv, D=128, H=8, Hkv=1, seed=51)
+    run_paged(ftm, case, 32, tag=f"paged {kv} G8 vector path")
+
+
+@pytest.mark.parametrize("B,lens,P", [(1, (8000, 8000), 16), (5, (100, 3000), 16),
+                                      (37, (1, 700), 64), (2, (2, 40), 16)])
+def test_paged_grouped_heads_balanced_schedule(ftm, B, lens, P):
+    """Long single sequences cut into many pieces, many short units, and
+    lengths below one piece, through the page table."""
+    Lmax = max(lens[1], 64)
+    case = W.Case("gb", B, 8, 1, 128, "bf16", ctx=Lmax, max_seq_len=Lmax,
+                  value_scale=1 / np.sqrt(128), lens=lens, seed=61 + B)
+    run_paged(ftm, case, P, tag=f"paged balanced B{B} L{lens} P{P}")
+
+
+def test_identity_table_is_the_contiguous_cache(ftm):
+    """One page per sequence of P = Lmax rows, table[b] = b: the pool is the
+    contiguous cache itself, byte for byte, before and after the step."""
+    case = small("f16", D=128, H=8, Hkv=8, seed=71).with_(max_seq_len=1024, ctx=1024, lens=(1, 1000))
+    inp = {k: (v.cuda() if torch.is_tensor(v) else v)
+           for k, v in W.make_inputs(case, "cpu", poison=True).items()}
+    kp, vp = inp["k_cache"].clone(), inp["v_cache"].clone()
+    table = torch.arange(case.batch, dtype=torch.int32, device="cuda").reshape(-1, 1)
+    out_c = gpu_call(ftm, inp, case)
+    out_p = torch.empty_like(out_c)
+    ftm.ftm_decode_mha_paged(inp["q"], inp["k_new"], inp["v_new"], inp["bias"], kp, vp, table,
+                             inp["seq_lens"], inp["step"], out_p)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out_p), bits(out_c))
+    assert torch.equal(bits(kp), bits(inp["k_cache"])) and torch.equal(bits(vp), bits(inp["v_cache"]))
+
+
+def _bad_pages(pg):
+    """Sequence 0: a history page outside the pool; sequence 1: its new
+    row's page outside the pool (negative); the rest untouched."""
+    t = pg["block_table"]
+    n = pg["k_pages"].shape[0]
+    L = pg["seq_lens"].tolist()
+    t[0, 0] = n + 3
+    t[1, (L[1] - 1) // (pg["k_pages"].shape[2])] = -1
+
+
+@pytest.mark.parametrize("kv,H,Hkv,P,chunk", [("f16", 8, 8, 16, 0), ("f16", 8, 8, 64, 256),
+                                             ("bf16", 8, 1, 16, 0), ("i8", 8, 8, 32, 0)])
+def test_pages_outside_the_pool(ftm, kv, H, Hkv, P, chunk):
+    case = small(kv, D=128, H=H, Hkv=Hkv, B=4, seed=81).with_(lens=(200, 1033))
+    out, ref = run_paged(ftm, case, P, chunk=chunk, mutate=_bad_pages, contiguous=False,
+                         tag=f"bad pages {kv} H{H}/{Hkv} P{P} c{chunk}")
+    assert np.isnan(ref[0]).all() and np.isnan(ref[1]).all() and np.isfinite(ref[2:]).all()
+
+
+@pytest.mark.parametrize("kv,Hkv", [("f16", 8), ("bf16", 1)])
+def test_paged_invalid_lengths(ftm, kv, Hkv):
+    case = small(kv, D=128, H=8, Hkv=Hkv, B=4, seed=91).with_(lens=None, ctx=700)
+    lens = torch.tensor([700, 0, 700, 650], dtype=torch.int32)
+    run_paged(ftm, case, 16, lens=lens, tag=f"paged invalid lengths {kv}")
+
+
+@pytest.mark.parametrize("name", ["7b_paged", "gqa_paged"])
+def test_full_size_paged_workload(ftm, name):
+    """The paged workloads at full size, in the launch configuration the
+    benchmark times: out bitwise equal to the contiguous entry point on the
+    same logical cache, appended rows equal, sampled units recomputed by the
+    oracle."""
+    case = W.CASES[name]
+    print(f"[full {name}] generating", flush=True)
+    inp = W.make_inputs(case, "cuda", poison=False)
+    contig = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    pg = W.to_paged(inp, case, case.page_size, poison=False)
+    kvd, act = case.kv_dtype, case.act_dtype
+    B, Hkv, P = case.batch, case.n_kv_heads, case.page_size
+    host = {k: to_np(contig[k], act) for k in ("q", "k_new", "v_new", "bias")}
+    host["seq_lens"] = contig["seq_lens"].cpu().numpy().astype(np.int32)
+    rng = np.random.default_rng(case.seed)
+    units = sorted({(int(b), int(j)) for b, j in zip(rng.integers(0, B, 4), rng.integers(0, Hkv, 4))}
+                   | {(B - 1, Hkv - 1)})
+    host["k_slab"] = {u: to_np(contig["k_cache"][u[0]:u[0] + 1, u[1]:u[1] + 1], kvd) for u in units}
+    host["v_slab"] = {u: to_np(contig["v_cache"][u[0]:u[0] + 1, u[1]:u[1] + 1], kvd) for u in units}
+    print(f"[full {name}] running", flush=True)
+    out_p = gpu_paged(ftm, pg, case)
+    out_c = gpu_call(ftm, contig, case)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out_p), bits(out_c)), "paged and contiguous outputs differ"
+    table = pg["block_table"].cpu()
+    for b in range(B):
+        L = int(host["seq_lens"][b])
+        pgi, row = int(table[b, (L - 1) // P]), (L - 1) % P
+        assert torch.equal(bits(pg["k_pages"][pgi, :, row]), bits(contig["k_cache"][b, :, L - 1]))
+        assert torch.equal(bits(pg["v_pages"][pgi, :, row]), bits(contig["v_cache"][b, :, L - 1]))
+    out_h = out_to_f64(out_p)
+    G = case.group
+    for (b, j) in units:
+        sub, sc = sub_problem(case, host, b, j)
+        ref, _ = oracle.decode_mha(sub["q"], sub["k_new"], sub["v_new"], sub["bias"],
+                                   sub["k_cache"], sub["v_cache"], sub["seq_lens"], sub["step"],
+                                   sc.n_heads, 1, sc.head_dim, kvd, sub["kv_scales"])
+        check(case, out_h[b:b + 1, j * G:(j + 1) * G], ref,
+              f"full {name} b{b} j{j} L{int(host['seq_lens'][b])}")

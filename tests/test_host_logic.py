@@ -110,3 +110,58 @@ def test_binding_rejects_mismatched_tensors():
         ftm.ftm_decode_mha(q, kn[:, :1], kn, None, kc, kc, None, 8, q)
     with pytest.raises(ValueError):
         ftm.ftm_decode_mha(q, kn, kn, None, kc, kc.transpose(2, 3), None, 8, q)
+
+
+def call_paged(**kw):
+    args = [("q", A), ("k_new", A), ("v_new", A), ("qkv_bias", A), ("k_pages", A), ("v_pages", A),
+            ("block_table", A), ("n_pages", 10), ("page_size", 16), ("max_pages_per_seq", 4),
+            ("seq_lens", A), ("batch", 2), ("step", 40), ("n_heads", 4), ("n_kv_heads", 2),
+            ("head_dim", 128), ("kv_dtype", ftm.FTM_F16), ("kv_scales", None), ("out", A),
+            ("stream", None)]
+    vals = [kw.get(k, v) for k, v in args]
+    rc = ftm.lib.ftm_decode_mha_paged(*vals)
+    return rc, ftm.ftm_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(block_table=None), 1, "block_table"),
+    (dict(block_table=A + 2), 1, "aligned"),
+    (dict(n_pages=0), 1, "n_pages"),
+    (dict(max_pages_per_seq=0), 1, "max_pages_per_seq"),
+    (dict(page_size=8), 1, "page_size"),
+    (dict(page_size=48), 1, "power of two"),
+    (dict(page_size=1 << 17), 1, "page_size"),
+    (dict(step=65), 1, "max_pages_per_seq * page_size"),
+    (dict(max_pages_per_seq=1 << 20, page_size=1 << 12), 2, "2^31"),
+    (dict(k_pages=A + 8), 1, "aligned"),
+    (dict(q=None), 1, "NULL"),
+    (dict(kv_dtype=ftm.FTM_I8), 1, "kv_scales"),
+    (dict(head_dim=96), 2, "head_dim"),
+])
+def test_paged_argument_errors_return_before_any_device_call(kw, status, needle):
+    rc, msg = call_paged(**kw)
+    assert rc == status
+    assert needle in msg
+
+
+def test_graph_argument_errors():
+    assert ftm.lib.ftm_graph_begin(None) == 1
+    assert "null stream" in ftm.ftm_last_error()
+    assert ftm.lib.ftm_graph_end(None, None) == 1
+    assert ftm.lib.ftm_graph_launch(None, None) == 1
+    assert "graph is NULL" in ftm.ftm_last_error()
+    assert ftm.lib.ftm_graph_destroy(None) == 0
+
+
+def test_binding_rejects_mismatched_paged_tensors():
+    import torch
+    q = torch.zeros(2, 4, 128, dtype=torch.float16)
+    kn = torch.zeros(2, 2, 128, dtype=torch.float16)
+    kp = torch.zeros(6, 2, 16, 128, dtype=torch.float16)
+    tbl = torch.zeros(2, 3, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        ftm.ftm_decode_mha_paged(q, kn, kn, None, kp, kp, tbl.long(), None, 8, q)
+    with pytest.raises(ValueError):
+        ftm.ftm_decode_mha_paged(q, kn, kn, None, kp, kp[:, :1], tbl, None, 8, q)
+    with pytest.raises(ValueError):
+        ftm.ftm_decode_mha_paged(q, kn, kn, None, kp, kp, tbl[:1], None, 8, q)
