@@ -25,6 +25,7 @@
 #include "ftm_internal.hpp"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace ftm {
 namespace {
@@ -182,6 +183,11 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
     return v;
 }
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
+    return v;
+}
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -218,7 +224,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* pool, in
                                                             int j, int pos, int end, bool& bad) {
     const int sh = p.page_shift;
     const int idx = min(pos >> sh, max(end - 1, 0) >> sh);
-    const int page = tbl[idx];
+    // the table is never written by a kernel: read it as constant memory,
+    // through the scalar cache, so that the read does not queue behind the
+    // K/V loads in flight
+    const int page = ((const __attribute__((address_space(4))) int32_t*)tbl)[idx];
     const int in_page = pos & ((1 << sh) - 1);
     const bool valid = (unsigned)page < (unsigned)p.n_pages;
     int rows = min(end - pos, (1 << sh) - in_page);
@@ -252,6 +261,9 @@ __device__ __forceinline__ bool new_row_index(const Params& p, int b, int j, int
 // receives what the cache now holds, as fp32 (INT8: the code), `scale` the
 // INT8 scale (1 otherwise), `packed` the 16 bytes this lane writes.
 // ---------------------------------------------------------------------------
+template <int KV, int EPL, int LPR>
+__device__ __forceinline__ void store_new_row(float* x, float* stored, float& scale, u32x4& packed);
+
 template <int KV, int D, int EPL, int LPR>
 __device__ __forceinline__ void make_new_row(const Params& p, const void* src, int bias_row,
                                              size_t src_row, int c, float* stored, float& scale,
@@ -264,6 +276,14 @@ __device__ __forceinline__ void make_new_row(const Params& p, const void* src, i
 #pragma unroll
         for (int e = 0; e < EPL; ++e) x[e] = x[e] + bx[e];   // one fp32 rounding
     }
+    store_new_row<KV, EPL, LPR>(x, stored, scale, packed);
+}
+
+// x (the biased row slice, fp32) as the cache type: `stored` what the cache
+// will hold, as fp32 (INT8: the code), `scale` the INT8 scale (1 otherwise),
+// `packed` the 16 bytes to write.
+template <int KV, int EPL, int LPR>
+__device__ __forceinline__ void store_new_row(float* x, float* stored, float& scale, u32x4& packed) {
     scale = 1.0f;
     if constexpr (KV == KV_F32) {
         packed = u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
@@ -712,6 +732,15 @@ __device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmc
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
 // Device-coherent accesses for data handed between workgroups on different
 // XCDs (relaxed atomics at agent scope: written through to, and read from,
 // the device coherence point).
@@ -723,6 +752,10 @@ __device__ __forceinline__ float coherent_load(const float* p) {
 }
 // Waits until this thread's stores have been acknowledged.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-position tiles whose loads each wave of the grouped-query pass keeps
+// in flight (register sets in rotation).
+constexpr int kGqaDepth = 2;
 
 // Largest batch the balanced schedule handles (its per-sequence work
 // offsets live in LDS); larger batches take the vector-ALU pass.
@@ -743,13 +776,14 @@ template <int D> struct GqaLds {
 };
 
 // One segment [pos0, pos1) of one unit (sequence b, KV head j, head group
-// hgi) streamed by the whole workgroup.  On return the workgroup's merged
-// state sits in LDS: n_states softmax states (m, l, o[HP][D]), one per wave
-// plus the appended row's when the segment holds it.
+// hgi) streamed by the whole workgroup.  On return the workgroup's states
+// sit in LDS: n_states softmax states (m, l, o[HP][D]), one per wave (o in
+// `tiles`) plus, when the segment holds the new row, the appended row's
+// (m and l in slot NW, o in sm_newo).
 template <int KV, int D, int HP, int NW, bool PG>
 __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles, unsigned char* qbuf,
-                                           float (*sm_m)[HP], float (*sm_l)[HP], int b, int j,
-                                           int hgi, int L, int pos0, int pos1) {
+                                           float (*sm_m)[HP], float (*sm_l)[HP], float* sm_newo,
+                                           int b, int j, int hgi, int L, int pos0, int pos1) {
     using MF = Mfma<KV>;
     using LD = GqaLds<D>;
     typedef typename MF::vec8 vec8;
@@ -787,44 +821,73 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
     unsigned char* ktile = tiles + wave * LD::WAVE;
     unsigned char* vtile = ktile + 16 * LD::KPITCH;
 
-    // K and V rows in the load layout: one wave-wide load is RPI whole rows
-    u32x4 kr[VL], vr[VL];
-    auto issue = [&](int base) {
+    // K and V rows in the load layout: one wave-wide load is RPI whole rows.
+    // DEPTH register sets rotate, so each wave has the loads of DEPTH tiles
+    // in flight while it works on one (set indices are compile-time).
+    constexpr int DEPTH = kGqaDepth;
+    u32x4 kr[DEPTH][VL], vr[DEPTH][VL];
+    auto issue = [&](auto set, int base) {
+        constexpr int S = decltype(set)::value;
         if constexpr (PG) {
             const auto kps = page_rsrc(p.k_cache, ROW_BYTES, tbl, p, j, base, stream_end, bad);
             const auto vps = page_rsrc(p.v_cache, ROW_BYTES, tbl, p, j, base, stream_end, bad);
 #pragma unroll
             for (int u = 0; u < VL; ++u) {
                 const int off = (u * RPI + r) * ROW_BYTES + c * 16;
-                kr[u] = __builtin_amdgcn_raw_buffer_load_b128(kps, off, 0, kStream);
-                vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vps, off, 0, kStream);
+                kr[S][u] = __builtin_amdgcn_raw_buffer_load_b128(kps, off, 0, kStream);
+                vr[S][u] = __builtin_amdgcn_raw_buffer_load_b128(vps, off, 0, kStream);
             }
         } else {
 #pragma unroll
             for (int u = 0; u < VL; ++u) {
                 const int off = (base + u * RPI + r) * ROW_BYTES + c * 16;
-                kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStream);
-                vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStream);
+                kr[S][u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStream);
+                vr[S][u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStream);
             }
         }
     };
-    int base = pos0 + wave * 16;
-    issue(base);
-    __builtin_amdgcn_sched_barrier(0);
-
     // query operand of S^T, shared by the workgroup: column n = head h0 + n
     // (zero past the group), hi and lo halves, in the K tile's layout; one
-    // 16-byte piece of one head per thread
-    for (int idx = threadIdx.x; idx < 16 * LPR; idx += NTH) {
-        const int col = idx / LPR;
-        const int pc = idx - col * LPR;
+    // 16-byte piece of one head per thread.  Its loads go out first, so that
+    // waiting for them leaves the K/V loads issued next in flight.
+    static_assert(16 * LPR <= NTH, "one query piece per thread");
+    const int qcol = threadIdx.x / LPR;
+    const int qpc = threadIdx.x - qcol * LPR;
+    const bool qload = threadIdx.x < 16 * LPR && qcol < heads_here;
+    const size_t qh_idx = (size_t)h0 + min(qcol, heads_here - 1);
+    // (without a bias the same offset is read from q, in bounds, and unused:
+    // no branch, so nothing waits for these loads before the K/V issue)
+    const uint16_t* bsrc = (const uint16_t*)(p.bias ? p.bias : p.q);
+    u32x4 qraw = u32x4{0u, 0u, 0u, 0u}, braw = u32x4{0u, 0u, 0u, 0u};
+    if (qload) {
+        qraw = *(const u32x4*)((const uint16_t*)p.q + ((size_t)b * p.H + qh_idx) * D + qpc * 8);
+        braw = *(const u32x4*)(bsrc + qh_idx * D + qpc * 8);
+    }
+    // the appended row's inputs (the piece holding position L-1, wave 0):
+    // loaded now, so the row is stored and scored while the first tiles are
+    // in flight (without a bias the offsets fall back to valid ones, unused)
+    const bool new_here = owns_new && wave == 0;
+    u32x4 nk = u32x4{0u, 0u, 0u, 0u}, nv = nk, nbk = nk, nbv = nk;
+    if (new_here) {
+        const size_t src = ((size_t)b * p.Hkv + j) * D + c * EPL;
+        nk = *(const u32x4*)((const uint16_t*)p.k_new + src);
+        nv = *(const u32x4*)((const uint16_t*)p.v_new + src);
+        const uint16_t* bb = (const uint16_t*)(p.bias ? p.bias : p.k_new);
+        nbk = *(const u32x4*)(bb + (p.bias ? (size_t)(p.H + j) * D : 0) + c * EPL);
+        nbv = *(const u32x4*)(bb + (p.bias ? (size_t)(p.H + p.Hkv + j) * D : 0) + c * EPL);
+    }
+
+    int base = pos0 + wave * 16;
+    static_for<DEPTH>([&](auto set) { issue(set, base + decltype(set)::value * BLOCK_ROWS); });
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (threadIdx.x < 16 * LPR) {
         float x[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        if (col < heads_here) {
-            const size_t h = (size_t)h0 + col;
-            load_act<KV, 8>(p.q, ((size_t)b * p.H + h) * D + pc * 8, x);
+        if (qload) {
+            Elem<KV>::unpack(qraw, x);
             if (p.bias) {
                 float bx[8];
-                load_act<KV, 8>(p.bias, h * D + pc * 8, bx);
+                Elem<KV>::unpack(braw, bx);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = x[e] + bx[e];
             }
@@ -833,10 +896,53 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
         }
         vec8 hi, lo;
         MF::split8(x, hi, lo);
-        *(vec8*)(qbuf + col * LD::KPITCH + pc * 16) = hi;
-        *(vec8*)(qbuf + 16 * LD::KPITCH + col * LD::KPITCH + pc * 16) = lo;
+        *(vec8*)(qbuf + qcol * LD::KPITCH + qpc * 16) = hi;
+        *(vec8*)(qbuf + 16 * LD::KPITCH + qcol * LD::KPITCH + qpc * 16) = lo;
     }
     __syncthreads();
+
+    // the appended row: stored, and kept as one more softmax state (score
+    // from the staged query halves, as for every other row of the pass)
+    if (new_here) {
+        float kx[EPL], vx[EPL], bx[EPL], ks, vs;
+        Elem<KV>::unpack(nk, kx);
+        Elem<KV>::unpack(nv, vx);
+        if (p.bias) {
+            Elem<KV>::unpack(nbk, bx);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) kx[e] = kx[e] + bx[e];
+            Elem<KV>::unpack(nbv, bx);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) vx[e] = vx[e] + bx[e];
+        }
+        u32x4 kpk, vpk;
+        store_new_row<KV, EPL, LPR>(kx, kx, ks, kpk);
+        store_new_row<KV, EPL, LPR>(vx, vx, vs, vpk);
+        size_t nrow, splane;
+        const bool ok = new_row_index<PG>(p, b, j, L - 1, nrow, splane);
+        if (ok && hgi == 0 && r == 0) {
+            *(u32x4*)((char*)p.k_cache + nrow * ROW_BYTES + c * 16) = kpk;
+            *(u32x4*)((char*)p.v_cache + nrow * ROW_BYTES + c * 16) = vpk;
+        }
+#pragma unroll
+        for (int h = 0; h < HP; ++h) {
+            float qh[8], ql[8];
+            Elem<KV>::unpack(*(const u32x4*)(qbuf + h * LD::KPITCH + c * 16), qh);
+            Elem<KV>::unpack(*(const u32x4*)(qbuf + 16 * LD::KPITCH + h * LD::KPITCH + c * 16), ql);
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) d = fmaf(qh[e] + ql[e], kx[e], d);
+            d = group_sum<LPR>(d);
+            if (r == 0) {
+                if (c == 0) {
+                    sm_m[NW][h] = d;
+                    sm_l[NW][h] = ok ? 1.0f : __builtin_nanf("");
+                }
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) sm_newo[h * D + c * EPL + e] = vx[e];
+            }
+        }
+    }
 
     float m = kNegInf;                      // head n: running max (same in all four quads)
     float l = 0.0f;                         // head n: this lane's share of the sum
@@ -844,16 +950,18 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
 #pragma unroll
     for (int tn = 0; tn < DT; ++tn) acc[tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (; base < stream_end; base += BLOCK_ROWS) {
-        // stage this tile in LDS, then send the next tile's loads out
+    // one 16-position tile starting at tb, from register set `set`
+    auto tile = [&](auto set, int tb) {
+        constexpr int S = decltype(set)::value;
+        // stage the tile in LDS, then send the loads DEPTH tiles ahead out
         lds_wave_fence();
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
-            *(u32x4*)(ktile + (u * RPI + r) * LD::KPITCH + c * 16) = kr[u];
-            *(u32x4*)(vtile + (u * RPI + r) * LD::VPITCH + c * 16) = vr[u];
+            *(u32x4*)(ktile + (u * RPI + r) * LD::KPITCH + c * 16) = kr[S][u];
+            *(u32x4*)(vtile + (u * RPI + r) * LD::VPITCH + c * 16) = vr[S][u];
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue(base + BLOCK_ROWS);
+        issue(set, tb + DEPTH * BLOCK_ROWS);
         __builtin_amdgcn_sched_barrier(0);
         lds_wave_fence();
 
@@ -868,14 +976,14 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
             st = MF::mma32(ka, qh, st);
             st = MF::mma32(ka, ql, st);
             // one step's operands live at a time (registers hold the next
-            // tile's loads and the accumulators)
+            // tiles' loads and the accumulators)
             __builtin_amdgcn_sched_barrier(0);
         }
 
         // online softmax per head (column n) over the positions of the tile
         float s[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = base + 4 * g + i < stream_end ? st[i] : kNegInf;
+        for (int i = 0; i < 4; ++i) s[i] = tb + 4 * g + i < stream_end ? st[i] : kNegInf;
         float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -911,13 +1019,18 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
             acc[tn] = MF::mma16(pl, vb, acc[tn]);
             if (tn & 1) __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    // DEPTH tiles per trip with no exit in between, so that the waits the
+    // compiler places before each tile's registers stay partial (a tile
+    // past the end is all masked: its loads fetch nothing, its weights are 0)
+    for (; base < stream_end; base += DEPTH * BLOCK_ROWS)
+        static_for<DEPTH>([&](auto set) { tile(set, base + decltype(set)::value * BLOCK_ROWS); });
 
     // l over the four quads of the column
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     __syncthreads();                        // every wave is done with its tiles
-    float* sm_o = (float*)tiles;            // [NW + 1][HP][D]
+    float* sm_o = (float*)tiles;            // [NW][HP][D]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * g + i;
@@ -931,45 +1044,6 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
         sm_l[wave][n] = bad ? __builtin_nanf("") : l;   // a page outside the pool: NaN result
     }
 
-    // the appended row: stored by wave 0, and kept as one more softmax state
-    if (owns_new && wave == 0) {
-        const int pnew = L - 1;
-        const size_t src_row = (size_t)b * p.Hkv + j;
-        float kx[EPL], vx[EPL], ks, vs;
-        u32x4 kpk, vpk;
-        make_new_row<KV, D, EPL, LPR>(p, p.k_new, p.H + j, src_row, c, kx, ks, kpk);
-        make_new_row<KV, D, EPL, LPR>(p, p.v_new, p.H + p.Hkv + j, src_row, c, vx, vs, vpk);
-        size_t nrow, splane;
-        const bool ok = new_row_index<PG>(p, b, j, pnew, nrow, splane);
-        if (ok && hgi == 0 && r == 0) {
-            *(u32x4*)((char*)p.k_cache + nrow * ROW_BYTES + c * 16) = kpk;
-            *(u32x4*)((char*)p.v_cache + nrow * ROW_BYTES + c * 16) = vpk;
-        }
-#pragma unroll
-        for (int h = 0; h < HP; ++h) {
-            const int hq = min(h0 + h, p.H - 1);
-            float qx[EPL];
-            load_act<KV, EPL>(p.q, ((size_t)b * p.H + hq) * D + c * EPL, qx);
-            if (p.bias) {
-                float bx[EPL];
-                load_act<KV, EPL>(p.bias, (size_t)hq * D + c * EPL, bx);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) qx[e] = qx[e] + bx[e];
-            }
-            float d = 0.0f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) d = fmaf(qx[e] * p.qscale, kx[e], d);
-            d = group_sum<LPR>(d);
-            if (r == 0) {
-                if (c == 0) {
-                    sm_m[NW][h] = d;
-                    sm_l[NW][h] = ok ? 1.0f : __builtin_nanf("");
-                }
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) sm_o[(NW * HP + h) * D + c * EPL + e] = vx[e];
-            }
-        }
-    }
     __syncthreads();
     return owns_new ? NW + 1 : NW;
 }
@@ -991,7 +1065,7 @@ __global__ void __launch_bounds__(64 * NW) gqa_kernel(const Params p) {
     using A = Act<KV>;
     using LD = GqaLds<D>;
     constexpr int NTH = 64 * NW;
-    constexpr int O_BYTES = (NW + 1) * HP * D * 4;
+    constexpr int O_BYTES = NW * HP * D * 4;
     static_assert(HP == 4 || HP == 8, "4 or 8 heads per pass");
 
     // per-wave tiles while streaming; the merge buffers afterwards
@@ -999,78 +1073,90 @@ __global__ void __launch_bounds__(64 * NW) gqa_kernel(const Params p) {
     __shared__ __attribute__((aligned(16))) unsigned char qbuf[LD::QBYTES];
     __shared__ float sm_m[NW + 1][HP];      // slot NW: the appended row
     __shared__ float sm_l[NW + 1][HP];
-    __shared__ int sm_pref[kGqaMaxBatch + 1];   // first piece of each sequence
-    __shared__ int sm_len[kGqaMaxBatch];
+    __shared__ float sm_newo[HP * D];       // the appended row's values
     __shared__ int sm_last;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int upb = p.Hkv * p.n_hg;         // units per sequence
     const int target = gridDim.x - p.B * upb;
 
-    // valid lengths, total work, slice length W, pieces per unit n_b and
-    // their exclusive prefix (in workgroups)
-    for (int i = threadIdx.x; i < p.B; i += NTH) {
-        const int Lb = p.seq_lens ? p.seq_lens[i] : p.step;
-        sm_len[i] = (Lb >= 1 && Lb <= p.step) ? Lb : 0;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        int tot = 0;
-        for (int base = 0; base < p.B; base += 64) tot += base + lane < p.B ? sm_len[base + lane] : 0;
-        tot = __builtin_amdgcn_readfirstlane(wave_sum_int(tot));
-        const long long total = (long long)tot * upb;
-        int W = (int)((total + target - 1) / max(target, 1));
-        W = max(W, p.seg_min);
-        int carry = 0;
-        for (int base = 0; base < p.B; base += 64) {
-            const int idx = base + lane;
-            const int Lb = idx < p.B ? sm_len[idx] : 0;
-            int v = Lb > 0 ? max(1, (Lb + W / 2) / W) * upb : 0;
+    // Every wave derives the schedule on its own, in registers (no LDS, no
+    // barrier): lane l holds sequences l, l + 64, ...; valid lengths, total
+    // work, slice length W, pieces per sequence n_b * upb and their prefix,
+    // then the sequence whose pieces include this workgroup's.
+    constexpr int NCH = kGqaMaxBatch / 64;
+    int len[NCH];
+    int tot = 0;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int t = __shfl_up(v, off);
-                if (lane >= off) v += t;
-            }
-            if (idx < p.B) sm_pref[idx + 1] = carry + v;
-            carry += __shfl(v, 63);
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int idx = ch * 64 + lane;
+        int Lb = 0;
+        if (idx < p.B) {
+            Lb = p.seq_lens ? p.seq_lens[idx] : p.step;
+            Lb = (Lb >= 1 && Lb <= p.step) ? Lb : 0;
         }
-        if (lane == 0) sm_pref[0] = 0;
+        len[ch] = Lb;
+        tot += Lb;
     }
-    __syncthreads();
-
-    // NaN rows for sequences whose length is invalid (no append for them)
-    for (int bb = blockIdx.x; bb < p.B; bb += gridDim.x) {
-        if (sm_len[bb] == 0)
-            for (int idx = threadIdx.x; idx < p.H * D; idx += NTH)
-                A::st(p.out, (size_t)bb * p.H * D + idx, __builtin_nanf(""));
-    }
+    tot = __builtin_amdgcn_readfirstlane(wave_sum_int(tot));
+    const long long total = (long long)tot * upb;
+    const int W = max((int)((total + target - 1) / max(target, 1)), p.seg_min);
     const int blk = blockIdx.x;
-    if (blk >= sm_pref[p.B]) return;
-
-    // this workgroup's piece: sequence b with pref[b] <= blk < pref[b+1]
-    int lo = 0, hi = p.B;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (sm_pref[mid] <= blk) lo = mid;
-        else hi = mid;
+    int carry = 0, b = -1, first = 0, npc = 0, L = 0;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int v = len[ch] > 0 ? max(1, (len[ch] + W / 2) / W) * upb : 0;
+        int incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        const bool hit = blk >= carry + incl - v && blk < carry + incl;
+        const unsigned long long m = __ballot(hit);
+        if (m) {
+            const int l = __builtin_ctzll(m);
+            b = ch * 64 + l;
+            first = carry + __builtin_amdgcn_readlane(incl - v, l);
+            npc = __builtin_amdgcn_readlane(v, l);
+            L = __builtin_amdgcn_readlane(len[ch], l);
+        }
+        carry += __builtin_amdgcn_readlane(incl, 63);
     }
-    const int b = lo;
-    const int L = sm_len[b];
-    const int nseg = (sm_pref[b + 1] - sm_pref[b]) / upb;
-    const int local = blk - sm_pref[b];
+
+    // NaN rows for sequences whose length is invalid (no append for them):
+    // block bb < B checks sequence bb (the grid has at least B blocks)
+    if (blk < p.B) {
+        int Lbb = 0;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+            if (ch == blk / 64) Lbb = __builtin_amdgcn_readlane(len[ch], blk % 64);
+        if (Lbb == 0)
+            for (int idx = threadIdx.x; idx < p.H * D; idx += NTH)
+                A::st(p.out, (size_t)blk * p.H * D + idx, __builtin_nanf(""));
+    }
+    if (b < 0) return;                      // no piece for this workgroup
+
+    // the piece, the same in every wave: scalar registers, so that the loop
+    // bounds, the descriptors and block-table reads stay scalar
+    b = __builtin_amdgcn_readfirstlane(b);
+    L = __builtin_amdgcn_readfirstlane(L);
+    const int nseg = __builtin_amdgcn_readfirstlane(npc / upb);
+    const int local = __builtin_amdgcn_readfirstlane(blk - first);
     const int ub = local / nseg;            // unit within the sequence: j * n_hg + hgi
     const int seg = local - ub * nseg;
     // piece boundaries on multiples of 16 (a tile never straddles a page)
-    const int pos0 = seg == 0 ? 0 : (int)((long long)seg * L / nseg) & ~15;
-    const int pos1 = seg == nseg - 1 ? L : (int)((long long)(seg + 1) * L / nseg) & ~15;
+    const int pos0 = __builtin_amdgcn_readfirstlane(seg == 0 ? 0 : (int)((long long)seg * L / nseg) & ~15);
+    const int pos1 = __builtin_amdgcn_readfirstlane(seg == nseg - 1 ? L
+                                                    : (int)((long long)(seg + 1) * L / nseg) & ~15);
     const int j = ub / p.n_hg;
     const int hgi = ub - j * p.n_hg;
     const int h0 = j * p.G + hgi * HP;
     const int heads_here = min(HP, p.G - hgi * HP);
     const int unit = b * upb + ub;
 
-    const int n_states = gqa_segment<KV, D, HP, NW, PG>(p, smem, qbuf, sm_m, sm_l, b, j, hgi, L, pos0, pos1);
+    const int n_states = gqa_segment<KV, D, HP, NW, PG>(p, smem, qbuf, sm_m, sm_l, sm_newo, b, j, hgi,
+                                                        L, pos0, pos1);
     float* sm_o = (float*)smem;
 
     // merge this workgroup's states; write out, or the unit's partial slot
@@ -1085,7 +1171,7 @@ __global__ void __launch_bounds__(64 * NW) gqa_kernel(const Params p) {
         for (int w = 0; w < n_states; ++w) {
             const float a = fast_exp2(sm_m[w][h] - ms);
             lsum += a * sm_l[w][h];
-            o += a * sm_o[(w * HP + h) * D + d];
+            o += a * (w < NW ? sm_o[(w * HP + h) * D + d] : sm_newo[h * D + d]);
         }
         if (nseg == 1) {
             A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o / lsum);
@@ -1197,8 +1283,8 @@ constexpr int unroll_for(int gt) { return gt <= 2 ? 8 : 4; }
 // of the fp32/fp16/bf16 caches fit without spilling.
 constexpr bool wide_built(int kv, int gt) { return gt == 1 && kv != KV_I8; }
 
-constexpr int kGqaWaves = 4;
-constexpr int kGqaBlocksPerCu = 2;   // target pieces per CU (3 fit: about 47 KiB of LDS and 140 registers each)
+constexpr int kGqaWaves = 8;
+constexpr int kGqaBlocksPerCu = 1;   // target pieces per CU (one 8-wave workgroup: about 83 KiB of LDS)
 
 template <int KV, int D, int HP, bool PG>
 hipError_t launch_gqa_t(const Params& p, hipStream_t s) {
