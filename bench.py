@@ -127,12 +127,96 @@ def cpu_baseline(case, inputs, lens, budget_s: float):
                       f"of K/V), fp64 oracle, best of {runs} runs, {total:.1f} s in total"}
 
 
+def run_projection(args, case):
+    """The fused QKV projection alone, weights rotating over distinct sets:
+    bound by the HBM stream of the weights."""
+    from decode_step_attention_amd import ftm
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev) if args.graph else torch.cuda.current_stream(dev)
+    print(f"# {case.name}: batch {case.batch}, hidden {case.hidden} -> {case.n_heads}q/{case.n_kv_heads}kv "
+          f"heads x {case.head_dim}, {case.dtype}; {case.rotate} weight sets", file=sys.stderr, flush=True)
+    sets = [W.make_proj_inputs(case, dev, layer=i) for i in range(case.rotate)]
+    dt = W.TORCH_DTYPES[case.dtype]
+    q = torch.empty((case.batch, case.n_heads, case.head_dim), dtype=dt, device=dev)
+    k = torch.empty((case.batch, case.n_kv_heads, case.head_dim), dtype=dt, device=dev)
+    v = torch.empty_like(k)
+    calls = [ftm.ftm_qkv_proj_prepared(st["x"], st["w"], st["bias"], q, k, v, stream=stream.cuda_stream)
+             for st in sets]
+    nbytes = W.proj_bytes(case)
+    for i in range(args.warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    graphs = []
+    if args.graph:
+        for c in calls:
+            ftm.ftm_graph_begin(stream.cuda_stream)
+            try:
+                c()
+            finally:
+                graphs.append(ftm.ftm_graph_end(stream.cuda_stream))
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for i in range(args.steps):
+        if graphs:
+            ftm.ftm_graph_launch(graphs[i % len(graphs)], stream.cuda_stream)
+        else:
+            calls[i % len(calls)]()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for g in graphs:
+        ftm.ftm_graph_destroy(g)
+    gpu_ms = r0.elapsed_time(r1)
+    elapsed = t1 - t0
+    avg_us = gpu_ms * 1e3 / args.steps
+    achieved = nbytes / (avg_us * 1e-6) / 1e9
+    traffic = read_traffic("qkv_proj_kernel", case.name)
+    result = {
+        "metric": "fused QKV projection GB/s (weights + x + outputs, % of HBM peak)",
+        "value": round(nbytes * args.steps / elapsed / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.dtype,
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": f"{case.name}: x [{case.batch}, {case.hidden}] times W "
+                               f"[{case.n_out}, {case.hidden}] -> q/k_new/v_new",
+                   "batch": case.batch, "hidden": case.hidden, "n_heads": case.n_heads,
+                   "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim, "weight_sets_rotated": case.rotate,
+                   "launch": "HIP graph replay" if graphs else "one library call"},
+        "pct_hbm_peak": round(100 * nbytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBS, 2),
+        "bytes_per_step": nbytes, "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
+                     "kernel": "qkv_proj_kernel", "avg_launch_us": round(avg_us, 2),
+                     "timing": "events bracketing the timed region / launches",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "flops_per_launch": 2 * case.batch * case.n_out * case.hidden},
+    }
+    if args.cpu_budget > 0:
+        import oracle
+        host = {kk: vv.cpu() for kk, vv in sets[0].items()}
+        hn = {kk: (vv.view(torch.int16).numpy().view(np.uint16) if case.dtype == "bf16" else vv.numpy())
+              for kk, vv in host.items()}
+        runs, total, best = 0, 0.0, float("inf")
+        while runs < 3 or (total < args.cpu_budget and runs < 50):
+            c0 = time.perf_counter()
+            oracle.qkv_proj(hn["x"], hn["w"], hn["bias"], case.n_heads, case.n_kv_heads, case.head_dim,
+                            case.dtype)
+            dtm = time.perf_counter() - c0
+            best, total, runs = min(best, dtm), total + dtm, runs + 1
+        result["cpu_baseline"] = {"value": round(nbytes / best / 1e9, 3), "unit": "GB/s",
+                                  "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                  "sample": f"the whole projection (weight set 0), float64 numpy, best of {runs} runs"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="7b", choices=sorted(W.CASES))
+    ap.add_argument("--config", default="7b", choices=sorted(W.CASES) + sorted(W.PROJ_CASES))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0 skips it)")
     ap.add_argument("--graph", action="store_true",
@@ -145,6 +229,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.config in W.PROJ_CASES:
+        run_projection(args, W.PROJ_CASES[args.config])
+        return
     from decode_step_attention_amd import ftm
 
     dev = torch.device("cuda:0")

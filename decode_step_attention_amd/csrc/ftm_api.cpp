@@ -526,6 +526,47 @@ int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new, co
     return decode_impl(a);
 }
 
+int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k_new, void* v_new,
+                 int batch, int hidden, int n_heads, int n_kv_heads, int head_dim, int act_dtype,
+                 void* stream_ptr) {
+    if (!x || !w || !q || !k_new || !v_new)
+        return fail(FTM_ERR_INVALID_ARG, "a required pointer (x, w, q, k_new, v_new) is NULL");
+    if (batch < 1 || hidden < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
+        return fail(FTM_ERR_INVALID_ARG, "batch, hidden, n_heads, n_kv_heads and head_dim must be >= 1");
+    if (n_heads % n_kv_heads != 0)
+        return fail(FTM_ERR_INVALID_ARG, "n_heads (" + std::to_string(n_heads) +
+                                             ") is not a multiple of n_kv_heads (" +
+                                             std::to_string(n_kv_heads) + ")");
+    if (act_dtype != FTM_F16 && act_dtype != FTM_BF16)
+        return fail(act_dtype == FTM_F32 ? FTM_ERR_UNSUPPORTED : FTM_ERR_INVALID_ARG,
+                    "the projection takes fp16 or bf16 activations and weights, not dtype " +
+                        std::to_string(act_dtype));
+    {
+        const void* vec[] = {x, w, bias, q, k_new, v_new};
+        for (const void* v : vec)
+            if (((uintptr_t)v & 15u) != 0)
+                return fail(FTM_ERR_INVALID_ARG, "x, w, bias, q, k_new and v_new must be 16-byte aligned");
+    }
+    if (batch > 64)
+        return fail(FTM_ERR_UNSUPPORTED, "batch " + std::to_string(batch) + " (built: up to 64 rows)");
+    if (hidden % 256 != 0 || hidden > 65536)
+        return fail(FTM_ERR_UNSUPPORTED, "hidden " + std::to_string(hidden) +
+                                             " (built: multiples of 256 up to 65536)");
+    if (head_dim % 16 != 0)
+        return fail(FTM_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) + " (built: multiples of 16)");
+    const long long n_out = (long long)(n_heads + 2 * n_kv_heads) * head_dim;
+    if (n_out / 16 > 0x7fffffffLL || n_out * hidden * 2 > (1LL << 40))
+        return fail(FTM_ERR_UNSUPPORTED, "weight matrix too large");
+    ftm::QkvParams p{x, w, bias, q, k_new, v_new, batch, hidden, n_heads, n_kv_heads, head_dim};
+    int device = 0;
+    hipError_t he = hipGetDevice(&device);
+    if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
+    he = ftm::launch_qkv_proj(p, act_dtype, cu_count(device), (hipStream_t)stream_ptr);
+    if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("projection launch: ") + hipGetErrorString(he));
+    g_last_error.clear();
+    return FTM_OK;
+}
+
 int ftm_graph_begin(void* stream) {
     if (!stream) return fail(FTM_ERR_INVALID_ARG, "the null stream cannot be captured: pass a created stream");
     hipError_t e = hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal);

@@ -56,7 +56,20 @@ int gqa_blocks_per_cu();
 // Whether the 16-wave workgroup is built for this cache type and group tile.
 bool wide_ok(int kv, int group_tile);
 
+// The fused QKV projection: y = x W^T (+ bias), split into q, k_new, v_new.
+struct QkvParams {
+    const void* x;          // [B, hidden] act
+    const void* w;          // [(H + 2 Hkv) D, hidden] act
+    const void* bias;       // [(H + 2 Hkv) D] act or null
+    void* q;                // [B, H, D] act
+    void* k_new;            // [B, Hkv, D] act
+    void* v_new;            // [B, Hkv, D] act
+    int B, hidden, H, Hkv, D;
+};
+
 hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, int nw, hipStream_t s);
+// act: KV_F16 or KV_BF16; B <= 64, hidden a multiple of 256, (H + 2 Hkv) D a multiple of 16.
+hipError_t launch_qkv_proj(const QkvParams& p, int act, int n_cu, hipStream_t s);
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);
 
 }  // namespace ftm

@@ -1,0 +1,273 @@
+// qkv_proj.hip -- gfx950 kernel for the fused QKV projection of a decode
+// step: y = x W^T (+ bias) for x [B, hidden] and W [(H + 2 Hkv) D, hidden],
+// written straight into the q [B, H, D], k_new [B, Hkv, D] and v_new
+// [B, Hkv, D] layouts the attention reads ([lpnh.cn/news/2765398] section
+// 2.1: Q, K and V come out of one projection and are split three ways with
+// no extra round trip through memory).
+//
+// At decode batch sizes (B <= 64) the product reads every weight once and
+// does at most 64 multiply-adds per weight: it is bound by the HBM stream
+// of W, so the design streams W exactly once, coalesced, and keeps the
+// arithmetic on the matrix cores out of its way.
+//
+// One workgroup (8 waves) owns 16 FT output features over the whole hidden
+// dimension, split in eight: wave w takes an eighth of the k range.  Per
+// iteration a wave loads 8 KiB of its weight rows (each load instruction
+// covers whole 128-512-byte row segments), stages them in LDS and reads
+// them back in the B-operand layout of v_mfma_f32_16x16x32; x, small and
+// read by every workgroup, comes from L2 directly in the A-operand layout,
+// each load serving FT products.  The next iteration's weights are in
+// flight while the matrix cores work.  The eight partial sums meet in LDS in
+// a fixed order, the bias is added in fp32, and the result is rounded to
+// nearest even.
+#include "ftm_internal.hpp"
+
+#include <cstdlib>
+
+namespace ftm {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;                 // the k range is split across the waves of a workgroup
+constexpr int kRsrcWord3 = 0x00020000;    // raw buffer access, gfx9 family
+constexpr int kStream = 2;                // non-temporal: every weight is read once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0, n, kRsrcWord3);
+}
+
+template <int ACT> struct QMma;
+template <> struct QMma<KV_BF16> {
+    __device__ static f32x4 mma(const u32x4 a, const u32x4 b, const f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static float ld(const void* p, size_t i) {
+        return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+    }
+    // fp32 -> bfloat16, round to nearest even; NaN to the quiet NaN with its sign
+    __device__ static void st(void* p, size_t i, float v) {
+        const uint32_t u = __float_as_uint(v);
+        const uint32_t r = (u & 0x7fffffffu) > 0x7f800000u ? (((u >> 16) & 0x8000u) | 0x7fc0u)
+                                                           : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+        ((uint16_t*)p)[i] = (uint16_t)r;
+    }
+};
+template <> struct QMma<KV_F16> {
+    __device__ static f32x4 mma(const u32x4 a, const u32x4 b, const f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ static float ld(const void* p, size_t i) {
+        return (float)__builtin_bit_cast(_Float16, ((const uint16_t*)p)[i]);
+    }
+    __device__ static void st(void* p, size_t i, float v) {
+        ((uint16_t*)p)[i] = __builtin_bit_cast(uint16_t, (_Float16)v);   // round to nearest even
+    }
+};
+
+// MT: batch tiles of 16 rows (B <= 16 MT).  FT: 16-feature column tiles
+// per workgroup, each wave computing all of them over its k range, so that
+// one load of x serves FT products (FT = MT keeps the bytes of x read per
+// weight byte at one).  A wave iteration covers KIT = 256 / FT k: 8 KiB of
+// weights whatever FT.
+template <int ACT, int MT, int FT>
+__global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p) {
+    using M = QMma<ACT>;
+    constexpr int COLS = 16 * FT;           // output features per workgroup
+    constexpr int KIT = 256 / FT;           // k per wave iteration
+    constexpr int KS = KIT / 32;            // MFMA k-steps per iteration
+    constexpr int PITCH = KIT * 2 + 16;     // LDS row pitch: 16-byte reads of 16 rows hit distinct banks
+    constexpr int LPRW = KIT / 8;           // weight loads: lanes per row (16 bytes each)
+    constexpr int RPIW = 64 / LPRW;         // weight loads: rows per instruction (8 instructions)
+    static_assert(8 * RPIW == COLS, "8 loads cover the workgroup's rows");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;                // MFMA operands: k group
+    const int n = lane & 15;                // MFMA operands: batch row (A), feature (B)
+    const int lrow = lane / LPRW;           // weight loads: row within an instruction's rows
+    const int lcol = lane % LPRW;           // weight loads: 16-byte chunk within the row
+    const int f0 = blockIdx.x * COLS;
+    const int nit = p.hidden / KIT;
+    const int it0 = wave * nit / kWaves;
+    const int it1 = (wave + 1) * nit / kWaves;
+    const uint32_t row_bytes = (uint32_t)p.hidden * 2;
+    // the workgroup's weight rows; x rows past the batch read as zero
+    const auto wrs = make_rsrc((const char*)p.w + (size_t)f0 * row_bytes, COLS * row_bytes);
+    const auto xrs = make_rsrc(p.x, (uint32_t)p.B * row_bytes);
+
+    // per-wave weight tiles; after the loop, the partial sums of the
+    // reduction (at most kWaves / 2 waves' MT x FT tiles at a time)
+    constexpr int TILE = COLS * PITCH;
+    constexpr int RED = kWaves / 2 * MT * FT * 64 * 16;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[TILE * kWaves > RED ? TILE * kWaves : RED];
+    unsigned char* tile = smem + wave * TILE;
+
+    // iterations outside [it0, it1) take an offset past the descriptor's
+    // range: their loads fetch nothing, so the prefetch needs no branch
+    // (a branch around it makes the compiler wait for every load in flight)
+    u32x4 wr[8];
+    auto issue_w = [&](int it) {
+        const uint32_t koff = it < it1 ? (uint32_t)it * (KIT * 2) : 0x40000000u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            wr[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (RPIW * u + lrow) * row_bytes + koff + lcol * 16,
+                                                          0, kStream);
+    };
+    f32x4 acc[MT][FT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) acc[mt][ft] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    issue_w(it0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = it0; it < it1; ++it) {
+        // this iteration's x (A operand: batch row 16 mt + n, k = 32 s + 8 g ..),
+        // issued after the weights of this iteration and before those of the next
+        u32x4 xr[MT][KS];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                xr[mt][s] = __builtin_amdgcn_raw_buffer_load_b128(
+                    xrs, (16 * mt + n) * row_bytes + (it * KIT + 32 * s + 8 * g) * 2, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // stage this iteration's weights, then send the next iteration's out
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < 8; ++u) *(u32x4*)(tile + (RPIW * u + lrow) * PITCH + lcol * 16) = wr[u];
+        __builtin_amdgcn_sched_barrier(0);
+        issue_w(it + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // B operand: feature 16 ft + n, k = 32 s + 8 g ..
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) {
+                const u32x4 wb = *(const u32x4*)(tile + (16 * ft + n) * PITCH + (32 * s + 8 * g) * 2);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt][ft] = M::mma(xr[mt][s], wb, acc[mt][ft]);
+            }
+        }
+    }
+
+    // the partial sums meet in wave 0 as a tree: waves [h, 2h) hand theirs
+    // to waves [0, h) for h = kWaves/2, ..., 1 (fixed order: the result is
+    // deterministic)
+    f32x4* red = (f32x4*)smem;              // [kWaves / 2][MT][FT][64]
+    auto slot = [&](int w, int mt, int ft) { return red + ((w * MT + mt) * FT + ft) * 64 + lane; };
+#pragma unroll
+    for (int h = kWaves / 2; h >= 1; h /= 2) {
+        __syncthreads();                    // the tiles, or the previous round's slots, are free
+        if (wave >= h && wave < 2 * h) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft) *slot(wave - h, mt, ft) = acc[mt][ft];
+        }
+        __syncthreads();
+        if (wave < h) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft) acc[mt][ft] += *slot(wave, mt, ft);
+        }
+    }
+    if (wave != 0) return;
+
+    // C layout: lane (g, n) holds feature f0 + 16 ft + n for batch rows
+    // 16 mt + 4 g + i.  Column tiles never straddle the Q/K/V boundaries
+    // (H D and Hkv D are multiples of 16).
+    const int qd = p.H * p.D, kd = p.Hkv * p.D;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+        const int f = f0 + 16 * ft + n;
+        const int fb = f0 + 16 * ft;        // the tile's first feature, the same in every lane
+        void* dst;
+        int width, col;
+        if (fb < qd) {
+            dst = p.q, width = qd, col = f;
+        } else if (fb < qd + kd) {
+            dst = p.k_new, width = kd, col = f - qd;
+        } else {
+            dst = p.v_new, width = kd, col = f - qd - kd;
+        }
+        const float bf = p.bias ? M::ld(p.bias, f) : 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mt + 4 * g + i;
+                if (row < p.B)
+                    M::st(dst, (size_t)row * width + col, p.bias ? acc[mt][ft][i] + bf : acc[mt][ft][i]);
+            }
+    }
+}
+
+// Column tiles per workgroup: four (x read once per weight byte up to four
+// batch tiles, 128-byte weight row segments) unless that leaves fewer
+// workgroups than half the CUs.  FTM_QKV_COLUMN_TILES (1, 2 or 4) forces
+// the choice.
+int column_tiles(int n_out, int n_cu) {
+    const char* e = std::getenv("FTM_QKV_COLUMN_TILES");
+    const int forced = e ? std::atoi(e) : 0;
+    if (forced == 1 || forced == 2 || forced == 4) return forced;
+    int ft = 4;
+    while (ft > 1 && 2 * (n_out / (16 * ft)) < n_cu) ft /= 2;
+    return ft;
+}
+
+template <int ACT, int MT, int FT>
+hipError_t launch_mf(const QkvParams& p, hipStream_t s) {
+    const int n_out = (p.H + 2 * p.Hkv) * p.D;
+    hipLaunchKernelGGL((qkv_proj_kernel<ACT, MT, FT>), dim3(n_out / (16 * FT)), dim3(64 * kWaves), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int ACT, int MT>
+hipError_t launch_m(const QkvParams& p, int ft, hipStream_t s) {
+    switch (ft) {
+    case 1: return launch_mf<ACT, MT, 1>(p, s);
+    case 2: return launch_mf<ACT, MT, 2>(p, s);
+    case 4: return launch_mf<ACT, MT, 4>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int ACT>
+hipError_t launch_t(const QkvParams& p, int n_cu, hipStream_t s) {
+    const int n_out = (p.H + 2 * p.Hkv) * p.D;
+    const int mt = (p.B + 15) / 16;
+    int ft = column_tiles(n_out, n_cu);
+    while (ft > 1 && n_out % (16 * ft) != 0) ft /= 2;
+    if (p.hidden % (256 / ft) != 0) return hipErrorInvalidValue;
+    switch (mt) {
+    case 1: return launch_m<ACT, 1>(p, ft, s);
+    case 2: return launch_m<ACT, 2>(p, ft, s);
+    case 3: return launch_m<ACT, 3>(p, ft, s);
+    case 4: return launch_m<ACT, 4>(p, ft, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_proj(const QkvParams& p, int act, int n_cu, hipStream_t s) {
+    switch (act) {
+    case KV_F16: return launch_t<KV_F16>(p, n_cu, s);
+    case KV_BF16: return launch_t<KV_BF16>(p, n_cu, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ftm

@@ -24,7 +24,7 @@ _ACT = {FTM_F32: torch.float32, FTM_F16: torch.float16, FTM_BF16: torch.bfloat16
         FTM_I8: torch.float16}
 
 # Every symbol include/ftm.h declares.
-EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_kv_cache_bytes", "ftm_last_error",
+EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_qkv_proj", "ftm_kv_cache_bytes", "ftm_last_error",
            "ftm_version", "ftm_set_split_chunk", "ftm_set_workgroup_waves", "ftm_release_workspaces",
            "ftm_graph_begin", "ftm_graph_end", "ftm_graph_launch", "ftm_graph_destroy",
            "ftm_timing_enable", "ftm_timing_disable", "ftm_timing_read")
@@ -42,6 +42,8 @@ def _load() -> ctypes.CDLL:
     lib.ftm_decode_mha_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i32,
                                          i32, i32, i32, i32, vp, vp, vp]
     lib.ftm_decode_mha_paged.restype = i32
+    lib.ftm_qkv_proj.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.ftm_qkv_proj.restype = i32
     lib.ftm_graph_begin.argtypes = [vp]
     lib.ftm_graph_begin.restype = i32
     lib.ftm_graph_end.argtypes = [vp, ctypes.POINTER(vp)]
@@ -255,6 +257,39 @@ def ftm_decode_mha_paged_prepared(q, k_new, v_new, qkv_bias, k_pages, v_pages, b
                           out, kv_scales, stream)
     keep = (q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, kv_scales)
     return _prepared(lib.ftm_decode_mha_paged, args, keep)
+
+
+def _marshal_qkv(x, w, bias, q, k_new, v_new, stream):
+    if x.dim() != 2 or q.dim() != 3 or k_new.dim() != 3:
+        raise ValueError("x must be [B, hidden], q [B, H, D] and k_new/v_new [B, Hkv, D]")
+    B, hidden = x.shape
+    _, H, D = q.shape
+    Hkv = k_new.shape[1]
+    act = {torch.float16: FTM_F16, torch.bfloat16: FTM_BF16}.get(x.dtype)
+    if act is None:
+        raise TypeError(f"unsupported activation dtype {x.dtype}")
+    N = (H + 2 * Hkv) * D
+    tensors = {"x": (x, x.dtype, (B, hidden)), "w": (w, x.dtype, (N, hidden)),
+               "q": (q, x.dtype, (B, H, D)), "k_new": (k_new, x.dtype, (B, Hkv, D)),
+               "v_new": (v_new, x.dtype, (B, Hkv, D))}
+    if bias is not None:
+        tensors["bias"] = (bias, x.dtype, (N,))
+    _check_tensors(tensors, x.device)
+    return (_ptr(x), _ptr(w), _ptr(bias), _ptr(q), _ptr(k_new), _ptr(v_new), B, hidden, H, Hkv, D, act,
+            _stream_ptr(stream, x.device))
+
+
+def ftm_qkv_proj(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], q: torch.Tensor,
+                 k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+    """The fused QKV projection (see include/ftm.h): q, k_new, v_new =
+    split(x @ w.T + bias).  x [B, hidden], w [(H + 2 Hkv) D, hidden]."""
+    _check(lib.ftm_qkv_proj(*_marshal_qkv(x, w, bias, q, k_new, v_new, stream)))
+
+
+def ftm_qkv_proj_prepared(x, w, bias, q, k_new, v_new, stream=None) -> Callable[[], None]:
+    """ftm_qkv_proj with the arguments marshalled once."""
+    args = _marshal_qkv(x, w, bias, q, k_new, v_new, stream)
+    return _prepared(lib.ftm_qkv_proj, args, (x, w, bias, q, k_new, v_new))
 
 
 def ftm_graph_begin(stream: int) -> None:

@@ -251,3 +251,57 @@ def kv_bytes(case: Case, lens: Optional[List[int]] = None) -> int:
     L = seq_lens(case).tolist() if lens is None else list(lens)
     row = case.head_dim * ELEM_BYTES[case.kv_dtype] + (4 if case.kv_dtype == "i8" else 0)
     return sum(L) * case.n_kv_heads * 2 * row
+
+
+@dataclass(frozen=True)
+class ProjCase:
+    """A fused QKV projection: x [batch, hidden] times W [(H + 2 Hkv) D, hidden].
+    x ~ N(0, 1) and W ~ N(0, 1/hidden), so each output is about N(0, 1);
+    the bias ~ N(0, 1/8)."""
+    name: str
+    batch: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    hidden: int
+    dtype: str
+    rotate: int = 1
+    seed: int = 2000
+
+    @property
+    def n_out(self) -> int:
+        return (self.n_heads + 2 * self.n_kv_heads) * self.head_dim
+
+    def with_(self, **kw) -> "ProjCase":
+        return replace(self, **kw)
+
+
+# The projections that feed the attention workloads' layers (hidden = H D):
+# the 7B-shaped layer, the 13B-shaped layer of the INT8 workload, and the
+# grouped-query layer.  Weight sets rotate so the 256 MB last-level cache
+# cannot serve repeated reads.
+PROJ_CASES: Dict[str, ProjCase] = {
+    "qkv_7b": ProjCase("qkv_7b", 8, 32, 32, 128, 4096, "f16", rotate=8, seed=2001),
+    "qkv_13b": ProjCase("qkv_13b", 64, 40, 40, 128, 5120, "f16", rotate=4, seed=2004),
+    "qkv_gqa": ProjCase("qkv_gqa", 16, 64, 8, 128, 8192, "bf16", rotate=4, seed=2003),
+}
+
+
+def make_proj_inputs(case: ProjCase, device="cpu", layer: int = 0) -> Dict[str, torch.Tensor]:
+    """x, w, bias of one projection (``case.seed`` and ``layer`` pick the draw)."""
+    dt = TORCH_DTYPES[case.dtype]
+
+    def draw(tag, shape, scale):
+        g = torch.Generator(device=device)
+        g.manual_seed((case.seed * 1_000_003 + tag * 10_007 + layer * 101) % (2 ** 62))
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * scale).to(dt)
+
+    return {"x": draw(1, (case.batch, case.hidden), 1.0),
+            "w": draw(2, (case.n_out, case.hidden), 1.0 / math.sqrt(case.hidden)),
+            "bias": draw(3, (case.n_out,), 1.0 / math.sqrt(8.0))}
+
+
+def proj_bytes(case: ProjCase) -> int:
+    """Bytes one projection must move: the weights, x and the outputs."""
+    e = ELEM_BYTES[case.dtype]
+    return (case.n_out * case.hidden + case.batch * case.hidden + case.batch * case.n_out) * e

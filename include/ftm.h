@@ -156,6 +156,37 @@ int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new,
                          int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
                          float* kv_scales, void* out, void* stream);
 
+/*
+ * ftm_qkv_proj -- the fused QKV projection that feeds a decode step.
+ *
+ * One projection produces Q, K and V for every sequence and its output is
+ * split three ways straight into the layouts ftm_decode_mha reads
+ * ([lpnh.cn/news/2765398] section 2.1: Q, K and V from one fused kernel,
+ * split without an extra write; section 1.2: every decode step reads the
+ * whole weight matrix):
+ *   y = x W^T (+ bias),  q = y[:, 0 : H D],  k_new = y[:, H D : (H + Hkv) D],
+ *   v_new = y[:, (H + Hkv) D :], each reshaped per head.
+ *
+ * Shapes (row-major, contiguous; N = (n_heads + 2 n_kv_heads) head_dim):
+ *   x      [batch, hidden]     act_dtype, read
+ *   w      [N, hidden]         act_dtype, read (one row of weights per output feature)
+ *   bias   [N] act_dtype or NULL
+ *   q      [batch, n_heads, head_dim]      act_dtype, written
+ *   k_new, v_new [batch, n_kv_heads, head_dim]  act_dtype, written
+ * act_dtype is FTM_F16 or FTM_BF16.  Products accumulate in fp32 (on the
+ * matrix cores), the bias is added in fp32, and the result is rounded to
+ * nearest even.  When the bias is added here, pass qkv_bias = NULL to
+ * ftm_decode_mha (or add it there instead, and pass NULL here).
+ *
+ * Supported: batch 1..64, hidden a multiple of 256 up to 65536, head_dim a
+ * multiple of 16.  All pointers 16-byte aligned; q, k_new and v_new must
+ * not overlap x or w.  Errors as for ftm_decode_mha (FTM_ERR_UNSUPPORTED for
+ * fp32 or sizes outside the supported set).  Only enqueues on `stream`.
+ */
+int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k_new,
+                 void* v_new, int batch, int hidden, int n_heads, int n_kv_heads, int head_dim,
+                 int act_dtype, void* stream);
+
 /* ---- HIP graphs ----------------------------------------------------------
  * A decode step of a model is one call per layer on fixed buffers; its
  * kernel launches can be recorded once and replayed as one graph launch, so
@@ -165,8 +196,8 @@ int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new,
  * section 2.3).
  *
  * ftm_graph_begin starts capturing `stream` (a created stream, not the null
- * stream; capture mode thread-local).  The ftm_decode_mha and
- * ftm_decode_mha_paged calls that follow on that stream and host thread are
+ * stream; capture mode thread-local).  The ftm_decode_mha, ftm_decode_mha_paged
+ * and ftm_qkv_proj calls that follow on that stream and host thread are
  * recorded, not run.  They allocate nothing: each needs a workspace that an
  * earlier call of the same or a larger shape on the same stream has already
  * grown, or it fails with FTM_ERR_INVALID_ARG and records nothing (the

@@ -180,6 +180,48 @@ def decode_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, s
     return out
 
 
+def qkv_proj(x, w, bias, n_heads, n_kv_heads, head_dim, act_dtype):
+    """The fused QKV projection of one decode step, in float64.
+
+    One projection produces Q, K and V together, and its output is split
+    three ways ([lpnh.cn/news/2765398] section 2.1): y = x W^T (+ bias)
+    with x [B, hidden] and W [(H + 2 Hkv) D, hidden] (one row of weights
+    per output feature), then features [0, H D) are Q as [B, H, D], the next
+    Hkv D are K and the last Hkv D are V, each [B, Hkv, D].
+
+    x, w, bias hold act_dtype values (bfloat16 as uint16 bit patterns).
+    Returns (q, k, v) float64 arrays, unrounded."""
+    xf = cache_to_f64(np.asarray(x), act_dtype)
+    wf = cache_to_f64(np.asarray(w), act_dtype)
+    B = xf.shape[0]
+    H, Hkv, D = n_heads, n_kv_heads, head_dim
+    N = (H + 2 * Hkv) * D
+    if wf.shape != (N, xf.shape[1]):
+        raise ValueError(f"w must be [{N}, {xf.shape[1]}]")
+    y = xf @ wf.T
+    if bias is not None:
+        y = y + cache_to_f64(np.asarray(bias), act_dtype)[None, :]
+    q = y[:, :H * D].reshape(B, H, D)
+    k = y[:, H * D:(H + Hkv) * D].reshape(B, Hkv, D)
+    v = y[:, (H + Hkv) * D:].reshape(B, Hkv, D)
+    return q, k, v
+
+
+def round_to_act(y, act_dtype):
+    """float64 values rounded to nearest even in the activation type, as the
+    array type the oracle takes (bfloat16 as uint16 bit patterns)."""
+    y = np.asarray(y, dtype=np.float64)
+    if act_dtype == "f32":
+        return y.astype(np.float32)
+    if act_dtype == "f16":
+        with np.errstate(over="ignore"):
+            return y.astype(np.float16)       # numpy rounds float64 to binary16 to nearest even
+    # via fp32 (exact double rounding: 24 >= 2 * 8 + 2), then the oracle's RNE
+    f = _load().orc_float_to_bf16_rne
+    flat = y.astype(np.float32).ravel()
+    return np.array([f(float(v)) for v in flat], dtype=np.uint16).reshape(y.shape)
+
+
 def f16_bits_to_double(bits: int) -> float:
     return _load().orc_f16_bits_to_double(bits)
 

@@ -1,0 +1,167 @@
+"""GPU parity of the fused QKV projection (ftm_qkv_proj) through the C ABI.
+
+Bar: the projection accumulates in fp32 and rounds once to the activation
+type, so |got - ref| <= 1 ulp of the output type at |ref| (half an ulp for
+the rounding, doubled to cover a binade edge) + hidden * 2^-24 * sum_k
+|x_k w_k| (the worst-case growth of an fp32 sum of `hidden` products,
+which are exact in fp32), with ref the float64 oracle.  Every output
+element is checked.  A routing case, one-hot weight rows that copy input
+elements, must be bitwise exact, which pins where every feature lands in
+q, k_new and v_new.  A chained case runs the projection and then the
+attention step, against the oracle's projection, rounded by the oracle,
+and the oracle's attention."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_step_attention_amd import workloads as W
+from tests.helpers import out_to_f64, to_np
+from tests.test_gpu_parity import bits, check
+
+pytestmark = pytest.mark.gpu
+
+FRAC = {"f16": 10, "bf16": 7}
+MIN_EXP = {"f16": -14, "bf16": -126}
+
+
+@pytest.fixture(scope="module")
+def ftm():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from decode_step_attention_amd import ftm as m
+    return m
+
+
+def run(ftm, inp, case, with_bias=True):
+    dt = W.TORCH_DTYPES[case.dtype]
+    B, H, Hkv, D = case.batch, case.n_heads, case.n_kv_heads, case.head_dim
+    g = {k: v.cuda() for k, v in inp.items()}
+    q = torch.empty((B, H, D), dtype=dt, device="cuda")
+    k = torch.empty((B, Hkv, D), dtype=dt, device="cuda")
+    v = torch.empty((B, Hkv, D), dtype=dt, device="cuda")
+    ftm.ftm_qkv_proj(g["x"], g["w"], g["bias"] if with_bias else None, q, k, v)
+    torch.cuda.synchronize()
+    return q, k, v
+
+
+def reference(inp, case, with_bias=True):
+    dt = case.dtype
+    x, w = to_np(inp["x"], dt), to_np(inp["w"], dt)
+    b = to_np(inp["bias"], dt) if with_bias else None
+    ref = oracle.qkv_proj(x, w, b, case.n_heads, case.n_kv_heads, case.head_dim, dt)
+    absdot = np.abs(oracle.cache_to_f64(x, dt)) @ np.abs(oracle.cache_to_f64(w, dt)).T   # [B, N]
+    return ref, absdot
+
+
+def check_proj(case, got, ref, absdot, tag):
+    dt = case.dtype
+    B = case.batch
+    g = np.concatenate([out_to_f64(t).reshape(B, -1) for t in got], axis=1)
+    r = np.concatenate([a.reshape(B, -1) for a in ref], axis=1)
+    e = np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** MIN_EXP[dt])))
+    ulp = 2.0 ** (e - FRAC[dt])
+    bound = ulp + case.hidden * 2.0 ** -24 * absdot
+    err = np.abs(g - r)
+    worst = float((err / bound).max())
+    print(f"[{tag}] max abs err {err.max():.3e}, worst err/bound {worst:.3f}", flush=True)
+    assert np.isfinite(g).all(), f"{tag}: non-finite output"
+    assert worst <= 1.0, f"{tag}: error beyond the bound ({worst:.3f} of it)"
+
+
+SHAPES = [
+    # dtype, B, H, Hkv, D, hidden
+    ("f16", 1, 8, 8, 64, 512),
+    ("bf16", 8, 8, 2, 128, 1024),
+    ("f16", 16, 16, 16, 128, 2048),
+    ("bf16", 17, 8, 8, 64, 768),       # a second batch tile, ragged; three k iterations over four waves
+    ("f16", 33, 4, 4, 128, 256),       # one k iteration: three waves idle
+    ("bf16", 64, 8, 1, 128, 4096),
+    ("f16", 5, 12, 4, 80, 1280),       # head_dim not a power of two
+]
+
+
+@pytest.mark.parametrize("dt,B,H,Hkv,D,hidden", SHAPES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_projection_parity(ftm, dt, B, H, Hkv, D, hidden, with_bias):
+    case = W.ProjCase("t", B, H, Hkv, D, hidden, dt, seed=17 + B + hidden)
+    inp = W.make_proj_inputs(case)
+    got = run(ftm, inp, case, with_bias)
+    ref, absdot = reference(inp, case, with_bias)
+    check_proj(case, got, ref, absdot, f"{dt} B{B} H{H}/{Hkv} D{D} hidden{hidden} bias{with_bias}")
+
+
+@pytest.mark.parametrize("ft", ["1", "2", "4"])
+@pytest.mark.parametrize("dt,B,hidden", [("bf16", 16, 1024), ("f16", 40, 768), ("bf16", 64, 2048)])
+def test_column_tiles(ftm, monkeypatch, ft, dt, B, hidden):
+    """Every number of column tiles per workgroup (forced), with one to four
+    batch tiles."""
+    monkeypatch.setenv("FTM_QKV_COLUMN_TILES", ft)
+    case = W.ProjCase("t", B, 8, 2, 128, hidden, dt, seed=31 + B)
+    inp = W.make_proj_inputs(case)
+    got = run(ftm, inp, case)
+    ref, absdot = reference(inp, case)
+    check_proj(case, got, ref, absdot, f"{dt} B{B} hidden{hidden} column tiles {ft}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_routing_is_exact(ftm, dt):
+    """One-hot weight rows: feature f copies x[:, perm[f]] exactly."""
+    B, H, Hkv, D, hidden = 9, 8, 2, 64, 1024
+    case = W.ProjCase("r", B, H, Hkv, D, hidden, dt, seed=5)
+    inp = W.make_proj_inputs(case)
+    N = case.n_out
+    perm = torch.from_numpy(np.random.default_rng(3).integers(0, hidden, N))
+    w = torch.zeros((N, hidden), dtype=W.TORCH_DTYPES[dt])
+    w[torch.arange(N), perm] = 1.0
+    inp["w"] = w
+    q, k, v = run(ftm, inp, case, with_bias=False)
+    y = torch.cat([q.reshape(B, -1), k.reshape(B, -1), v.reshape(B, -1)], dim=1).cpu()
+    want = inp["x"][:, perm]
+    assert torch.equal(bits(y), bits(want))
+
+
+@pytest.mark.parametrize("name", sorted(W.PROJ_CASES))
+def test_full_size_projection(ftm, name):
+    """The benchmark's projections at full size, every output checked."""
+    case = W.PROJ_CASES[name]
+    inp = W.make_proj_inputs(case)
+    got = run(ftm, inp, case)
+    ref, absdot = reference(inp, case)
+    check_proj(case, got, ref, absdot, f"full {name}")
+
+
+@pytest.mark.parametrize("dt,H,Hkv", [("f16", 8, 8), ("bf16", 8, 2)])
+def test_projection_then_attention(ftm, dt, H, Hkv):
+    """x -> projection -> decode step, against the oracle's projection
+    (float64, rounded to the activation type by the oracle) and the oracle's
+    step.  The appended rows may differ from the oracle's by the rounding of
+    k_new/v_new (fp32 against float64 sums): within one ulp."""
+    B, D = 3, 128
+    hidden = H * D
+    pc = W.ProjCase("c", B, H, Hkv, D, hidden, dt, seed=23)
+    inp = W.make_proj_inputs(pc)
+    ac = W.Case("c", B, H, Hkv, D, dt, ctx=700, max_seq_len=720, value_scale=1 / np.sqrt(D),
+                lens=(1, 700), seed=29)
+    ai = W.make_inputs(ac, "cpu", poison=True)
+    # oracle chain
+    (qr, kr, vr), _ = reference(inp, pc, with_bias=False)
+    qn, kn, vn = (oracle.round_to_act(a, dt) for a in (qr, kr, vr))
+    kc, vc = to_np(ai["k_cache"], dt), to_np(ai["v_cache"], dt)
+    lens = ai["seq_lens"].numpy().astype(np.int32)
+    ref, _ = oracle.decode_mha(qn, kn, vn, to_np(ai["bias"], dt), kc, vc, lens, ai["step"], H, Hkv, D, dt,
+                               n_threads=8)
+    # GPU chain
+    q, k, v = run(ftm, inp, pc, with_bias=False)
+    g = {kk: (t.cuda() if torch.is_tensor(t) else t) for kk, t in ai.items()}
+    out = torch.empty((B, H, D), dtype=W.TORCH_DTYPES[dt], device="cuda")
+    ftm.ftm_decode_mha(q, k, v, g["bias"], g["k_cache"], g["v_cache"], g["seq_lens"], g["step"], out)
+    torch.cuda.synchronize()
+    check(ac, out, ref, f"projection + attention {dt} H{H}/{Hkv}")
+    gk = oracle.cache_to_f64(to_np(g["k_cache"], dt), dt)
+    rk = oracle.cache_to_f64(kc, dt)
+    for b in range(B):
+        p = int(lens[b]) - 1
+        d = np.abs(gk[b, :, p] - rk[b, :, p])
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(rk[b, :, p]), 2.0 ** MIN_EXP[dt]))) - FRAC[dt])
+        assert (d <= ulp).all(), f"appended K row of sequence {b} beyond one ulp"

@@ -165,3 +165,46 @@ def test_binding_rejects_mismatched_paged_tensors():
         ftm.ftm_decode_mha_paged(q, kn, kn, None, kp, kp[:, :1], tbl, None, 8, q)
     with pytest.raises(ValueError):
         ftm.ftm_decode_mha_paged(q, kn, kn, None, kp, kp, tbl[:1], None, 8, q)
+
+
+def call_qkv(**kw):
+    args = [("x", A), ("w", A), ("bias", None), ("q", A), ("k_new", A), ("v_new", A), ("batch", 8),
+            ("hidden", 4096), ("n_heads", 32), ("n_kv_heads", 32), ("head_dim", 128),
+            ("act_dtype", ftm.FTM_F16), ("stream", None)]
+    vals = [kw.get(k, v) for k, v in args]
+    rc = ftm.lib.ftm_qkv_proj(*vals)
+    return rc, ftm.ftm_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), 1, "NULL"),
+    (dict(v_new=None), 1, "NULL"),
+    (dict(batch=0), 1, ">= 1"),
+    (dict(n_heads=31), 1, "multiple"),
+    (dict(act_dtype=ftm.FTM_F32), 2, "fp16 or bf16"),
+    (dict(act_dtype=ftm.FTM_I8), 1, "fp16 or bf16"),
+    (dict(w=A + 4), 1, "aligned"),
+    (dict(bias=A + 2), 1, "aligned"),
+    (dict(batch=65), 2, "batch"),
+    (dict(hidden=4000), 2, "hidden"),
+    (dict(hidden=1 << 17), 2, "hidden"),
+    (dict(head_dim=72), 2, "head_dim"),
+])
+def test_projection_argument_errors_return_before_any_device_call(kw, status, needle):
+    rc, msg = call_qkv(**kw)
+    assert rc == status
+    assert needle in msg
+
+
+def test_binding_rejects_mismatched_projection_tensors():
+    import torch
+    x = torch.zeros(2, 256, dtype=torch.bfloat16)
+    w = torch.zeros((4 + 2 * 2) * 16, 256, dtype=torch.bfloat16)
+    q = torch.zeros(2, 4, 16, dtype=torch.bfloat16)
+    k = torch.zeros(2, 2, 16, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        ftm.ftm_qkv_proj(x.float(), w, None, q, k, k)
+    with pytest.raises(ValueError):
+        ftm.ftm_qkv_proj(x, w[:-16], None, q, k, k)
+    with pytest.raises(TypeError):
+        ftm.ftm_qkv_proj(x, w.half(), None, q, k, k)
