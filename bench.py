@@ -127,6 +127,24 @@ def cpu_baseline(case, inputs, lens, budget_s: float):
                       f"of K/V), fp64 oracle, best of {runs} runs, {total:.1f} s in total"}
 
 
+def device_copy_gbs(dev) -> float:
+    """A plain device copy of known size (1 GiB, above the last-level cache):
+    reference bandwidth, and the calibration dispatch for the HBM counters."""
+    n_copy = 1 << 30
+    src = torch.empty(n_copy, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n_copy * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
 def run_projection(args, case):
     """The fused QKV projection alone, weights rotating over distinct sets:
     bound by the HBM stream of the weights."""
@@ -143,6 +161,7 @@ def run_projection(args, case):
     calls = [ftm.ftm_qkv_proj_prepared(st["x"], st["w"], st["bias"], q, k, v, stream=stream.cuda_stream)
              for st in sets]
     nbytes = W.proj_bytes(case)
+    copy_gbs = device_copy_gbs(dev)
     for i in range(args.warmup):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
@@ -185,6 +204,7 @@ def run_projection(args, case):
                    "launch": "HIP graph replay" if graphs else "one library call"},
         "pct_hbm_peak": round(100 * nbytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBS, 2),
         "bytes_per_step": nbytes, "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+        "device_copy_GBs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
@@ -268,20 +288,7 @@ def main():
     def call(i):
         calls[i % rotate][i & 1]()
 
-    # a plain device copy of known size (1 GiB, above the last-level cache):
-    # reference bandwidth, and the calibration dispatch for the HBM counters
-    n_copy = 1 << 30
-    src = torch.empty(n_copy, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dst.copy_(src)
-    e0.record()
-    for _ in range(5):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * n_copy * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    copy_gbs = device_copy_gbs(dev)
 
     k = 0
     for _ in range(args.warmup):
