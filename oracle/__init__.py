@@ -207,6 +207,73 @@ def qkv_proj(x, w, bias, n_heads, n_kv_heads, head_dim, act_dtype):
     return q, k, v
 
 
+def prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, n_heads, n_kv_heads,
+                head_dim, kv_dtype):
+    """Prefill: the whole prompt of every sequence in one step.  Writes the
+    prompt's K/V rows into the cache in place and returns out[B, S, H, D]
+    float64 (rows past a sequence's prompt are 0).
+
+    The prompt is processed in parallel where decode goes token by token
+    ([lpnh.cn/news/2765398] section 1.1): for sequence b with prompt length
+    S_b, position t of every query head attends to positions [0, t] of its
+    KV head, causally.  Each position is what a decode step at length t + 1
+    computes, with the same readings: the bias added in fp32 before the K/V
+    rows are stored (rounded to the cache type), the stored rows used in the
+    attention, the query with its bias unrounded, scale 1/sqrt(D), the
+    maximum subtracted before exp.
+
+    Layouts: q [B, S, H, D]; k_new, v_new [B, S, Hkv, D]; qkv_bias
+    [(H + 2 Hkv) D] or None; caches [B, Hkv, Lmax, D] with Lmax >= S;
+    seq_lens [B] int32 (1 <= S_b <= S) or None for every S_b = S.  fp16 and
+    bf16 caches (bf16 as uint16 bit patterns)."""
+    import torch
+    if kv_dtype not in ("f16", "bf16"):
+        raise ValueError("prefill takes fp16 or bf16")
+    B, S, H, D = q.shape
+    Hkv = n_kv_heads
+    G = H // Hkv
+    if H != n_heads or D != head_dim or k_new.shape != (B, S, Hkv, D):
+        raise ValueError("shapes do not match n_heads / n_kv_heads / head_dim")
+    lens = np.full(B, S) if seq_lens is None else np.asarray(seq_lens, dtype=np.int64)
+    tdt = torch.float16 if kv_dtype == "f16" else torch.bfloat16
+
+    def f32(a):
+        return torch.from_numpy(cache_to_f64(np.asarray(a), kv_dtype).astype(np.float32))
+
+    bias = None if qkv_bias is None else f32(qkv_bias)
+    out = np.zeros((B, S, H, D), dtype=np.float64)
+    inv = 1.0 / np.sqrt(D)
+    for b in range(B):
+        Sb = int(lens[b])
+        if Sb < 1 or Sb > S:
+            out[b] = np.nan
+            continue
+        for which, src, cache in ((0, k_new, k_cache), (1, v_new, v_cache)):
+            x = f32(src[b, :Sb])                              # [Sb, Hkv, D]
+            if bias is not None:
+                x = x + bias[(H + which * Hkv) * D:(H + (which + 1) * Hkv) * D].reshape(Hkv, D)
+            stored = x.to(tdt)                                # round to nearest even
+            if kv_dtype == "bf16":
+                cache[b, :, :Sb] = stored.view(torch.int16).numpy().view(np.uint16).transpose(1, 0, 2)
+            else:
+                cache[b, :, :Sb] = stored.numpy().transpose(1, 0, 2)
+        K = cache_to_f64(k_cache[b, :, :Sb], kv_dtype)       # [Hkv, Sb, D]
+        V = cache_to_f64(v_cache[b, :, :Sb], kv_dtype)
+        causal = np.tril(np.ones((Sb, Sb), dtype=bool))
+        for h in range(H):
+            j = h // G
+            qh = cache_to_f64(np.asarray(q[b, :Sb, h]), kv_dtype)
+            if bias is not None:
+                qh = qh + bias[h * D:(h + 1) * D].double().numpy()[None, :]
+            s = (qh @ K[j].T) * inv                            # [Sb, Sb]
+            s = np.where(causal, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            p = w / w.sum(axis=1, keepdims=True)
+            out[b, :Sb, h] = p @ V[j]
+    return out
+
+
 def round_to_act(y, act_dtype):
     """float64 values rounded to nearest even in the activation type, as the
     array type the oracle takes (bfloat16 as uint16 bit patterns)."""
