@@ -231,12 +231,93 @@ def run_projection(args, case):
     print(json.dumps(result), flush=True)
 
 
+MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 matrix peak, published
+
+
+def run_prefill(args, case):
+    """Prefill of the whole prompts: compute-bound on the matrix cores."""
+    from decode_step_attention_amd import ftm
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    print(f"# {case.name}: batch {case.batch} x {case.prompt}-token prompts, {case.n_heads}q/{case.n_kv_heads}kv "
+          f"heads x {case.head_dim}, {case.dtype}", file=sys.stderr, flush=True)
+    inp = W.make_prefill_inputs(case, dev, poison=False)
+    out = torch.empty((case.batch, case.prompt, case.n_heads, case.head_dim), dtype=W.TORCH_DTYPES[case.dtype],
+                      device=dev)
+    call = ftm.ftm_prefill_mha_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"], inp["k_cache"],
+                                        inp["v_cache"], inp["seq_lens"], out, stream=stream.cuda_stream)
+    lens = inp["seq_lens"].cpu().tolist()
+    flops = W.prefill_flops(case, lens)
+    copy_gbs = device_copy_gbs(dev)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for _ in range(args.steps):
+        call()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gpu_ms = r0.elapsed_time(r1) / args.steps
+    elapsed = t1 - t0
+    tflops = flops / (gpu_ms * 1e-3) / 1e12
+    result = {
+        "metric": "prefill attention TFLOP/s (causal q.k + p.v, % of the dense fp16/bf16 matrix peak)",
+        "value": round(flops * args.steps / elapsed / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.dtype,
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": f"{case.name}: batch {case.batch} x {case.prompt} tokens, {case.n_heads}q/"
+                               f"{case.n_kv_heads}kv heads x {case.head_dim}",
+                   "batch": case.batch, "prompt": case.prompt, "n_heads": case.n_heads,
+                   "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim},
+        "tokens_per_s": round(sum(lens) * args.steps / elapsed, 1),
+        "gpu_ms_per_step": round(gpu_ms, 5), "flops_per_step": flops, "kernels_per_step": 2,
+        "device_copy_GBs": round(copy_gbs, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_attn_kernel (+ prefill_append_kernel)",
+                     "avg_launch_us": round(gpu_ms * 1e3, 2),
+                     "timing": "events bracketing the timed region / steps (append + attention)"},
+    }
+    if args.cpu_budget > 0:
+        import oracle
+        hc = {k: (v.cpu().view(torch.int16).numpy().view(np.uint16) if case.dtype == "bf16" else v.cpu().numpy())
+              for k, v in inp.items() if k != "seq_lens"}
+        # one sequence, the first head group only: a bounded sample
+        G = case.n_heads // case.n_kv_heads
+        D = case.head_dim
+        qh = np.ascontiguousarray(hc["q"][:1, :, :G])
+        kn = np.ascontiguousarray(hc["k_new"][:1, :, :1])
+        vn = np.ascontiguousarray(hc["v_new"][:1, :, :1])
+        H, Hkv = case.n_heads, case.n_kv_heads
+        bb = hc["bias"]
+        sb = np.concatenate([bb[:G * D], bb[H * D:(H + 1) * D], bb[(H + Hkv) * D:(H + Hkv + 1) * D]])
+        runs, total, best = 0, 0.0, float("inf")
+        while runs < 2 or (total < args.cpu_budget and runs < 20):
+            kc = np.zeros((1, 1, case.max_seq_len, D), dtype=qh.dtype)
+            vc = kc.copy()
+            c0 = time.perf_counter()
+            oracle.prefill_mha(qh, kn, vn, sb, kc, vc, None, G, 1, D, case.dtype)
+            dtm = time.perf_counter() - c0
+            best, total, runs = min(best, dtm), total + dtm, runs + 1
+        sample_flops = W.prefill_flops(case.with_(batch=1, n_heads=G, n_kv_heads=1))
+        result["cpu_baseline"] = {"value": round(sample_flops / best / 1e12, 4), "unit": "TFLOP/s",
+                                  "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                  "sample": f"sequence 0, query heads 0..{G - 1} (one KV head), float64 numpy, "
+                                            f"best of {runs} runs"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="7b", choices=sorted(W.CASES) + sorted(W.PROJ_CASES))
+    ap.add_argument("--config", default="7b",
+                    choices=sorted(W.CASES) + sorted(W.PROJ_CASES) + sorted(W.PREFILL_CASES))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0 skips it)")
     ap.add_argument("--graph", action="store_true",
@@ -251,6 +332,9 @@ def main():
         sys.exit(2)
     if args.config in W.PROJ_CASES:
         run_projection(args, W.PROJ_CASES[args.config])
+        return
+    if args.config in W.PREFILL_CASES:
+        run_prefill(args, W.PREFILL_CASES[args.config])
         return
     from decode_step_attention_amd import ftm
 

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libftm.so")
 SOURCES = [os.path.join(CSRC, "decode_attention.hip"), os.path.join(CSRC, "qkv_proj.hip"),
-           os.path.join(CSRC, "ftm_api.cpp")]
+           os.path.join(CSRC, "prefill.hip"), os.path.join(CSRC, "ftm_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

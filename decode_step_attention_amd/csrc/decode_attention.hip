@@ -22,44 +22,18 @@
 // ([pptc.cn/news/144085] section 3.4) and an INT8 cache converted back at
 // compute time ([pptc.cn/news/144085] section 3.1; [intelliparadigm.com
 // .../2131745] section 2.1).  Scores never leave registers.
-#include "ftm_internal.hpp"
-
 #include <cstdlib>
-#include <type_traits>
+
+#include "gfx950.hpp"
 
 namespace ftm {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kWaves = 4;                 // waves per combine workgroup
 constexpr int kThreads = 64 * kWaves;
-// Buffer descriptor word 3 for raw (untyped) buffer access on the gfx9 family.
-constexpr int kRsrcWord3 = 0x00020000;
 // Cache policy of the K/V stream: non-temporal (every byte is used once).
 constexpr int kStream = 2;
 constexpr float kNegInf = -__builtin_inff();
-
-// ---------------------------------------------------------------------------
-// Number formats
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
-    return __uint_as_float(h << 16);
-}
-// fp32 -> binary16, round to nearest even (the hardware's default mode).
-__device__ __forceinline__ uint32_t float_to_half_bits(float x) {
-    return __builtin_bit_cast(uint16_t, (_Float16)x);
-}
-// fp32 -> bfloat16, round to nearest even on the integer pattern; NaN maps
-// to the canonical quiet NaN with its sign.
-__device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 
 // Cache element type: size and how a 16-byte vector unpacks into fp32.
 template <int KV> struct Elem;
@@ -199,18 +173,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Buffer descriptor over [base, base + bytes).  Both are the same across the
-// wave; readfirstlane states that, so the descriptor sits in scalar
-// registers instead of being rebuilt per lane around every load.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)base;
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0, n, kRsrcWord3);
-}
 
 // Paged cache: position `pos` of (sequence b, KV head j) is row pos mod P of
 // page tbl[pos / P] of a [n_pages, Hkv, P, row] pool (P a power of two; tbl
@@ -662,85 +624,6 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
 // The softmax runs on the S^T tile: lane (g, n) holds head n at positions
 // 4g..4g+3 of each 16-position tile.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-template <int KV> struct Mfma;
-template <> struct Mfma<KV_BF16> {
-    typedef bf16x8 vec8;
-    typedef s16x4 vec4;
-    __device__ static vec8 bits8(const u32x4 w) { return __builtin_bit_cast(vec8, w); }
-    __device__ static vec4 bits4(const u32x2 w) { return __builtin_bit_cast(vec4, w); }
-    __device__ static void split8(const float* x, vec8& hi, vec8& lo) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const __bf16 h = (__bf16)x[i];
-            hi[i] = h;
-            lo[i] = (__bf16)(x[i] - (float)h);
-        }
-    }
-    __device__ static void split4(const float* x, vec4& hi, vec4& lo) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const __bf16 h = (__bf16)x[i];
-            hi[i] = __builtin_bit_cast(short, h);
-            lo[i] = __builtin_bit_cast(short, (__bf16)(x[i] - (float)h));
-        }
-    }
-    __device__ static f32x4 mma32(const vec8 a, const vec8 b, const f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static f32x4 mma16(const vec4 a, const vec4 b, const f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Mfma<KV_F16> {
-    typedef f16x8 vec8;
-    typedef f16x4 vec4;
-    __device__ static vec8 bits8(const u32x4 w) { return __builtin_bit_cast(vec8, w); }
-    __device__ static vec4 bits4(const u32x2 w) { return __builtin_bit_cast(vec4, w); }
-    __device__ static void split8(const float* x, vec8& hi, vec8& lo) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const _Float16 h = (_Float16)x[i];
-            hi[i] = h;
-            lo[i] = (_Float16)(x[i] - (float)h);
-        }
-    }
-    __device__ static void split4(const float* x, vec4& hi, vec4& lo) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const _Float16 h = (_Float16)x[i];
-            hi[i] = h;
-            lo[i] = (_Float16)(x[i] - (float)h);
-        }
-    }
-    __device__ static f32x4 mma32(const vec8 a, const vec8 b, const f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-    __device__ static f32x4 mma16(const vec4 a, const vec4 b, const f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-    }
-};
-
-// Orders this wave's LDS accesses: everything issued before has completed.
-__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order.
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (N > 0) {
-        static_for<N - 1>(f);
-        f(std::integral_constant<int, N - 1>{});
-    }
-}
-
 // Device-coherent accesses for data handed between workgroups on different
 // XCDs (relaxed atomics at agent scope: written through to, and read from,
 // the device coherence point).

@@ -567,6 +567,50 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
     return FTM_OK;
 }
 
+int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                    void* k_cache, void* v_cache, const int32_t* seq_lens, int batch, int max_seq_len,
+                    int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, void* out,
+                    void* stream_ptr) {
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
+        return fail(FTM_ERR_INVALID_ARG, "a required pointer (q, k_new, v_new, k_cache, v_cache, out) is NULL");
+    if (batch < 1 || max_seq_len < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
+        return fail(FTM_ERR_INVALID_ARG, "batch, max_seq_len, n_heads, n_kv_heads and head_dim must be >= 1");
+    if (n_heads % n_kv_heads != 0)
+        return fail(FTM_ERR_INVALID_ARG, "n_heads (" + std::to_string(n_heads) +
+                                             ") is not a multiple of n_kv_heads (" +
+                                             std::to_string(n_kv_heads) + ")");
+    if (prompt_len < 1 || prompt_len > max_seq_len)
+        return fail(FTM_ERR_INVALID_ARG, "prompt_len " + std::to_string(prompt_len) +
+                                             " outside [1, max_seq_len=" + std::to_string(max_seq_len) + "]");
+    if (kv_dtype < FTM_F32 || kv_dtype > FTM_I8)
+        return fail(FTM_ERR_INVALID_ARG, "unknown kv_dtype " + std::to_string(kv_dtype));
+    if (kv_dtype != FTM_F16 && kv_dtype != FTM_BF16)
+        return fail(FTM_ERR_UNSUPPORTED, "prefill takes fp16 or bf16 caches");
+    {
+        const void* vec[] = {q, k_new, v_new, qkv_bias, k_cache, v_cache, out};
+        for (const void* v : vec)
+            if (((uintptr_t)v & 15u) != 0)
+                return fail(FTM_ERR_INVALID_ARG, "q, k_new, v_new, qkv_bias, k_cache, v_cache and out must be 16-byte aligned");
+        if (((uintptr_t)seq_lens & 3u) != 0)
+            return fail(FTM_ERR_INVALID_ARG, "seq_lens must be 4-byte aligned");
+    }
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FTM_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) + " (built: 64, 128)");
+    if (n_heads > 65535 || batch > 65535)
+        return fail(FTM_ERR_UNSUPPORTED, "grid too large: n_heads and batch must be <= 65535");
+    if ((size_t)max_seq_len * head_dim * 2 > 0x7fffffffu)
+        return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
+    if ((long long)batch * prompt_len * n_kv_heads * (head_dim / 8) > 0x7fffffffLL * 256)
+        return fail(FTM_ERR_UNSUPPORTED, "prompt too large for one append launch");
+    ftm::PrefillParams p{q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, batch, prompt_len,
+                         max_seq_len, n_heads, n_kv_heads,
+                         (float)(1.4426950408889634 / std::sqrt((double)head_dim))};
+    hipError_t he = ftm::launch_prefill(p, kv_dtype, head_dim, (hipStream_t)stream_ptr);
+    if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(he));
+    g_last_error.clear();
+    return FTM_OK;
+}
+
 int ftm_graph_begin(void* stream) {
     if (!stream) return fail(FTM_ERR_INVALID_ARG, "the null stream cannot be captured: pass a created stream");
     hipError_t e = hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal);

@@ -67,7 +67,23 @@ struct QkvParams {
     int B, hidden, H, Hkv, D;
 };
 
+// Prefill: the whole prompt of every sequence.
+struct PrefillParams {
+    const void* q;          // [B, S, H, D] act
+    const void* k_new;      // [B, S, Hkv, D] act
+    const void* v_new;      // [B, S, Hkv, D] act
+    const void* bias;       // [(H + 2 Hkv) D] act or null
+    void* k_cache;          // [B, Hkv, Lmax, D] kv (= act)
+    void* v_cache;
+    const int32_t* seq_lens;// [B] prompt lengths or null (all S)
+    void* out;              // [B, S, H, D] act
+    int B, S, Lmax, H, Hkv;
+    float qscale;           // log2(e) / sqrt(D)
+};
+
 hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, int nw, hipStream_t s);
+// kv: KV_F16 or KV_BF16; head_dim 64 or 128.  Two launches: append, then attention.
+hipError_t launch_prefill(const PrefillParams& p, int kv, int head_dim, hipStream_t s);
 // act: KV_F16 or KV_BF16; B <= 64, hidden a multiple of 256, (H + 2 Hkv) D a multiple of 16.
 hipError_t launch_qkv_proj(const QkvParams& p, int act, int n_cu, hipStream_t s);
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);

@@ -20,57 +20,29 @@
 // flight while the matrix cores work.  The eight partial sums meet in LDS in
 // a fixed order, the bias is added in fp32, and the result is rounded to
 // nearest even.
-#include "ftm_internal.hpp"
-
 #include <cstdlib>
+
+#include "gfx950.hpp"
 
 namespace ftm {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kWaves = 8;                 // the k range is split across the waves of a workgroup
-constexpr int kRsrcWord3 = 0x00020000;    // raw buffer access, gfx9 family
 constexpr int kStream = 2;                // non-temporal: every weight is read once
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)base;
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0, n, kRsrcWord3);
-}
-
-template <int ACT> struct QMma;
-template <> struct QMma<KV_BF16> {
+// The activation type's matrix-core product on 16-byte operands, and its
+// scalar load and round-to-nearest-even store.
+template <int ACT> struct QMma {
+    using MF = Mfma<ACT>;
     __device__ static f32x4 mma(const u32x4 a, const u32x4 b, const f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+        return MF::mma32(MF::bits8(a), MF::bits8(b), c);
     }
     __device__ static float ld(const void* p, size_t i) {
-        return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
-    }
-    // fp32 -> bfloat16, round to nearest even; NaN to the quiet NaN with its sign
-    __device__ static void st(void* p, size_t i, float v) {
-        const uint32_t u = __float_as_uint(v);
-        const uint32_t r = (u & 0x7fffffffu) > 0x7f800000u ? (((u >> 16) & 0x8000u) | 0x7fc0u)
-                                                           : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-        ((uint16_t*)p)[i] = (uint16_t)r;
-    }
-};
-template <> struct QMma<KV_F16> {
-    __device__ static f32x4 mma(const u32x4 a, const u32x4 b, const f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-    __device__ static float ld(const void* p, size_t i) {
-        return (float)__builtin_bit_cast(_Float16, ((const uint16_t*)p)[i]);
+        const uint32_t h = ((const uint16_t*)p)[i];
+        return ACT == KV_F16 ? half_bits_to_float(h) : bf16_bits_to_float(h);
     }
     __device__ static void st(void* p, size_t i, float v) {
-        ((uint16_t*)p)[i] = __builtin_bit_cast(uint16_t, (_Float16)v);   // round to nearest even
+        ((uint16_t*)p)[i] = (uint16_t)(ACT == KV_F16 ? float_to_half_bits(v) : float_to_bf16_bits(v));
     }
 };
 

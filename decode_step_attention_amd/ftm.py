@@ -24,7 +24,8 @@ _ACT = {FTM_F32: torch.float32, FTM_F16: torch.float16, FTM_BF16: torch.bfloat16
         FTM_I8: torch.float16}
 
 # Every symbol include/ftm.h declares.
-EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_qkv_proj", "ftm_kv_cache_bytes", "ftm_last_error",
+EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_qkv_proj", "ftm_prefill_mha", "ftm_kv_cache_bytes",
+           "ftm_last_error",
            "ftm_version", "ftm_set_split_chunk", "ftm_set_workgroup_waves", "ftm_release_workspaces",
            "ftm_graph_begin", "ftm_graph_end", "ftm_graph_launch", "ftm_graph_destroy",
            "ftm_timing_enable", "ftm_timing_disable", "ftm_timing_read")
@@ -44,6 +45,8 @@ def _load() -> ctypes.CDLL:
     lib.ftm_decode_mha_paged.restype = i32
     lib.ftm_qkv_proj.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.ftm_qkv_proj.restype = i32
+    lib.ftm_prefill_mha.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.ftm_prefill_mha.restype = i32
     lib.ftm_graph_begin.argtypes = [vp]
     lib.ftm_graph_begin.restype = i32
     lib.ftm_graph_end.argtypes = [vp, ctypes.POINTER(vp)]
@@ -290,6 +293,41 @@ def ftm_qkv_proj_prepared(x, w, bias, q, k_new, v_new, stream=None) -> Callable[
     """ftm_qkv_proj with the arguments marshalled once."""
     args = _marshal_qkv(x, w, bias, q, k_new, v_new, stream)
     return _prepared(lib.ftm_qkv_proj, args, (x, w, bias, q, k_new, v_new))
+
+
+def _marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream):
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, S, H, D] and the caches [B, Hkv, Lmax, D]")
+    B, S, H, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    kv = _TORCH_TO_KV.get(k_cache.dtype)
+    if kv is None:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    dt = k_cache.dtype
+    tensors = {"q": (q, dt, (B, S, H, D)), "k_new": (k_new, dt, (B, S, Hkv, D)),
+               "v_new": (v_new, dt, (B, S, Hkv, D)), "k_cache": (k_cache, dt, (B, Hkv, Lmax, D)),
+               "v_cache": (v_cache, dt, (B, Hkv, Lmax, D)), "out": (out, dt, (B, S, H, D))}
+    if qkv_bias is not None:
+        tensors["qkv_bias"] = (qkv_bias, dt, ((H + 2 * Hkv) * D,))
+    if seq_lens is not None:
+        tensors["seq_lens"] = (seq_lens, torch.int32, (B,))
+    _check_tensors(tensors, k_cache.device)
+    return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_cache), _ptr(v_cache),
+            _ptr(seq_lens), B, Lmax, S, H, Hkv, D, kv, _ptr(out), _stream_ptr(stream, k_cache.device))
+
+
+def ftm_prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream=None) -> None:
+    """Prefill (see include/ftm.h): q/out [B, S, H, D], k_new/v_new
+    [B, S, Hkv, D], caches [B, Hkv, Lmax, D], seq_lens int32 [B] or None."""
+    _check(lib.ftm_prefill_mha(*_marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens,
+                                                 out, stream)))
+
+
+def ftm_prefill_mha_prepared(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out,
+                             stream=None) -> Callable[[], None]:
+    """ftm_prefill_mha with the arguments marshalled once."""
+    args = _marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream)
+    return _prepared(lib.ftm_prefill_mha, args, (q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out))
 
 
 def ftm_graph_begin(stream: int) -> None:

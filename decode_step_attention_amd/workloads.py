@@ -305,3 +305,61 @@ def proj_bytes(case: ProjCase) -> int:
     """Bytes one projection must move: the weights, x and the outputs."""
     e = ELEM_BYTES[case.dtype]
     return (case.n_out * case.hidden + case.batch * case.hidden + case.batch * case.n_out) * e
+
+
+@dataclass(frozen=True)
+class PrefillCase:
+    """Prefill of a batch of prompts: q [B, S, H, D], k_new/v_new [B, S, Hkv, D],
+    all values N(0, 1) / sqrt(D) like the decode workloads; ``lens`` None for
+    every prompt at S, or (lo, hi) drawn per sequence."""
+    name: str
+    batch: int
+    prompt: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str
+    max_seq_len: int
+    lens: Optional[tuple] = None
+    seed: int = 3000
+
+    def with_(self, **kw) -> "PrefillCase":
+        return replace(self, **kw)
+
+
+# Prefill of 2048-token prompts for the 7B-shaped layer and the grouped-query layer.
+PREFILL_CASES: Dict[str, PrefillCase] = {
+    "prefill_7b": PrefillCase("prefill_7b", 4, 2048, 32, 32, 128, "f16", 2048, seed=3001),
+    "prefill_gqa": PrefillCase("prefill_gqa", 4, 2048, 64, 8, 128, "bf16", 2048, seed=3003),
+}
+
+
+def make_prefill_inputs(case: PrefillCase, device="cpu", poison: bool = True) -> Dict[str, torch.Tensor]:
+    """Inputs of one prefill step; caches are NaN (poison) or zero before it."""
+    dt = TORCH_DTYPES[case.dtype]
+    B, S, H, Hkv, D = case.batch, case.prompt, case.n_heads, case.n_kv_heads, case.head_dim
+
+    def draw(tag, shape):
+        g = torch.Generator(device=device)
+        g.manual_seed((case.seed * 1_000_003 + tag * 10_007) % (2 ** 62))
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) / math.sqrt(D)).to(dt)
+
+    t = {"q": draw(1, (B, S, H, D)), "k_new": draw(2, (B, S, Hkv, D)), "v_new": draw(3, (B, S, Hkv, D)),
+         "bias": draw(4, ((H + 2 * Hkv) * D,))}
+    fill = float("nan") if poison else 0.0
+    t["k_cache"] = torch.full((B, Hkv, case.max_seq_len, D), fill, dtype=dt, device=device)
+    t["v_cache"] = torch.full_like(t["k_cache"], fill)
+    if case.lens is None:
+        L = torch.full((B,), S, dtype=torch.int32)
+    else:
+        g = torch.Generator().manual_seed(case.seed + 77)
+        L = torch.randint(case.lens[0], case.lens[1] + 1, (B,), generator=g, dtype=torch.int32)
+    t["seq_lens"] = L.to(device)
+    return t
+
+
+def prefill_flops(case: PrefillCase, lens: Optional[List[int]] = None) -> int:
+    """Multiply-adds x 2 of the causal attention: q.k and p.v over positions
+    [0, t] for every prompt position t and query head."""
+    L = [case.prompt] * case.batch if lens is None else list(lens)
+    return sum(4 * (l * (l + 1) // 2) * case.n_heads * case.head_dim for l in L)

@@ -187,6 +187,34 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
                  void* v_new, int batch, int hidden, int n_heads, int n_kv_heads, int head_dim,
                  int act_dtype, void* stream);
 
+/*
+ * ftm_prefill_mha -- prefill: the whole prompt of every sequence in one step.
+ *
+ * The prompt is processed in parallel where decode goes token by token
+ * ([lpnh.cn/news/2765398] section 1.1): the prompt's K/V rows (bias added
+ * in fp32, rounded to nearest even) are written to cache positions
+ * [0, S_b), and every prompt position t of every query head attends
+ * causally to positions [0, t] of its KV head, reading the stored rows.
+ * Position t gets what ftm_decode_mha computes at length t + 1, with the
+ * same readings (scale 1/sqrt(D), maximum subtracted, fp32 accumulation).
+ *
+ * Shapes (row-major, contiguous; S = prompt_len):
+ *   q         [batch, S, n_heads, D]      read
+ *   k_new, v_new [batch, S, n_kv_heads, D]  read
+ *   qkv_bias  [(n_heads + 2 n_kv_heads) D] or NULL
+ *   k_cache, v_cache [batch, n_kv_heads, max_seq_len, D]  rows [0, S_b) written
+ *   seq_lens  [batch] int32 prompt lengths S_b in [1, S], or NULL (all S)
+ *   out       [batch, S, n_heads, D]      rows t < S_b written, the rest untouched
+ * kv_dtype FTM_F16 or FTM_BF16 (activations of the same type); head_dim 64
+ * or 128; S <= max_seq_len.  A sequence whose length lies outside [1, S] is
+ * not appended and gets NaN rows.  Two kernels are enqueued (append, then
+ * attention).  Errors as for ftm_decode_mha.
+ */
+int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                    void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
+                    int max_seq_len, int prompt_len, int n_heads, int n_kv_heads, int head_dim,
+                    int kv_dtype, void* out, void* stream);
+
 /* ---- HIP graphs ----------------------------------------------------------
  * A decode step of a model is one call per layer on fixed buffers; its
  * kernel launches can be recorded once and replayed as one graph launch, so

@@ -1,0 +1,131 @@
+"""GPU parity of prefill (ftm_prefill_mha) through the C ABI, against the
+prefill oracle on the same seeded inputs.
+
+Bar: the caches must equal the oracle's bytewise over the whole buffers (the
+prompt rows appended bit-exactly, everything else, NaN poison included,
+untouched); every output row t < S_b must meet the decode bar (max-abs 2e-3
+and row-normwise relative 1e-2, or one ulp of the output type at the
+reference where that is larger)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_step_attention_amd import workloads as W
+from tests.helpers import out_to_f64, to_np
+from tests.test_gpu_parity import check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ftm():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from decode_step_attention_amd import ftm as m
+    return m
+
+
+def gpu_prefill(ftm, inp, case):
+    g = {k: v.cuda() for k, v in inp.items()}
+    out = torch.zeros((case.batch, case.prompt, case.n_heads, case.head_dim), dtype=W.TORCH_DTYPES[case.dtype],
+                      device="cuda")
+    ftm.ftm_prefill_mha(g["q"], g["k_new"], g["v_new"], g["bias"], g["k_cache"], g["v_cache"], g["seq_lens"], out)
+    torch.cuda.synchronize()
+    return g, out
+
+
+def compare(ftm, case, tag, lens_override=None):
+    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+    if lens_override is not None:
+        inp["seq_lens"] = torch.tensor(lens_override, dtype=torch.int32)
+    dt = case.dtype
+    npi = {k: to_np(v, dt) for k, v in inp.items() if k != "seq_lens"}
+    lens = inp["seq_lens"].numpy().astype(np.int32)
+    print(f"[{tag}] oracle", flush=True)
+    ref = oracle.prefill_mha(npi["q"], npi["k_new"], npi["v_new"], npi["bias"], npi["k_cache"], npi["v_cache"],
+                             lens, case.n_heads, case.n_kv_heads, case.head_dim, dt)
+    print(f"[{tag}] gpu", flush=True)
+    g, out = gpu_prefill(ftm, inp, case)
+    assert to_np(g["k_cache"], dt).tobytes() == npi["k_cache"].tobytes(), f"{tag}: k_cache"
+    assert to_np(g["v_cache"], dt).tobytes() == npi["v_cache"].tobytes(), f"{tag}: v_cache"
+    got = out_to_f64(out)
+    ac = W.Case("p", case.batch, case.n_heads, case.n_kv_heads, case.head_dim, dt, ctx=case.prompt,
+                max_seq_len=case.max_seq_len, value_scale=1.0)
+    for b in range(case.batch):
+        Sb = int(lens[b])
+        if Sb < 1 or Sb > case.prompt:
+            assert np.isnan(got[b]).all(), f"{tag}: invalid length {Sb} must give NaN rows"
+            continue
+        check(ac, got[b, :Sb], ref[b, :Sb], f"{tag} b{b} S{Sb}")
+    return got, ref
+
+
+SHAPES = [
+    # dtype, B, S, H, Hkv, D, Lmax, lens
+    ("f16", 2, 200, 4, 4, 128, 256, (1, 200)),
+    ("bf16", 3, 150, 8, 2, 64, 160, (20, 150)),
+    ("bf16", 1, 64, 2, 1, 128, 64, None),
+    ("f16", 2, 1, 4, 2, 64, 8, None),
+    ("f16", 1, 700, 2, 2, 128, 704, None),
+    ("bf16", 2, 333, 12, 4, 128, 400, (300, 333)),
+]
+
+
+@pytest.mark.parametrize("dt,B,S,H,Hkv,D,Lmax,lens", SHAPES)
+def test_prefill_parity(ftm, dt, B, S, H, Hkv, D, Lmax, lens):
+    case = W.PrefillCase("t", B, S, H, Hkv, D, dt, Lmax, lens=lens, seed=41 + S + H)
+    compare(ftm, case, f"prefill {dt} B{B} S{S} H{H}/{Hkv} D{D}")
+
+
+def test_prefill_invalid_lengths(ftm):
+    case = W.PrefillCase("t", 3, 100, 4, 2, 128, "f16", 128, seed=7)
+    compare(ftm, case, "prefill invalid lengths", lens_override=[100, 0, 101])
+
+
+def test_prefill_last_position_matches_a_decode_step(ftm):
+    """The last prompt position of a prefill and a decode step at that
+    length over the cache the prefill wrote agree within the decode bar."""
+    case = W.PrefillCase("t", 2, 300, 8, 4, 128, "bf16", 320, seed=9)
+    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+    g, out = gpu_prefill(ftm, inp, case)
+    S = case.prompt
+    kc, vc = g["k_cache"].clone(), g["v_cache"].clone()
+    dec_out = torch.empty((case.batch, case.n_heads, case.head_dim), dtype=out.dtype, device="cuda")
+    ftm.ftm_decode_mha(g["q"][:, S - 1].contiguous(), g["k_new"][:, S - 1].contiguous(),
+                       g["v_new"][:, S - 1].contiguous(), g["bias"], kc, vc, None, S, dec_out)
+    torch.cuda.synchronize()
+    d = (dec_out.float() - out[:, S - 1].float()).abs().max().item()
+    assert d <= 2e-3, d
+    assert torch.equal(kc.view(torch.int16), g["k_cache"].view(torch.int16))
+
+
+@pytest.mark.parametrize("name", sorted(W.PREFILL_CASES))
+def test_full_size_prefill_sampled_heads(ftm, name):
+    """The benchmark's prefill at full size; the appended caches are checked
+    whole against a float32/torch recomputation of the append rule, and two
+    (sequence, head) pairs are recomputed by the oracle."""
+    case = W.PREFILL_CASES[name]
+    inp = W.make_prefill_inputs(case, "cuda", poison=False)
+    print(f"[full {name}] gpu", flush=True)
+    g, out = gpu_prefill(ftm, {k: v for k, v in inp.items()}, case)
+    dt = case.dtype
+    G = case.n_heads // case.n_kv_heads
+    for b, h in ((0, 0), (case.batch - 1, case.n_heads - 1)):
+        j = h // G
+        H, Hkv, D = case.n_heads, case.n_kv_heads, case.head_dim
+        bias = inp["bias"].cpu()
+        sub_bias = torch.cat([bias[h * D:(h + 1) * D], bias[(H + j) * D:(H + j + 1) * D],
+                              bias[(H + Hkv + j) * D:(H + Hkv + j + 1) * D]])
+        q = to_np(inp["q"][b:b + 1, :, h:h + 1], dt)
+        kn = to_np(inp["k_new"][b:b + 1, :, j:j + 1], dt)
+        vn = to_np(inp["v_new"][b:b + 1, :, j:j + 1], dt)
+        zero = np.zeros((1, 1, case.max_seq_len, D), dtype=q.dtype)
+        kc, vc = zero.copy(), zero.copy()
+        print(f"[full {name}] oracle b{b} h{h}", flush=True)
+        ref = oracle.prefill_mha(q, kn, vn, to_np(sub_bias, dt), kc, vc, None, 1, 1, D, dt)
+        assert to_np(g["k_cache"][b:b + 1, j:j + 1], dt).tobytes() == kc.tobytes(), "appended K rows"
+        assert to_np(g["v_cache"][b:b + 1, j:j + 1], dt).tobytes() == vc.tobytes(), "appended V rows"
+        ac = W.Case("p", 1, 1, 1, D, dt, ctx=case.prompt, max_seq_len=case.max_seq_len, value_scale=1.0)
+        check(ac, out_to_f64(out[b:b + 1, :, h:h + 1]).reshape(case.prompt, 1, D),
+              ref.reshape(case.prompt, 1, D), f"full {name} b{b} h{h}")
