@@ -8,13 +8,15 @@
 //   rounded to nearest even into the cache (one 16-byte slice per thread).
 // prefill_attn_kernel: one workgroup of 4 waves owns 64 query positions of
 //   one query head; wave w owns 16 of them.  The workgroup streams the key
-//   positions [0, last query] in tiles of 64 through LDS; each wave computes
-//   S^T = K Q^T for 16 keys x its 16 queries and O += P V on the matrix cores
+//   positions [0, last query] in tiles of 64 through LDS; each wave computes,
+//   32 keys at a time (four independent accumulation chains), S^T = K Q^T
+//   for 16 keys x its 16 queries and O += P V on the matrix cores
 //   (v_mfma_f32_16x16x32 and 16x16x16), with the online softmax in between
 //   and the causal mask on the diagonal tiles.  S^T leaves each lane with
 //   four consecutive keys of one query, which is the A-operand layout of P;
 //   V is read down its columns with the transposing LDS read.  The query
-//   (bias added, log2(e)/sqrt(D) folded in) and the weights enter as hi/lo
+//   (bias added, log2(e)/sqrt(D) folded in, kept in registers) and the
+//   weights enter as hi/lo
 //   halves, so about 16 (bf16) or 22 (fp16) bits of each reach the fp32
 //   accumulators, as in the decode pass.  Workgroups with the most keys
 //   are launched first.
@@ -79,9 +81,13 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(const PrefillParams p
     constexpr int LPR = D / 8;              // tile loads: lanes per row (16 bytes each)
     constexpr int RPI = 256 / LPR;          // tile loads: rows per workgroup-wide load
     constexpr int NLD = kPK / RPI;          // tile loads per thread per tile, each of K and V
-    __shared__ __attribute__((aligned(16))) unsigned char ktile[kPK * KPITCH];
-    __shared__ __attribute__((aligned(16))) unsigned char vtile[kPK * VPITCH];
-    __shared__ __attribute__((aligned(16))) unsigned char qbuf[4][2 * 16 * KPITCH];
+    // K and V tiles; before the first tile the same memory stages the query
+    // operand, which the waves then keep in registers
+    constexpr int QBYTES = 2 * 16 * KPITCH;
+    static_assert(4 * QBYTES <= kPK * (KPITCH + VPITCH), "query staging fits in the tiles");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kPK * (KPITCH + VPITCH)];
+    unsigned char* ktile = smem;
+    unsigned char* vtile = smem + kPK * KPITCH;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -111,7 +117,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(const PrefillParams p
     // query operand of S^T for this wave's 16 queries: hi and lo halves of
     // (q + b_q) * log2(e) / sqrt(D); queries past the prompt are zero
     {
-        unsigned char* qb = qbuf[wave];
+        unsigned char* qb = smem + wave * QBYTES;
 #pragma unroll
         for (int r = 0; r < 16 / (64 / LPR); ++r) {
             const int row = r * (64 / LPR) + lane / LPR;
@@ -158,10 +164,21 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(const PrefillParams p
     f32x4 acc[DT];                          // O[query 4g+i][16 tn + n]
 #pragma unroll
     for (int tn = 0; tn < DT; ++tn) acc[tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const unsigned char* qb = qbuf[wave];
+    // the query operand stays in registers: B operand of step kk, hi and lo
+    vec8 qh[KK], ql[KK];
+    {
+        const unsigned char* qb = smem + wave * QBYTES;
+        lds_wave_fence();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int piece = (kk * 4 + g) * 16;
+            qh[kk] = MF::bits8(*(const u32x4*)(qb + n * KPITCH + piece));
+            ql[kk] = MF::bits8(*(const u32x4*)(qb + 16 * KPITCH + n * KPITCH + piece));
+        }
+    }
 
     for (int k0 = 0; k0 < kend; k0 += kPK) {
-        __syncthreads();                    // the previous tile is consumed (and qbuf written)
+        __syncthreads();                    // the previous tile is consumed
 #pragma unroll
         for (int u = 0; u < NLD; ++u) {
             *(u32x4*)(ktile + (u * RPI + lr) * KPITCH + lc * 16) = kr[u];
@@ -170,26 +187,37 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(const PrefillParams p
         __syncthreads();
         if (k0 + kPK < kend) issue(k0 + kPK);
         __builtin_amdgcn_sched_barrier(0);
+        // two 16-key sub-tiles per step: four independent accumulation chains
 #pragma unroll
-        for (int st = 0; st < kPK / 16; ++st) {
-            const int kb = k0 + 16 * st;    // first key of the sub-tile
+        for (int sp = 0; sp < kPK / 32; ++sp) {
+            const int kb = k0 + 32 * sp;    // first key of the pair
             if (kb > tq + 15) break;        // every key after every query of this wave
-            // S^T: row = key kb + 4g + i, column = query tq + n
-            f32x4 s4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            // S^T: row = key kb + 16 h2 + 4g + i, column = query tq + n
+            f32x4 sh[2], sl[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) sh[h2] = sl[h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const int piece = (kk * 4 + g) * 16;
-                const vec8 ka = MF::bits8(*(const u32x4*)(ktile + (16 * st + n) * KPITCH + piece));
-                const vec8 qh = MF::bits8(*(const u32x4*)(qb + n * KPITCH + piece));
-                const vec8 ql = MF::bits8(*(const u32x4*)(qb + 16 * KPITCH + n * KPITCH + piece));
-                s4 = MF::mma32(ka, qh, s4);
-                s4 = MF::mma32(ka, ql, s4);
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const vec8 ka = MF::bits8(*(const u32x4*)(ktile + (32 * sp + 16 * h2 + n) * KPITCH + piece));
+                    sh[h2] = MF::mma32(ka, qh[kk], sh[h2]);
+                    sl[h2] = MF::mma32(ka, ql[kk], sl[h2]);
+                }
             }
             // causal mask (and keys past the prompt, which lie after every valid query)
-            float s[4];
+            float s[2][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] = kb + 4 * g + i <= tq + n ? s4[i] : kNegInfP;
-            float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s[h2][i] = kb + 16 * h2 + 4 * g + i <= tq + n ? sh[h2][i] + sl[h2][i] : kNegInfP;
+            float mt = kNegInfP;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[h2][i]);
             mt = fmaxf(mt, __shfl_xor(mt, 16));
             mt = fmaxf(mt, __shfl_xor(mt, 32));
             const float mn = fmaxf(m, mt);
@@ -198,29 +226,34 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(const PrefillParams p
             m = mn;
             float ls = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[i] = fast_exp2(s[i] - ms);
-                ls += s[i];
-            }
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s[h2][i] = fast_exp2(s[h2][i] - ms);
+                    ls += s[h2][i];
+                }
             l = l * alpha + ls;
-            vec4 ph, pl;
-            MF::split4(s, ph, pl);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float ai = __shfl(alpha, 4 * g + i);
 #pragma unroll
                 for (int tn = 0; tn < DT; ++tn) acc[tn][i] *= ai;
             }
-            // B operand V[key 4g+i][16 tn + n]: lane n of group g names row
-            // 4g + n/4 of the sub-tile, columns 4(n%4)..+3
-            const unsigned char* vrow = vtile + (16 * st + 4 * g + (n >> 2)) * VPITCH + (n & 3) * 8;
 #pragma unroll
-            for (int tn = 0; tn < DT; ++tn) {
-                const s16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(vrow + tn * 32));
-                const vec4 vb = __builtin_bit_cast(vec4, tv);
-                acc[tn] = MF::mma16(ph, vb, acc[tn]);
-                acc[tn] = MF::mma16(pl, vb, acc[tn]);
+            for (int h2 = 0; h2 < 2; ++h2) {
+                vec4 ph, pl;
+                MF::split4(s[h2], ph, pl);
+                // B operand V[key 4g+i][16 tn + n]: lane n of group g names row
+                // 4g + n/4 of the sub-tile, columns 4(n%4)..+3
+                const unsigned char* vrow = vtile + (32 * sp + 16 * h2 + 4 * g + (n >> 2)) * VPITCH + (n & 3) * 8;
+#pragma unroll
+                for (int tn = 0; tn < DT; ++tn) {
+                    const s16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(vrow + tn * 32));
+                    const vec4 vb = __builtin_bit_cast(vec4, tv);
+                    acc[tn] = MF::mma16(ph, vb, acc[tn]);
+                    acc[tn] = MF::mma16(pl, vb, acc[tn]);
+                }
             }
         }
     }
