@@ -50,6 +50,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0, n, kRsrcWord3);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes bytes lds + 16 i .. +15 (lds is the same for the whole wave).
+// Offsets past the buffer's end read zero.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, int offset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, offset, 0, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Eight fp16 or bf16 values in a 16-byte vector, as fp32.
@@ -132,6 +139,27 @@ template <> struct Mfma<KV_F16> {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
     }
 };
+
+// Reduction over the four lanes l % 16 + 16 r (r = 0..3) that share a
+// column of a 16x16 matrix-core result.  v_permlane16_swap exchanges rows
+// 0<->1 and 2<->3 of two copies of x, v_permlane32_swap the two halves of
+// the wave; each step leaves the lane with its own value and its partner's,
+// so every lane of a column ends with the same result.
+template <typename Op>
+__device__ __forceinline__ float column_reduce(float x, Op op) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(x);
+    const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float column_max(float x) {
+    return column_reduce(x, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float column_sum(float x) {
+    return column_reduce(x, [](float a, float b) { return a + b; });
+}
 
 // Orders this wave's LDS accesses: everything issued before has completed.
 __device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

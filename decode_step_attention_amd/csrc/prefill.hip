@@ -27,9 +27,11 @@
 namespace ftm {
 namespace {
 
-constexpr int kPQ = 64;                   // query positions per workgroup (16 per wave)
+constexpr int kQB = 2;                    // 16-query blocks per wave
+constexpr int kPQ = 4 * 16 * kQB;         // query positions per workgroup
 constexpr int kPK = 64;                   // key positions per LDS tile
 constexpr float kNegInfP = -__builtin_inff();
+constexpr float kLazy = 8.0f;             // log2 headroom of the softmax reference
 
 template <int KV, int D>
 __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams p) {
@@ -69,35 +71,49 @@ __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams
 }
 
 template <int KV, int D>
-__global__ void __launch_bounds__(256) prefill_attn_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_attn_kernel(const PrefillParams p) {
     using MF = Mfma<KV>;
     typedef typename MF::vec8 vec8;
-    typedef typename MF::vec4 vec4;
-    constexpr int ROW = D * 2;
-    constexpr int KPITCH = ROW + 16;        // 16-byte reads of 16 rows hit distinct banks
-    constexpr int VPITCH = ROW + 32;        // transposing reads of 4 rows x 32 bytes hit distinct banks
+    constexpr int ROW = D * 2;              // bytes per cache row
+    constexpr int NCH = ROW / 16;           // 16-byte chunks per row
+    constexpr int TILE = kPK * ROW;         // bytes per K (or V) tile
+    constexpr int NI = TILE / 1024 / 4;     // tile loads per wave, each of K and V (1 KiB each)
     constexpr int KK = D / 32;              // S^T: MFMA steps over the head dim
-    constexpr int DT = D / 16;              // O: 16-column tiles
-    constexpr int LPR = D / 8;              // tile loads: lanes per row (16 bytes each)
-    constexpr int RPI = 256 / LPR;          // tile loads: rows per workgroup-wide load
-    constexpr int NLD = kPK / RPI;          // tile loads per thread per tile, each of K and V
-    // K and V tiles; before the first tile the same memory stages the query
-    // operand, which the waves then keep in registers
-    constexpr int QBYTES = 2 * 16 * KPITCH;
-    static_assert(4 * QBYTES <= kPK * (KPITCH + VPITCH), "query staging fits in the tiles");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kPK * (KPITCH + VPITCH)];
-    unsigned char* ktile = smem;
-    unsigned char* vtile = smem + kPK * KPITCH;
+    constexpr int DT = D / 16;              // O^T: 16-row tiles
+    static_assert(NI >= 1 && TILE % 4096 == 0, "tile loads cover the tile");
+    // Tiles are stored unpadded, filled by loads straight from memory into
+    // LDS (lane i of a load writes bytes 16i..16i+15 of its 1 KiB), two
+    // buffers deep.  Chunk c of row r sits in slot c ^ kswz(r) (K) or
+    // c ^ vswz(r) (V), so the 16-byte reads of 16 rows (K) and the
+    // transposing reads of 4 rows x 32 bytes per 16 lanes (V) hit distinct
+    // banks.
+    // (four separate arrays, each named at compile time wherever it is
+    // used, so that the compiler can tell the buffer being filled from the
+    // one being read and need not wait for the fill before the reads)
+    __shared__ __attribute__((aligned(1024))) unsigned char ktile0[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char vtile0[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char ktile1[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char vtile1[TILE];
+    auto kswz = [](int r) { return (r * NCH / 16) & (NCH - 1); };
+    auto vswz = [](int r) { return 2 * ((r * NCH / 16) & (NCH / 2 - 1)); };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;                // MFMA layout: k group / key quad
     const int n = lane & 15;                // MFMA layout: key row (A) / query column (B, C)
-    const int b = blockIdx.z;
-    const int h = blockIdx.y;
-    const int j = h / (p.H / p.Hkv);
-    const int qblk = gridDim.x - 1 - blockIdx.x;   // the blocks with the most keys first
+    // blockIdx.x = r + B Hkv gi with r = b Hkv + j: the G query heads of one
+    // KV head sit B Hkv apart, which keeps them on one L2 when B Hkv is a
+    // multiple of the eight dispatch slots; blockIdx.y counts query blocks
+    // from the last (the most keys) down, so the longest blocks go first
+    const int G = p.H / p.Hkv;
+    const int R = p.B * p.Hkv;
+    const int r = blockIdx.x % R;
+    const int b = r / p.Hkv;
+    const int j = r - b * p.Hkv;
+    const int h = j * G + blockIdx.x / R;
+    const int qblk = gridDim.y - 1 - blockIdx.y;
     const int Sb = __builtin_amdgcn_readfirstlane(p.seq_lens ? p.seq_lens[b] : p.S);
     const int t0 = qblk * kPQ;
     if (Sb < 1 || Sb > p.S) {               // invalid length: NaN rows
@@ -112,166 +128,212 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(const PrefillParams p
     }
     if (t0 >= Sb) return;                   // past the prompt: nothing to do
     const int kend = min(t0 + kPQ, Sb);     // keys [0, kend) are needed
-    const int tq = t0 + wave * 16;          // this wave's first query
+    const int tq = t0 + wave * 16 * kQB;    // this wave's first query
 
-    // query operand of S^T for this wave's 16 queries: hi and lo halves of
-    // (q + b_q) * log2(e) / sqrt(D); queries past the prompt are zero
-    {
-        unsigned char* qb = smem + wave * QBYTES;
-#pragma unroll
-        for (int r = 0; r < 16 / (64 / LPR); ++r) {
-            const int row = r * (64 / LPR) + lane / LPR;
-            const int pc = lane % LPR;
-            const int t = tq + row;
-            float x[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-            if (t < Sb) {
-                const u32x4 raw = *(const u32x4*)((const uint16_t*)p.q + (((size_t)b * p.S + t) * p.H + h) * D + pc * 8);
-                Elem16<KV>::unpack(raw, x);
-                if (p.bias) {
-                    float bx[8];
-                    Elem16<KV>::unpack(*(const u32x4*)((const uint16_t*)p.bias + (size_t)h * D + pc * 8), bx);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = x[e] + bx[e];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] *= p.qscale;
-            }
-            vec8 hi, lo;
-            MF::split8(x, hi, lo);
-            *(vec8*)(qb + row * KPITCH + pc * 16) = hi;
-            *(vec8*)(qb + 16 * KPITCH + row * KPITCH + pc * 16) = lo;
-        }
-    }
-
-    // K/V rows [0, kend) of (b, j) from the cache; rows past kend read as zero
+    // K/V rows [0, kend) of (b, j) from the cache; rows past kend read as
+    // zero (and the V rows past kend are cleared below as well)
     const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;
     const auto krs = make_rsrc((const char*)p.k_cache + row0 * ROW, (uint32_t)kend * ROW);
     const auto vrs = make_rsrc((const char*)p.v_cache + row0 * ROW, (uint32_t)kend * ROW);
-    const int lr = tid / LPR, lc = tid % LPR;
-    u32x4 kr[NLD], vr[NLD];
-    auto issue = [&](int k0) {
+    auto issue = [&](int k0, unsigned char* kdst, unsigned char* vdst) {
 #pragma unroll
-        for (int u = 0; u < NLD; ++u) {
-            const int off = (k0 + u * RPI + lr) * ROW + lc * 16;
-            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+        for (int u = 0; u < NI; ++u) {
+            const int base = (wave * NI + u) * 1024;       // this load's bytes in the tile
+            const int row = (base + lane * 16) / ROW;
+            const int slot = (base + lane * 16) % ROW / 16;
+            buffer_load_lds16(krs, kdst + base, (k0 + row) * ROW + (slot ^ kswz(row)) * 16);
+            buffer_load_lds16(vrs, vdst + base, (k0 + row) * ROW + (slot ^ vswz(row)) * 16);
         }
     };
-    issue(0);
-
-    float m = kNegInfP;                     // query n: running max (same in all four quads)
-    float l = 0.0f;                         // query n: this lane's share of the sum
-    f32x4 acc[DT];                          // O[query 4g+i][16 tn + n]
+    // query operand of S^T, B layout, straight from memory: lane (n, g) of
+    // step kk holds elements 32 kk + 8 g .. +7 of query tq + 16 qb + n, as
+    // hi and lo halves of (q + b_q) * log2(e) / sqrt(D); queries past the
+    // prompt are zero.  The loads are unconditional (a query past the
+    // prompt reads the last row, a missing bias reads q, and both are
+    // selected away) so that they are all in flight together.
+    const bool has_bias = p.bias != nullptr;
+    const uint16_t* const bsrc = has_bias ? (const uint16_t*)p.bias + (size_t)h * D : (const uint16_t*)p.q;
+    u32x4 qraw[kQB][KK], braw[KK];
 #pragma unroll
-    for (int tn = 0; tn < DT; ++tn) acc[tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // the query operand stays in registers: B operand of step kk, hi and lo
-    vec8 qh[KK], ql[KK];
-    {
-        const unsigned char* qb = smem + wave * QBYTES;
-        lds_wave_fence();
+    for (int kk = 0; kk < KK; ++kk) braw[kk] = *(const u32x4*)(bsrc + 32 * kk + 8 * g);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        const int tc = min(tq + 16 * qb + n, Sb - 1);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qraw[qb][kk] = *(const u32x4*)((const uint16_t*)p.q + (((size_t)b * p.S + tc) * p.H + h) * D + 32 * kk + 8 * g);
+    }
+    issue(0, ktile0, vtile0);
+    vec8 qh[kQB][KK], ql[kQB][KK];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        const bool live = tq + 16 * qb + n < Sb;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const int piece = (kk * 4 + g) * 16;
-            qh[kk] = MF::bits8(*(const u32x4*)(qb + n * KPITCH + piece));
-            ql[kk] = MF::bits8(*(const u32x4*)(qb + 16 * KPITCH + n * KPITCH + piece));
+            float x[8], bx[8];
+            Elem16<KV>::unpack(qraw[qb][kk], x);
+            Elem16<KV>::unpack(braw[kk], bx);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y = has_bias ? x[e] + bx[e] : x[e];
+                x[e] = live ? y * p.qscale : 0.0f;
+            }
+            MF::split8(x, qh[qb][kk], ql[qb][kk]);
         }
     }
 
-    for (int k0 = 0; k0 < kend; k0 += kPK) {
-        __syncthreads();                    // the previous tile is consumed
+    // online softmax of query tq + 16 qb + n (the lane's column), in the
+    // log2 domain.  m is the reference the weights are taken against; it is
+    // raised only when some query of the wave sees a score more than kLazy
+    // above its own, so a weight never exceeds 2^kLazy and most steps skip
+    // the rescale of O (in exact arithmetic the result does not depend on
+    // the reference).
+    float m[kQB], l[kQB];                   // l: this lane's share of the sum
+    f32x4 acc[kQB][DT];                     // O^T[16 tn + 4g + i][query tq + 16 qb + n]
 #pragma unroll
-        for (int u = 0; u < NLD; ++u) {
-            *(u32x4*)(ktile + (u * RPI + lr) * KPITCH + lc * 16) = kr[u];
-            *(u32x4*)(vtile + (u * RPI + lr) * VPITCH + lc * 16) = vr[u];
+    for (int qb = 0; qb < kQB; ++qb) {
+        m[qb] = kNegInfP;
+        l[qb] = 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < DT; ++tn) acc[qb][tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    // per-lane LDS offsets: K row n of a 16-row block at step kk; V row
+    // 4g + n/4 of a 16-row block, bytes 8 (n % 4) .. +7 of column tile tn
+    // (the swizzles depend on the row only modulo 16)
+    int koff[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) koff[kk] = n * ROW + (((4 * kk + g) ^ kswz(n)) * 16);
+    const int vrow = 4 * g + (n >> 2);
+    const int vsw = vswz(vrow);
+    const int vbase = vrow * ROW + ((n & 3) >> 1) * 16 + (n & 1) * 8;
+
+    // one 64-key tile in buffer BUF (0 or 1, a compile-time constant)
+    auto tile = [&](const int k0, auto BUF) {
+        unsigned char* const kt = BUF ? ktile1 : ktile0;
+        unsigned char* const vt = BUF ? vtile1 : vtile0;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this lane's loads of the tile landed
+        __syncthreads();                    // every lane's did; the other buffer is consumed
+        if (k0 + kPK > kend) {              // last, partial tile: clear the V rows past kend
+            for (int off = (kend - k0) * ROW + tid * 16; off < TILE; off += 256 * 16)
+                *(u32x4*)(vt + off) = u32x4{0u, 0u, 0u, 0u};
+            __syncthreads();
         }
-        __syncthreads();
-        if (k0 + kPK < kend) issue(k0 + kPK);
+        if (k0 + kPK < kend) issue(k0 + kPK, BUF ? ktile0 : ktile1, BUF ? vtile0 : vtile1);
         __builtin_amdgcn_sched_barrier(0);
-        // two 16-key sub-tiles per step: four independent accumulation chains
-#pragma unroll
+        // 32 keys per step, as two 16-key halves
+#pragma unroll 1
         for (int sp = 0; sp < kPK / 32; ++sp) {
-            const int kb = k0 + 32 * sp;    // first key of the pair
-            if (kb > tq + 15) break;        // every key after every query of this wave
-            // S^T: row = key kb + 16 h2 + 4g + i, column = query tq + n
-            f32x4 sh[2], sl[2];
+            const int kb = k0 + 32 * sp;    // first key of the step
+            if (kb > tq + 16 * kQB - 1) break;   // every key after every query of this wave
+            // S^T: row = key kb + 16 h2 + 4g + i, column = query tq + 16 qb + n
+            // (the hi and lo products share one fp32 accumulator)
+            f32x4 sa[kQB][2];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) sh[h2] = sl[h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) sa[qb][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const int piece = (kk * 4 + g) * 16;
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    const vec8 ka = MF::bits8(*(const u32x4*)(ktile + (32 * sp + 16 * h2 + n) * KPITCH + piece));
-                    sh[h2] = MF::mma32(ka, qh[kk], sh[h2]);
-                    sl[h2] = MF::mma32(ka, ql[kk], sl[h2]);
+                    const vec8 ka = MF::bits8(*(const u32x4*)(kt + (32 * sp + 16 * h2) * ROW + koff[kk]));
+#pragma unroll
+                    for (int qb = 0; qb < kQB; ++qb) {
+                        sa[qb][h2] = MF::mma32(ka, qh[qb][kk], sa[qb][h2]);
+                        sa[qb][h2] = MF::mma32(ka, ql[qb][kk], sa[qb][h2]);
+                    }
                 }
             }
-            // causal mask (and keys past the prompt, which lie after every valid query)
-            float s[2][4];
+            // slot 4 h2 + i of this lane: key kb + 16 h2 + 4g + i
+            float s[kQB][8];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
+            for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s[h2][i] = kb + 16 * h2 + 4 * g + i <= tq + n ? sh[h2][i] + sl[h2][i] : kNegInfP;
-            float mt = kNegInfP;
+                for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
+                    for (int i = 0; i < 4; ++i) s[qb][4 * h2 + i] = sa[qb][h2][i];
+            if (kb + 31 > tq) {             // a key after some query: causal mask (also
+                                            // covers keys past the prompt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[h2][i]);
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float mn = fmaxf(m, mt);
-            const float ms = mn == kNegInfP ? 0.0f : mn;
-            const float alpha = fast_exp2(m - ms);
-            m = mn;
-            float ls = 0.0f;
+                for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s[h2][i] = fast_exp2(s[h2][i] - ms);
-                    ls += s[h2][i];
-                }
-            l = l * alpha + ls;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 4 * g + i);
-#pragma unroll
-                for (int tn = 0; tn < DT; ++tn) acc[tn][i] *= ai;
+                    for (int e = 0; e < 8; ++e)
+                        if (kb + 16 * (e / 4) + 4 * g + e % 4 > tq + 16 * qb + n) s[qb][e] = kNegInfP;
             }
+            float mt[kQB];
+            bool raise = false;
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                vec4 ph, pl;
-                MF::split4(s[h2], ph, pl);
-                // B operand V[key 4g+i][16 tn + n]: lane n of group g names row
-                // 4g + n/4 of the sub-tile, columns 4(n%4)..+3
-                const unsigned char* vrow = vtile + (32 * sp + 16 * h2 + 4 * g + (n >> 2)) * VPITCH + (n & 3) * 8;
+            for (int qb = 0; qb < kQB; ++qb) {
+                mt[qb] = fmaxf(fmaxf(fmaxf(s[qb][0], s[qb][1]), fmaxf(s[qb][2], s[qb][3])),
+                               fmaxf(fmaxf(s[qb][4], s[qb][5]), fmaxf(s[qb][6], s[qb][7])));
+                mt[qb] = column_max(mt[qb]);
+                raise = raise || mt[qb] > m[qb] + kLazy;
+            }
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
-                for (int tn = 0; tn < DT; ++tn) {
-                    const s16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(vrow + tn * 32));
-                    const vec4 vb = __builtin_bit_cast(vec4, tv);
-                    acc[tn] = MF::mma16(ph, vb, acc[tn]);
-                    acc[tn] = MF::mma16(pl, vb, acc[tn]);
+                for (int qb = 0; qb < kQB; ++qb) {
+                    const float mn = fmaxf(m[qb], mt[qb]);
+                    const float alpha = fast_exp2(m[qb] - (mn == kNegInfP ? 0.0f : mn));
+                    m[qb] = mn;
+                    l[qb] *= alpha;
+#pragma unroll
+                    for (int tn = 0; tn < DT; ++tn)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[qb][tn][i] *= alpha;
+                }
+            }
+            vec8 ph[kQB], pl[kQB];
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) {
+                const float ms = m[qb] == kNegInfP ? 0.0f : m[qb];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    s[qb][e] = fast_exp2(s[qb][e] - ms);
+                    l[qb] += s[qb][e];
+                }
+                MF::split8(s[qb], ph[qb], pl[qb]);
+            }
+            // O^T += V^T P^T: A = V^T (row 16 tn + n, the slots' keys, read
+            // down V's columns), B = P^T (this lane's slots for its query)
+#pragma unroll
+            for (int tn = 0; tn < DT; ++tn) {
+                const unsigned char* va0 = vt + 32 * sp * ROW + vbase + ((2 * tn) ^ vsw) * 16;
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(va0));
+                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(va0 + 16 * ROW));
+                const vec8 va = __builtin_bit_cast(vec8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) {
+                    acc[qb][tn] = MF::mma32(va, ph[qb], acc[qb][tn]);
+                    acc[qb][tn] = MF::mma32(va, pl[qb], acc[qb][tn]);
                 }
             }
         }
+    };
+    for (int k0 = 0; k0 < kend; k0 += 2 * kPK) {
+        tile(k0, std::integral_constant<int, 0>{});
+        if (k0 + kPK < kend) tile(k0 + kPK, std::integral_constant<int, 1>{});
     }
 
-    // l over the four quads of the column; out = O / l, rows 4g + i
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    // out[query][16 tn + 4g + i] = O^T / l, four consecutive columns
+    // (8 bytes) per lane and tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = tq + 4 * g + i;
-        const float inv = 1.0f / __shfl(l, 4 * g + i);
+    for (int qb = 0; qb < kQB; ++qb) {
+        const float inv = 1.0f / column_sum(l[qb]);
+        const int t = tq + 16 * qb + n;
         if (t < Sb) {
-            const size_t o = (((size_t)b * p.S + t) * p.H + h) * D;
+            uint16_t* orow = (uint16_t*)p.out + (((size_t)b * p.S + t) * p.H + h) * D + 4 * g;
 #pragma unroll
             for (int tn = 0; tn < DT; ++tn) {
-                const float v = acc[tn][i] * inv;
-                ((uint16_t*)p.out)[o + tn * 16 + n] =
-                    (uint16_t)(KV == KV_F16 ? float_to_half_bits(v) : float_to_bf16_bits(v));
+                uint32_t hb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = acc[qb][tn][i] * inv;
+                    hb[i] = KV == KV_F16 ? float_to_half_bits(v) : float_to_bf16_bits(v);
+                }
+                *(u32x2*)(orow + tn * 16) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
             }
         }
     }
@@ -283,7 +345,7 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     hipLaunchKernelGGL((prefill_append_kernel<KV, D>), dim3((unsigned)((slices + 255) / 256)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((p.S + kPQ - 1) / kPQ, p.H, p.B);
+    const dim3 grid((unsigned)(p.B * p.H), (p.S + kPQ - 1) / kPQ);
     hipLaunchKernelGGL((prefill_attn_kernel<KV, D>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
