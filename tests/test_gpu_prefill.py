@@ -35,8 +35,9 @@ def gpu_prefill(ftm, inp, case):
     return g, out
 
 
-def compare(ftm, case, tag, lens_override=None):
-    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+def compare(ftm, case, tag, lens_override=None, inp=None):
+    if inp is None:
+        inp = W.make_prefill_inputs(case, "cpu", poison=True)
     if lens_override is not None:
         inp["seq_lens"] = torch.tensor(lens_override, dtype=torch.int32)
     dt = case.dtype
@@ -76,6 +77,41 @@ SHAPES = [
 def test_prefill_parity(ftm, dt, B, S, H, Hkv, D, Lmax, lens):
     case = W.PrefillCase("t", B, S, H, Hkv, D, dt, Lmax, lens=lens, seed=41 + S + H)
     compare(ftm, case, f"prefill {dt} B{B} S{S} H{H}/{Hkv} D{D}")
+
+
+@pytest.mark.parametrize("dt,D", [("f16", 128), ("bf16", 64), ("bf16", 128)])
+def test_prefill_growing_scores(ftm, dt, D):
+    """Keys grow along one direction shared with every query, so the score
+    of key t' rises with t' by about 60 (log2 units) over the prompt and the
+    softmax concentrates on the newest keys: the running maximum grows many
+    times past any headroom, which exercises every rescale of the partial
+    output; the bias is left out so the growth stays as built."""
+    B, S, H, Hkv = 2, 520, 4, 2
+    case = W.PrefillCase("t", B, S, H, Hkv, D, dt, S + 8, lens=(400, 520), seed=61 + D)
+    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+    tdt = W.TORCH_DTYPES[dt]
+    u = torch.from_numpy(np.random.default_rng(5).choice([-1.0, 1.0], D)).float()
+    ramp = torch.arange(S, dtype=torch.float32) / S                              # [S]
+    amp = 60.0 / (1.4426950408889634 * np.sqrt(D))                               # score of the last key ~ 60
+    inp["q"] = (inp["q"].float() + u).to(tdt)
+    inp["k_new"] = (inp["k_new"].float() + amp * ramp[None, :, None, None] * u).to(tdt)
+    inp["v_new"] = (inp["v_new"].float() * np.sqrt(D)).to(tdt)                   # N(0, 1) values
+    inp["bias"] = torch.zeros_like(inp["bias"])
+    compare(ftm, case, f"prefill growing scores {dt} D{D}", inp=inp)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_prefill_sharp_scores(ftm, dt):
+    """Unit-variance queries, keys and values (no 1/sqrt(D) on the inputs):
+    scores of standard deviation about 1.4 in log2 units, a peaked softmax
+    whose maximum still moves now and then along the prompt."""
+    B, S, H, Hkv, D = 2, 600, 4, 4, 128
+    case = W.PrefillCase("t", B, S, H, Hkv, D, dt, S, lens=(500, 600), seed=83)
+    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+    tdt = W.TORCH_DTYPES[dt]
+    for k in ("q", "k_new", "v_new", "bias"):
+        inp[k] = (inp[k].float() * np.sqrt(D)).to(tdt)
+    compare(ftm, case, f"prefill sharp scores {dt}", inp=inp)
 
 
 def test_prefill_invalid_lengths(ftm):
