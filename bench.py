@@ -262,7 +262,21 @@ def run_prefill(args, case):
     t1 = time.perf_counter()
     gpu_ms = r0.elapsed_time(r1) / args.steps
     elapsed = t1 - t0
-    tflops = flops / (gpu_ms * 1e-3) / 1e12
+    # timed region 2: the same steps with a HIP event pair recorded around
+    # each of the two kernels, on the launch stream (kind 0: the attention,
+    # kind 1: the append)
+    ftm.ftm_timing_enable(args.steps + 8)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    n_att, ms_att = ftm.ftm_timing_read(0)
+    n_app, ms_app = ftm.ftm_timing_read(1)
+    ftm.ftm_timing_disable()
+    att_us = ms_att * 1e3 / max(n_att, 1)
+    app_us = ms_app * 1e3 / max(n_app, 1)
+    tflops = flops / (att_us * 1e-6) / 1e12
+    traffic = read_traffic("prefill_attn_kernel", case.name)
     result = {
         "metric": "prefill attention TFLOP/s (causal q.k + p.v, % of the dense fp16/bf16 matrix peak)",
         "value": round(flops * args.steps / elapsed / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -277,10 +291,13 @@ def run_prefill(args, case):
         "gpu_ms_per_step": round(gpu_ms, 5), "flops_per_step": flops, "kernels_per_step": 2,
         "device_copy_GBs": round(copy_gbs, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_attn_kernel (+ prefill_append_kernel)",
-                     "avg_launch_us": round(gpu_ms * 1e3, 2),
-                     "timing": "events bracketing the timed region / steps (append + attention)"},
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
+                     "kernel": "prefill_attn_kernel", "avg_launch_us": round(att_us, 2),
+                     "timing": "event pair around every attention launch in timed region 2",
+                     "launches": n_att, "flops_per_launch": flops,
+                     "append_kernel_avg_us": round(app_us, 2),
+                     "append_bytes_per_launch": W.prefill_append_bytes(case, lens)},
     }
     if args.cpu_budget > 0:
         import oracle

@@ -596,17 +596,31 @@ int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const v
     }
     if (head_dim != 64 && head_dim != 128)
         return fail(FTM_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) + " (built: 64, 128)");
-    if (n_heads > 65535 || batch > 65535)
-        return fail(FTM_ERR_UNSUPPORTED, "grid too large: n_heads and batch must be <= 65535");
+    if (batch > 65535 || (long long)batch * n_heads > 0x7fffffffLL || (prompt_len + 127) / 128 > 65535 ||
+        n_kv_heads > 65535 * 16)
+        return fail(FTM_ERR_UNSUPPORTED, "grid too large: batch <= 65535, batch * n_heads < 2^31, "
+                                         "prompt_len <= 65535 * 128 and n_kv_heads <= 65535 * 16");
     if ((size_t)max_seq_len * head_dim * 2 > 0x7fffffffu)
         return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
-    if ((long long)batch * prompt_len * n_kv_heads * (head_dim / 8) > 0x7fffffffLL * 256)
-        return fail(FTM_ERR_UNSUPPORTED, "prompt too large for one append launch");
     ftm::PrefillParams p{q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, batch, prompt_len,
                          max_seq_len, n_heads, n_kv_heads,
                          (float)(1.4426950408889634 / std::sqrt((double)head_dim))};
-    hipError_t he = ftm::launch_prefill(p, kv_dtype, head_dim, (hipStream_t)stream_ptr);
-    if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(he));
+    hipStream_t stream = (hipStream_t)stream_ptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (stream && hipStreamIsCapturing(stream, &cs) != hipSuccess)
+        return fail(FTM_ERR_HIP, "hipStreamIsCapturing failed");
+    const bool capturing = cs != hipStreamCaptureStatusNone;
+    const auto none = std::pair<hipEvent_t, hipEvent_t>{nullptr, nullptr};
+    auto ev = capturing ? none : timing_slot(1);
+    if (ev.first) (void)hipEventRecord(ev.first, stream);
+    hipError_t he = ftm::launch_prefill_append(p, kv_dtype, head_dim, stream);
+    if (ev.second) (void)hipEventRecord(ev.second, stream);
+    if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("prefill append launch: ") + hipGetErrorString(he));
+    ev = capturing ? none : timing_slot(0);
+    if (ev.first) (void)hipEventRecord(ev.first, stream);
+    he = ftm::launch_prefill_attention(p, kv_dtype, head_dim, stream);
+    if (ev.second) (void)hipEventRecord(ev.second, stream);
+    if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("prefill attention launch: ") + hipGetErrorString(he));
     g_last_error.clear();
     return FTM_OK;
 }

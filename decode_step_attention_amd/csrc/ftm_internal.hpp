@@ -83,7 +83,9 @@ struct PrefillParams {
 
 hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, int nw, hipStream_t s);
 // kv: KV_F16 or KV_BF16; head_dim 64 or 128.  Two launches: append, then attention.
-hipError_t launch_prefill(const PrefillParams& p, int kv, int head_dim, hipStream_t s);
+// The prompt's K/V rows into the cache, then the causal attention over them.
+hipError_t launch_prefill_append(const PrefillParams& p, int kv, int head_dim, hipStream_t s);
+hipError_t launch_prefill_attention(const PrefillParams& p, int kv, int head_dim, hipStream_t s);
 // act: KV_F16 or KV_BF16; B <= 64, hidden a multiple of 256, (H + 2 Hkv) D a multiple of 16.
 hipError_t launch_qkv_proj(const QkvParams& p, int act, int n_cu, hipStream_t s);
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);

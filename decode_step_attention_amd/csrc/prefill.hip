@@ -35,38 +35,39 @@ constexpr float kLazy = 8.0f;             // log2 headroom of the softmax refere
 
 template <int KV, int D>
 __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams p) {
-    constexpr int EPL = 8;                  // elements per thread (16 bytes)
-    constexpr int SL = D / EPL;             // slices per row
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t per_seq = (size_t)p.S * p.Hkv * SL;
-    if (idx >= (size_t)p.B * per_seq) return;
-    const int b = (int)(idx / per_seq);
-    const size_t rem = idx - (size_t)b * per_seq;
-    const int t = (int)(rem / ((size_t)p.Hkv * SL));
-    const int j = (int)(rem / SL % p.Hkv);
-    const int c = (int)(rem % SL);
+    // grid (S, slices of a row / 256, B): thread c of row (b, t) owns bytes
+    // 16 c .. +15 of the row's Hkv D elements, i.e. KV head c / (D / 8)
+    constexpr int SL = D / 8;               // 16-byte slices per head row
+    const int t = blockIdx.x;
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    const int b = blockIdx.z;
+    if (c >= p.Hkv * SL) return;
     const int Sb = p.seq_lens ? p.seq_lens[b] : p.S;
     if (Sb < 1 || Sb > p.S || t >= Sb) return;         // invalid length: no append
-    const size_t src = (((size_t)b * p.S + t) * p.Hkv + j) * D + c * EPL;
-    const size_t dst = (((size_t)b * p.Hkv + j) * p.Lmax + t) * D + c * EPL;
+    const int j = c / SL;
+    const int e0 = (c % SL) * 8;
+    const size_t src = ((size_t)b * p.S + t) * p.Hkv * D + (size_t)c * 8;
+    const size_t dst = (((size_t)b * p.Hkv + j) * p.Lmax + t) * D + e0;
+    const u32x4 kraw = *(const u32x4*)((const uint16_t*)p.k_new + src);
+    const u32x4 vraw = *(const u32x4*)((const uint16_t*)p.v_new + src);
+    u32x4 kb = u32x4{0u, 0u, 0u, 0u}, vb = kb;
+    if (p.bias) {
+        kb = *(const u32x4*)((const uint16_t*)p.bias + (size_t)(p.H + j) * D + e0);
+        vb = *(const u32x4*)((const uint16_t*)p.bias + (size_t)(p.H + p.Hkv + j) * D + e0);
+    }
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        const void* in = which ? p.v_new : p.k_new;
-        void* cache = which ? p.v_cache : p.k_cache;
-        const u32x4 raw = *(const u32x4*)((const uint16_t*)in + src);
-        uint32_t hb[EPL];
+        float x[8], bx[8];
+        Elem16<KV>::unpack(which ? vraw : kraw, x);
+        Elem16<KV>::unpack(which ? vb : kb, bx);
+        uint32_t hb[8];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const uint32_t bits = (raw[e / 2] >> (16 * (e % 2))) & 0xffffu;
-            float x = KV == KV_F16 ? half_bits_to_float(bits) : bf16_bits_to_float(bits);
-            if (p.bias) {
-                const uint32_t bb = ((const uint16_t*)p.bias)[(size_t)(p.H + which * p.Hkv + j) * D + c * EPL + e];
-                x = x + (KV == KV_F16 ? half_bits_to_float(bb) : bf16_bits_to_float(bb));   // one fp32 rounding
-            }
-            hb[e] = KV == KV_F16 ? float_to_half_bits(x) : float_to_bf16_bits(x);
+        for (int e = 0; e < 8; ++e) {
+            const float y = x[e] + bx[e];   // one fp32 rounding (an absent bias adds +0)
+            hb[e] = KV == KV_F16 ? float_to_half_bits(y) : float_to_bf16_bits(y);
         }
-        *(u32x4*)((uint16_t*)cache + dst) = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
-                                                  hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+        *(u32x4*)((uint16_t*)(which ? p.v_cache : p.k_cache) + dst) =
+            u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
     }
 }
 
@@ -340,11 +341,14 @@ prefill_attn_kernel(const PrefillParams p) {
 }
 
 template <int KV, int D>
-hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
-    const size_t slices = (size_t)p.B * p.S * p.Hkv * (D / 8);
-    hipLaunchKernelGGL((prefill_append_kernel<KV, D>), dim3((unsigned)((slices + 255) / 256)), dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_append_t(const PrefillParams& p, hipStream_t s) {
+    const dim3 grid((unsigned)p.S, (unsigned)((p.Hkv * (D / 8) + 255) / 256), (unsigned)p.B);
+    hipLaunchKernelGGL((prefill_append_kernel<KV, D>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int KV, int D>
+hipError_t launch_attention_t(const PrefillParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.B * p.H), (p.S + kPQ - 1) / kPQ);
     hipLaunchKernelGGL((prefill_attn_kernel<KV, D>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
@@ -352,9 +356,17 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, int kv, int head_dim, hipStream_t s) {
-    if (kv == KV_F16) return head_dim == 64 ? launch_prefill_t<KV_F16, 64>(p, s) : launch_prefill_t<KV_F16, 128>(p, s);
-    if (kv == KV_BF16) return head_dim == 64 ? launch_prefill_t<KV_BF16, 64>(p, s) : launch_prefill_t<KV_BF16, 128>(p, s);
+hipError_t launch_prefill_append(const PrefillParams& p, int kv, int head_dim, hipStream_t s) {
+    if (kv == KV_F16) return head_dim == 64 ? launch_append_t<KV_F16, 64>(p, s) : launch_append_t<KV_F16, 128>(p, s);
+    if (kv == KV_BF16) return head_dim == 64 ? launch_append_t<KV_BF16, 64>(p, s) : launch_append_t<KV_BF16, 128>(p, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_attention(const PrefillParams& p, int kv, int head_dim, hipStream_t s) {
+    if (kv == KV_F16)
+        return head_dim == 64 ? launch_attention_t<KV_F16, 64>(p, s) : launch_attention_t<KV_F16, 128>(p, s);
+    if (kv == KV_BF16)
+        return head_dim == 64 ? launch_attention_t<KV_BF16, 64>(p, s) : launch_attention_t<KV_BF16, 128>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -358,6 +358,13 @@ def make_prefill_inputs(case: PrefillCase, device="cpu", poison: bool = True) ->
     return t
 
 
+def prefill_append_bytes(case: PrefillCase, lens: Optional[List[int]] = None) -> int:
+    """Bytes the append moves: every prompt row of K and V read once (bias
+    aside) and written once to the cache."""
+    L = [case.prompt] * case.batch if lens is None else list(lens)
+    return sum(L) * case.n_kv_heads * case.head_dim * ELEM_BYTES[case.dtype] * 2 * 2
+
+
 def prefill_flops(case: PrefillCase, lens: Optional[List[int]] = None) -> int:
     """Multiply-adds x 2 of the causal attention: q.k and p.v over positions
     [0, t] for every prompt position t and query head."""

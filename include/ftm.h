@@ -208,7 +208,12 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
  * kv_dtype FTM_F16 or FTM_BF16 (activations of the same type); head_dim 64
  * or 128; S <= max_seq_len.  A sequence whose length lies outside [1, S] is
  * not appended and gets NaN rows.  Two kernels are enqueued (append, then
- * attention).  Errors as for ftm_decode_mha.
+ * attention).  The attention runs on the matrix cores with fp32
+ * accumulation; the query (bias added and scale folded in, in fp32) and the
+ * softmax weights enter as hi and lo halves, so about 22 (fp16) or 16
+ * (bf16) bits of each reach the accumulators.  Limits: batch up to 65535,
+ * batch * n_heads below 2^31, prompt_len up to 65535 * 128.  Errors as for
+ * ftm_decode_mha.
  */
 int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                     void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
@@ -284,13 +289,16 @@ int ftm_set_workgroup_waves(int waves);
 void ftm_release_workspaces(void);
 
 /* ---- kernel timing -------------------------------------------------------
- * For measurement only.  While enabled, every ftm_decode_mha call records a
- * HIP event pair around each kernel it launches, on the call's stream.
+ * For measurement only.  While enabled, every ftm_decode_mha(_paged) and
+ * ftm_prefill_mha call records a HIP event pair around each kernel it
+ * launches, on the call's stream (not while the stream is being captured).
  * ftm_timing_read() waits for the recorded events, returns the number of
  * launches and their summed duration in milliseconds for one kernel kind
- * and clears that kind's records.  Kinds: 0 = attention pass (split or
- * single-pass), 1 = combine.  At most `capacity` launches are kept per
- * kind; later ones are not recorded.  Returns FTM_OK or an error. */
+ * and clears that kind's records.  Kinds: 0 = attention pass (decode: split
+ * or single-pass; prefill: the causal attention), 1 = decode: combine,
+ * prefill: the append of the prompt's K/V rows.  At most `capacity`
+ * launches are kept per kind; later ones are not recorded.  Returns FTM_OK
+ * or an error. */
 int ftm_timing_enable(int capacity);
 int ftm_timing_disable(void);
 int ftm_timing_read(int kind, int* launches, double* total_ms);

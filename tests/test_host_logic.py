@@ -208,3 +208,36 @@ def test_binding_rejects_mismatched_projection_tensors():
         ftm.ftm_qkv_proj(x, w[:-16], None, q, k, k)
     with pytest.raises(TypeError):
         ftm.ftm_qkv_proj(x, w.half(), None, q, k, k)
+
+
+def call_prefill(**kw):
+    args = [("q", A), ("k_new", A), ("v_new", A), ("bias", None), ("k_cache", A), ("v_cache", A),
+            ("seq_lens", None), ("batch", 4), ("max_seq_len", 2048), ("prompt_len", 2048), ("n_heads", 32),
+            ("n_kv_heads", 32), ("head_dim", 128), ("kv_dtype", ftm.FTM_F16), ("out", A), ("stream", None)]
+    vals = [kw.get(k, v) for k, v in args]
+    rc = ftm.lib.ftm_prefill_mha(*vals)
+    return rc, ftm.ftm_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "NULL"),
+    (dict(out=None), 1, "NULL"),
+    (dict(batch=0), 1, ">= 1"),
+    (dict(n_heads=31), 1, "multiple"),
+    (dict(prompt_len=0), 1, "prompt_len"),
+    (dict(prompt_len=2049), 1, "prompt_len"),
+    (dict(kv_dtype=ftm.FTM_F32), 2, "fp16 or bf16"),
+    (dict(kv_dtype=ftm.FTM_I8), 2, "fp16 or bf16"),
+    (dict(kv_dtype=7), 1, "kv_dtype"),
+    (dict(k_cache=A + 8), 1, "aligned"),
+    (dict(seq_lens=A + 2), 1, "aligned"),
+    (dict(head_dim=96), 2, "head_dim"),
+    (dict(batch=65536, n_heads=1, n_kv_heads=1), 2, "grid"),
+    (dict(batch=40000, n_heads=65536, n_kv_heads=1), 2, "grid"),
+    (dict(max_seq_len=1 << 23, prompt_len=1), 2, "2 GiB"),
+    (dict(max_seq_len=1 << 23, prompt_len=(1 << 23) - 64), 2, "grid"),
+])
+def test_prefill_argument_errors_return_before_any_device_call(kw, status, needle):
+    rc, msg = call_prefill(**kw)
+    assert rc == status
+    assert needle in msg
