@@ -71,6 +71,27 @@ __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams
     }
 }
 
+// hi + lo halves of eight softmax weights (0 <= x <= 2^kLazy): hi keeps the
+// leading 11 (fp16) or 8 (bf16) significant bits by truncation, so it
+// converts exactly (for x at least 2^-14 in fp16) and the fp32 residual
+// x - hi is exact; lo is that residual rounded to the half type.
+template <int KV>
+__device__ __forceinline__ void split_weights(const float* x, typename Mfma<KV>::vec8& hi,
+                                              typename Mfma<KV>::vec8& lo) {
+    constexpr uint32_t kKeep = KV == KV_F16 ? 0xFFFFE000u : 0xFFFF0000u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float h = __uint_as_float(__float_as_uint(x[i]) & kKeep);
+        if constexpr (KV == KV_F16) {
+            hi[i] = (_Float16)h;
+            lo[i] = (_Float16)(x[i] - h);
+        } else {
+            hi[i] = (__bf16)h;
+            lo[i] = (__bf16)(x[i] - h);
+        }
+    }
+}
+
 template <int KV, int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_attn_kernel(const PrefillParams p) {
@@ -136,16 +157,24 @@ prefill_attn_kernel(const PrefillParams p) {
     const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;
     const auto krs = make_rsrc((const char*)p.k_cache + row0 * ROW, (uint32_t)kend * ROW);
     const auto vrs = make_rsrc((const char*)p.v_cache + row0 * ROW, (uint32_t)kend * ROW);
-    auto issue = [&](int k0, unsigned char* kdst, unsigned char* vdst) {
+    // one 64-key tile of K or V into LDS: NI loads per lane; load u of this
+    // wave fills tile bytes base(u) .. +1023, lane i bytes base + 16 i .. +15,
+    // which hold chunk slot ^ swz(row) of cache row k0 + row
+    int koffs[NI], voffs[NI];
 #pragma unroll
-        for (int u = 0; u < NI; ++u) {
-            const int base = (wave * NI + u) * 1024;       // this load's bytes in the tile
-            const int row = (base + lane * 16) / ROW;
-            const int slot = (base + lane * 16) % ROW / 16;
-            buffer_load_lds16(krs, kdst + base, (k0 + row) * ROW + (slot ^ kswz(row)) * 16);
-            buffer_load_lds16(vrs, vdst + base, (k0 + row) * ROW + (slot ^ vswz(row)) * 16);
-        }
+    for (int u = 0; u < NI; ++u) {
+        const int base = (wave * NI + u) * 1024;
+        const int row = (base + lane * 16) / ROW;
+        const int slot = (base + lane * 16) % ROW / 16;
+        koffs[u] = row * ROW + (slot ^ kswz(row)) * 16;
+        voffs[u] = row * ROW + (slot ^ vswz(row)) * 16;
+    }
+    auto issue = [&](const auto& rs, int k0, unsigned char* dst, const int* offs) {
+        const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * ROW));
+#pragma unroll
+        for (int u = 0; u < NI; ++u) buffer_load_lds16(rs, dst + (wave * NI + u) * 1024, offs[u], so);
     };
+
     // query operand of S^T, B layout, straight from memory: lane (n, g) of
     // step kk holds elements 32 kk + 8 g .. +7 of query tq + 16 qb + n, as
     // hi and lo halves of (q + b_q) * log2(e) / sqrt(D); queries past the
@@ -164,7 +193,9 @@ prefill_attn_kernel(const PrefillParams p) {
         for (int kk = 0; kk < KK; ++kk)
             qraw[qb][kk] = *(const u32x4*)((const uint16_t*)p.q + (((size_t)b * p.S + tc) * p.H + h) * D + 32 * kk + 8 * g);
     }
-    issue(0, ktile0, vtile0);
+    issue(krs, 0, ktile0, koffs);
+    issue(vrs, 0, vtile0, voffs);
+    issue(krs, kPK, ktile1, koffs);
     vec8 qh[kQB][KK], ql[kQB][KK];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
@@ -209,114 +240,183 @@ prefill_attn_kernel(const PrefillParams p) {
     const int vsw = vswz(vrow);
     const int vbase = vrow * ROW + ((n & 3) >> 1) * 16 + (n & 1) * 8;
 
-    // one 64-key tile in buffer BUF (0 or 1, a compile-time constant)
-    auto tile = [&](const int k0, auto BUF) {
-        unsigned char* const kt = BUF ? ktile1 : ktile0;
-        unsigned char* const vt = BUF ? vtile1 : vtile0;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this lane's loads of the tile landed
-        __syncthreads();                    // every lane's did; the other buffer is consumed
-        if (k0 + kPK > kend) {              // last, partial tile: clear the V rows past kend
-            for (int off = (kend - k0) * ROW + tid * 16; off < TILE; off += 256 * 16)
+    // The keys go in steps of 32 (two per 64-key tile), software-pipelined
+    // so that the matrix cores have work while the softmax runs: step j
+    // takes the softmax of its scores S(j), then computes S(j + 1) = K Q^T
+    // for the next step interleaved with the exponentials of step j, then
+    // O^T += V^T P(j).  K tiles are needed one step before V tiles, so the
+    // two are double-buffered a step apart: at every even step (new tile T)
+    // the workgroup waits for V(T) and refills the other V buffer with
+    // V(T + 1); at every odd step it waits for K(T + 1) and refills the other
+    // K buffer with K(T + 2).  Each load has two steps to land, and LDS holds
+    // two K and two V tiles.  Waves whose queries end earlier keep taking
+    // part in the barriers and loads.
+    const int nsteps = (kend + 31) / 32;
+    const int last_j = tq < Sb ? tq / 32 : -1;   // this wave's last (diagonal) step
+    // Every refill is issued, also past the last tile (its offsets lie past
+    // the buffer's end, so it writes zeros into a buffer no step reads
+    // again): the waits are then always "all but the newest batch of NI
+    // loads", and neither they nor the loads sit behind a branch, whose join
+    // made the compiler wait for every load in flight before the LDS reads.
+    // s_waitcnt vmcnt(NI): the gfx9 encoding puts vmcnt in bits 3:0, expcnt
+    // (7) in 6:4 and lgkmcnt (15) in 11:8; through the builtin the compiler
+    // sees the wait too.
+    auto wait_one_batch_behind = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70 | NI); };
+    // A workgroup barrier for LDS that leaves the newest tile loads in
+    // flight (__syncthreads would wait for every load into LDS): this wave's
+    // LDS accesses complete (lgkmcnt(0); vmcnt 63, expcnt 7 untouched), then
+    // s_barrier, which the compiler may not move memory accesses across.
+    auto lds_barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("s_barrier" ::: "memory");
+    };
+    static_assert(NI == 1 || NI == 2 || NI == 4, "tile loads per lane");
+    auto clear_v_tail = [&](int T, unsigned char* vt) {      // rows past kend of a partial tile
+        if (T * kPK + kPK > kend) {
+            for (int off = (kend - T * kPK) * ROW + tid * 16; off < TILE; off += 256 * 16)
                 *(u32x4*)(vt + off) = u32x4{0u, 0u, 0u, 0u};
-            __syncthreads();
+            lds_barrier();
         }
-        if (k0 + kPK < kend) issue(k0 + kPK, BUF ? ktile0 : ktile1, BUF ? vtile0 : vtile1);
-        __builtin_amdgcn_sched_barrier(0);
-        // 32 keys per step, as two 16-key halves
-#pragma unroll 1
-        for (int sp = 0; sp < kPK / 32; ++sp) {
-            const int kb = k0 + 32 * sp;    // first key of the step
-            if (kb > tq + 16 * kQB - 1) break;   // every key after every query of this wave
-            // S^T: row = key kb + 16 h2 + 4g + i, column = query tq + 16 qb + n
-            // (the hi and lo products share one fp32 accumulator)
-            f32x4 sa[kQB][2];
+    };
+
+    // S^T for the 32 keys of step jj from K buffer kt: row = key 32 jj + 16 h2
+    // + 4g + i, column = query tq + 16 qb + n (hi and lo products share one
+    // fp32 accumulator)
+    typedef f32x4 Scores[kQB][2];
+    auto qk = [&](Scores& sa, const unsigned char* kt, int half) {
 #pragma unroll
-            for (int qb = 0; qb < kQB; ++qb)
+        for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) sa[qb][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int h2 = 0; h2 < 2; ++h2) sa[qb][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
+        for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const vec8 ka = MF::bits8(*(const u32x4*)(kt + (32 * sp + 16 * h2) * ROW + koff[kk]));
-#pragma unroll
-                    for (int qb = 0; qb < kQB; ++qb) {
-                        sa[qb][h2] = MF::mma32(ka, qh[qb][kk], sa[qb][h2]);
-                        sa[qb][h2] = MF::mma32(ka, ql[qb][kk], sa[qb][h2]);
-                    }
-                }
-            }
-            // slot 4 h2 + i of this lane: key kb + 16 h2 + 4g + i
-            float s[kQB][8];
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s[qb][4 * h2 + i] = sa[qb][h2][i];
-            if (kb + 31 > tq) {             // a key after some query: causal mask (also
-                                            // covers keys past the prompt)
-#pragma unroll
-                for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (kb + 16 * (e / 4) + 4 * g + e % 4 > tq + 16 * qb + n) s[qb][e] = kNegInfP;
-            }
-            float mt[kQB];
-            bool raise = false;
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-                mt[qb] = fmaxf(fmaxf(fmaxf(s[qb][0], s[qb][1]), fmaxf(s[qb][2], s[qb][3])),
-                               fmaxf(fmaxf(s[qb][4], s[qb][5]), fmaxf(s[qb][6], s[qb][7])));
-                mt[qb] = column_max(mt[qb]);
-                raise = raise || mt[qb] > m[qb] + kLazy;
-            }
-            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const vec8 ka = MF::bits8(*(const u32x4*)(kt + (32 * half + 16 * h2) * ROW + koff[kk]));
 #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) {
-                    const float mn = fmaxf(m[qb], mt[qb]);
-                    const float alpha = fast_exp2(m[qb] - (mn == kNegInfP ? 0.0f : mn));
-                    m[qb] = mn;
-                    l[qb] *= alpha;
-#pragma unroll
-                    for (int tn = 0; tn < DT; ++tn)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[qb][tn][i] *= alpha;
-                }
-            }
-            vec8 ph[kQB], pl[kQB];
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-                const float ms = m[qb] == kNegInfP ? 0.0f : m[qb];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    s[qb][e] = fast_exp2(s[qb][e] - ms);
-                    l[qb] += s[qb][e];
-                }
-                MF::split8(s[qb], ph[qb], pl[qb]);
-            }
-            // O^T += V^T P^T: A = V^T (row 16 tn + n, the slots' keys, read
-            // down V's columns), B = P^T (this lane's slots for its query)
-#pragma unroll
-            for (int tn = 0; tn < DT; ++tn) {
-                const unsigned char* va0 = vt + 32 * sp * ROW + vbase + ((2 * tn) ^ vsw) * 16;
-                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(va0));
-                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(va0 + 16 * ROW));
-                const vec8 va = __builtin_bit_cast(vec8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) {
-                    acc[qb][tn] = MF::mma32(va, ph[qb], acc[qb][tn]);
-                    acc[qb][tn] = MF::mma32(va, pl[qb], acc[qb][tn]);
+                    sa[qb][h2] = MF::mma32(ka, qh[qb][kk], sa[qb][h2]);
+                    sa[qb][h2] = MF::mma32(ka, ql[qb][kk], sa[qb][h2]);
                 }
             }
         }
     };
-    for (int k0 = 0; k0 < kend; k0 += 2 * kPK) {
-        tile(k0, std::integral_constant<int, 0>{});
-        if (k0 + kPK < kend) tile(k0 + kPK, std::integral_constant<int, 1>{});
+
+    Scores scur, snext;
+    __builtin_amdgcn_s_waitcnt(0x0F70);     // the first tiles (and the query) landed
+    __syncthreads();
+    clear_v_tail(0, vtile0);
+    if (0 <= last_j) qk(scur, ktile0, 0);
+
+    // step j = j0 + U of a 4-step (two-tile) group: buffers by U
+    auto step = [&](const int j0, auto U) {
+        constexpr int u = decltype(U)::value;
+        const int j = j0 + u;
+        const int T = j / 2;
+        unsigned char* const vt = (u / 2) ? vtile1 : vtile0;               // V(T)
+        if constexpr (u % 2 == 0) {
+            // new tile T: V(T) must have landed; V(T - 1)'s buffer is free
+            if (j > 0) {
+                wait_one_batch_behind();    // K(T + 1) was issued after V(T)
+                lds_barrier();
+                clear_v_tail(T, vt);
+            }
+            issue(vrs, T * kPK + kPK, (u / 2) ? vtile0 : vtile1, voffs);
+        } else {
+            // K(T + 1) must have landed; K(T)'s buffer is free for K(T + 2)
+            wait_one_batch_behind();        // V(T + 1) was issued after K(T + 1)
+            lds_barrier();
+            issue(krs, T * kPK + 2 * kPK, (u / 2) ? ktile1 : ktile0, koffs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (j > last_j) return;
+        const int kb = 32 * j;              // first key of the step
+        // scores of this step; slot 4 h2 + i of this lane: key kb + 16 h2 + 4g + i
+        float s[kQB][8];
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[qb][4 * h2 + i] = scur[qb][h2][i];
+        if (j == last_j) {                  // the diagonal step: causal mask (also covers
+                                            // keys past the prompt)
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (kb + 16 * (e / 4) + 4 * g + e % 4 > tq + 16 * qb + n) s[qb][e] = kNegInfP;
+        }
+        // the reference only needs raising when some score lies more than
+        // kLazy above it; the maxima are taken only then
+        bool raise = false;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const float thr = m[qb] + kLazy;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) raise = raise || s[qb][e] > thr;
+        }
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) {
+                const float mt = fmaxf(fmaxf(fmaxf(s[qb][0], s[qb][1]), fmaxf(s[qb][2], s[qb][3])),
+                                       fmaxf(fmaxf(s[qb][4], s[qb][5]), fmaxf(s[qb][6], s[qb][7])));
+                const float mn = fmaxf(m[qb], column_max(mt));
+                const float alpha = fast_exp2(m[qb] - (mn == kNegInfP ? 0.0f : mn));
+                m[qb] = mn;
+                l[qb] *= alpha;
+#pragma unroll
+                for (int tn = 0; tn < DT; ++tn)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[qb][tn][i] *= alpha;
+            }
+        }
+        // S(j + 1) for the next step (K of tile (j + 1) / 2), interleaved by
+        // the scheduler with this step's exponentials.  Unconditional, so
+        // that no branch separates the two: after a wave's last step the
+        // result is not used (and may come from stale LDS).
+        qk(snext, (u == 0 || u == 3) ? ktile0 : ktile1, (j + 1) % 2);
+        vec8 ph[kQB], pl[kQB];
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const float ms = m[qb] == kNegInfP ? 0.0f : m[qb];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                s[qb][e] = fast_exp2(s[qb][e] - ms);
+                l[qb] += s[qb][e];
+            }
+            split_weights<KV>(s[qb], ph[qb], pl[qb]);
+        }
+        // O^T += V^T P^T: A = V^T (row 16 tn + n, the slots' keys, read
+        // down V's columns), B = P^T (this lane's slots for its query)
+#pragma unroll
+        for (int tn = 0; tn < DT; ++tn) {
+            const unsigned char* va0 = vt + 32 * (j % 2) * ROW + vbase + ((2 * tn) ^ vsw) * 16;
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(va0));
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(va0 + 16 * ROW));
+            const vec8 va = __builtin_bit_cast(vec8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) {
+                acc[qb][tn] = MF::mma32(va, ph[qb], acc[qb][tn]);
+                acc[qb][tn] = MF::mma32(va, pl[qb], acc[qb][tn]);
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) scur[qb][h2] = snext[qb][h2];
+    };
+    for (int j0 = 0; j0 < nsteps; j0 += 4) {
+        step(j0, std::integral_constant<int, 0>{});
+        if (j0 + 1 < nsteps) step(j0, std::integral_constant<int, 1>{});
+        if (j0 + 2 < nsteps) step(j0, std::integral_constant<int, 2>{});
+        if (j0 + 3 < nsteps) step(j0, std::integral_constant<int, 3>{});
     }
+    // the last refills are still in flight: let them land before the wave
+    // can end and the workgroup's LDS be handed on
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // out[query][16 tn + 4g + i] = O^T / l, four consecutive columns
     // (8 bytes) per lane and tile
