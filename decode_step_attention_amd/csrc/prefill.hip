@@ -6,20 +6,20 @@
 //
 // prefill_append_kernel: the prompt's K/V rows, with the bias added in fp32,
 //   rounded to nearest even into the cache (one 16-byte slice per thread).
-// prefill_attn_kernel: one workgroup of 4 waves owns 64 query positions of
-//   one query head; wave w owns 16 of them.  The workgroup streams the key
-//   positions [0, last query] in tiles of 64 through LDS; each wave computes,
-//   32 keys at a time (four independent accumulation chains), S^T = K Q^T
-//   for 16 keys x its 16 queries and O += P V on the matrix cores
-//   (v_mfma_f32_16x16x32 and 16x16x16), with the online softmax in between
-//   and the causal mask on the diagonal tiles.  S^T leaves each lane with
-//   four consecutive keys of one query, which is the A-operand layout of P;
-//   V is read down its columns with the transposing LDS read.  The query
+// prefill_attn_kernel: one workgroup of 4 waves owns 128 query positions of
+//   one query head; each wave owns two blocks of 16.  Keys [0, last query]
+//   go through LDS in 64-key tiles, loaded straight from the cache into LDS
+//   (16 bytes per lane) and swizzled against bank conflicts.  Each wave
+//   takes 32 keys per step: S^T = K Q^T on the matrix cores
+//   (v_mfma_f32_16x16x32), which leaves each lane with four keys of one
+//   query, already the B-operand layout of P^T; the online softmax in the
+//   query's own lanes; and O^T += V^T P^T, with V read down its columns by the
+//   transposing LDS read.  The steps are software-pipelined: the next
+//   step's S^T is computed between this step's exponentials.  The query
 //   (bias added, log2(e)/sqrt(D) folded in, kept in registers) and the
-//   weights enter as hi/lo
-//   halves, so about 16 (bf16) or 22 (fp16) bits of each reach the fp32
-//   accumulators, as in the decode pass.  Workgroups with the most keys
-//   are launched first.
+//   weights enter as hi/lo halves, so about 16 (bf16) or 22 (fp16) bits of
+//   each reach the fp32 accumulators, as in the decode pass.  Workgroups
+//   with the most keys are launched first.
 #include <cstdlib>
 
 #include "gfx950.hpp"
