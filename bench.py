@@ -460,6 +460,17 @@ def main():
         n_att, ms_att = ftm.ftm_timing_read(0)
         n_cmb, ms_cmb = ftm.ftm_timing_read(1)
         ftm.ftm_timing_disable()
+    # timed region 3: an event pair around every step, for the distribution
+    # of step times (each pair adds its own dispatch and release, a few us)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run_step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_us = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in ev]))
     for g in graphs:
         ftm.ftm_graph_destroy(g)
     elapsed = t1 - t0
@@ -504,6 +515,11 @@ def main():
         "kernels_per_step": kernels_per_step,
         "gpu_ms_per_step": round(region_gpu_ms / args.steps, 5),
         "combine_avg_launch_us": round(ms_cmb * 1e3 / n_cmb, 2) if n_cmb else None,
+        "step_us_per_step_events": {"p50": round(float(np.percentile(step_us, 50)), 2),
+                                    "p99": round(float(np.percentile(step_us, 99)), 2),
+                                    "mean": round(float(step_us.mean()), 2),
+                                    "note": "timed region 3: an event pair around every step, which adds "
+                                            "its own dispatch and release time"},
         "device_copy_GBs": round(copy_gbs, 1),
         "roofline": roof,
     }

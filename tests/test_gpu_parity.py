@@ -174,7 +174,9 @@ def test_grouped_heads_matrix_core_and_vector_paths(ftm, monkeypatch, vector_alu
 @pytest.mark.parametrize("B,Lmax,lens,kv", [(1, 8192, (8192, 8192), "bf16"),   # one unit, many slices
                                              (2, 3000, (1, 3000), "f16"),
                                              (37, 700, (1, 700), "bf16"),      # many short units
-                                             (5, 64, (1, 64), "f16")])          # less work than one slice
+                                             (5, 64, (1, 64), "f16"),           # less work than one slice
+                                             (256, 96, (1, 96), "bf16"),        # the largest batch of the pass
+                                             (257, 96, (1, 96), "f16")])        # one more: the vector path
 def test_grouped_heads_balanced_schedule(ftm, B, Lmax, lens, kv):
     """The grouped-query pass splits the total work evenly over a fixed grid;
     slices cross unit boundaries and a unit may be merged from many slices

@@ -114,6 +114,27 @@ def test_prefill_sharp_scores(ftm, dt):
     compare(ftm, case, f"prefill sharp scores {dt}", inp=inp)
 
 
+@pytest.mark.parametrize("dt,D", [("f16", 128), ("bf16", 64)])
+def test_prefill_without_bias_and_lengths(ftm, dt, D):
+    """qkv_bias = NULL and seq_lens = NULL (every prompt S long)."""
+    case = W.PrefillCase("t", 2, 170, 6, 2, D, dt, 176, seed=71 + D)
+    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+    npi = {k: to_np(v, dt) for k, v in inp.items() if k != "seq_lens"}
+    ref = oracle.prefill_mha(npi["q"], npi["k_new"], npi["v_new"], None, npi["k_cache"], npi["v_cache"], None,
+                             case.n_heads, case.n_kv_heads, D, dt)
+    g = {k: v.cuda() for k, v in inp.items()}
+    out = torch.zeros((case.batch, case.prompt, case.n_heads, D), dtype=W.TORCH_DTYPES[dt], device="cuda")
+    ftm.ftm_prefill_mha(g["q"], g["k_new"], g["v_new"], None, g["k_cache"], g["v_cache"], None, out)
+    torch.cuda.synchronize()
+    assert to_np(g["k_cache"], dt).tobytes() == npi["k_cache"].tobytes(), "k_cache"
+    assert to_np(g["v_cache"], dt).tobytes() == npi["v_cache"].tobytes(), "v_cache"
+    ac = W.Case("p", case.batch, case.n_heads, case.n_kv_heads, D, dt, ctx=case.prompt,
+                max_seq_len=case.max_seq_len, value_scale=1.0)
+    got = out_to_f64(out)
+    for b in range(case.batch):
+        check(ac, got[b], ref[b], f"prefill no bias/lengths {dt} D{D} b{b}")
+
+
 def test_prefill_invalid_lengths(ftm):
     case = W.PrefillCase("t", 3, 100, 4, 2, 128, "f16", 128, seed=7)
     compare(ftm, case, "prefill invalid lengths", lens_override=[100, 0, 101])
