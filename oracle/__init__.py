@@ -274,6 +274,52 @@ def prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, n_heads, 
     return out
 
 
+def prefill_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, n_heads,
+                      n_kv_heads, head_dim, kv_dtype):
+    """Prefill into a paged cache: writes the prompt's K/V rows into their
+    pages in place and returns out[B, S, H, D] float64.
+
+    Position i of sequence b is row i mod P of page block_table[b, i // P]
+    (paging is address translation only: [intelliparadigm.com .../2131745]
+    section 5.1, [framerc.cn/news/4453289] section 3.2).  A prefill reads
+    only the rows it writes itself, so it is the contiguous prefill above run
+    on a fresh contiguous cache, whose rows [0, S_b) are then written to the
+    pages the table names.
+
+    Contract for a table entry outside [0, n_pages) among the pages of
+    positions [0, S_b): the sequence's output rows [0, S_b) are NaN, and
+    only the rows whose page is valid are appended.
+
+    Layouts: k_pages/v_pages [n_pages, Hkv, P, D]; block_table int32
+    [B, max_pages] with max_pages P >= S."""
+    n_pages, Hkv, P, D = k_pages.shape
+    B, S = q.shape[0], q.shape[1]
+    _, max_pages = block_table.shape
+    if Hkv != n_kv_heads or D != head_dim or v_pages.shape != k_pages.shape:
+        raise ValueError("page pool shape does not match n_kv_heads / head_dim")
+    if max_pages * P < S:
+        raise ValueError("the table has too few pages for the prompt")
+    lens = np.full(B, S) if seq_lens is None else np.asarray(seq_lens, dtype=np.int64)
+    kc = np.zeros((B, Hkv, S, D), dtype=k_pages.dtype)
+    vc = np.zeros_like(kc)
+    out = prefill_mha(q, k_new, v_new, qkv_bias, kc, vc, seq_lens, n_heads, n_kv_heads, head_dim, kv_dtype)
+    tbl = np.asarray(block_table, dtype=np.int64)
+    for b in range(B):
+        Sb = int(lens[b])
+        if Sb < 1 or Sb > S:
+            continue                        # NaN rows already, no append
+        entries = tbl[b, :(Sb + P - 1) // P]
+        ok = (entries >= 0) & (entries < n_pages)
+        if not ok.all():
+            out[b, :Sb] = np.nan
+        for t in range(Sb):
+            if ok[t // P]:
+                pg = int(entries[t // P])
+                k_pages[pg, :, t % P] = kc[b, :, t]
+                v_pages[pg, :, t % P] = vc[b, :, t]
+    return out
+
+
 def round_to_act(y, act_dtype):
     """float64 values rounded to nearest even in the activation type, as the
     array type the oracle takes (bfloat16 as uint16 bit patterns)."""
