@@ -244,8 +244,14 @@ def run_prefill(args, case):
     inp = W.make_prefill_inputs(case, dev, poison=False)
     out = torch.empty((case.batch, case.prompt, case.n_heads, case.head_dim), dtype=W.TORCH_DTYPES[case.dtype],
                       device=dev)
-    call = ftm.ftm_prefill_mha_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"], inp["k_cache"],
-                                        inp["v_cache"], inp["seq_lens"], out, stream=stream.cuda_stream)
+    if case.page_size:
+        inp = W.prefill_to_paged(inp, case, case.page_size)
+        call = ftm.ftm_prefill_mha_paged_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"], inp["k_pages"],
+                                                  inp["v_pages"], inp["block_table"], inp["seq_lens"], out,
+                                                  stream=stream.cuda_stream)
+    else:
+        call = ftm.ftm_prefill_mha_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"], inp["k_cache"],
+                                            inp["v_cache"], inp["seq_lens"], out, stream=stream.cuda_stream)
     lens = inp["seq_lens"].cpu().tolist()
     flops = W.prefill_flops(case, lens)
     copy_gbs = device_copy_gbs(dev)
@@ -286,7 +292,8 @@ def run_prefill(args, case):
         "config": {"workload": f"{case.name}: batch {case.batch} x {case.prompt} tokens, {case.n_heads}q/"
                                f"{case.n_kv_heads}kv heads x {case.head_dim}",
                    "batch": case.batch, "prompt": case.prompt, "n_heads": case.n_heads,
-                   "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim},
+                   "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim,
+                   "cache_layout": f"paged, {case.page_size}-token pages" if case.page_size else "contiguous"},
         "tokens_per_s": round(sum(lens) * args.steps / elapsed, 1),
         "gpu_ms_per_step": round(gpu_ms, 5), "flops_per_step": flops, "kernels_per_step": 2,
         "device_copy_GBs": round(copy_gbs, 1),
@@ -302,7 +309,7 @@ def run_prefill(args, case):
     if args.cpu_budget > 0:
         import oracle
         hc = {k: (v.cpu().view(torch.int16).numpy().view(np.uint16) if case.dtype == "bf16" else v.cpu().numpy())
-              for k, v in inp.items() if k != "seq_lens"}
+              for k, v in inp.items() if k not in ("seq_lens", "block_table")}
         # one sequence, the first head group only: a bounded sample
         G = case.n_heads // case.n_kv_heads
         D = case.head_dim

@@ -567,21 +567,29 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
     return FTM_OK;
 }
 
-int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
-                    void* k_cache, void* v_cache, const int32_t* seq_lens, int batch, int max_seq_len,
-                    int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, void* out,
-                    void* stream_ptr) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the contiguous and the paged prefill: cache_rows is max_seq_len
+// (contiguous) or max_pages_per_seq * page_size (paged), the rows a sequence
+// can hold; block_table null for the contiguous cache.
+int prefill_impl(const void* q, const void* k_new, const void* v_new, const void* qkv_bias, void* k_cache,
+                 void* v_cache, const int32_t* seq_lens, int batch, int cache_rows, const char* cache_rows_name,
+                 int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, void* out,
+                 void* stream_ptr, const int32_t* block_table, int page_shift, int max_pages, int n_pages) {
     if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
         return fail(FTM_ERR_INVALID_ARG, "a required pointer (q, k_new, v_new, k_cache, v_cache, out) is NULL");
-    if (batch < 1 || max_seq_len < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
-        return fail(FTM_ERR_INVALID_ARG, "batch, max_seq_len, n_heads, n_kv_heads and head_dim must be >= 1");
+    if (batch < 1 || cache_rows < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
+        return fail(FTM_ERR_INVALID_ARG, std::string("batch, ") + cache_rows_name +
+                                             ", n_heads, n_kv_heads and head_dim must be >= 1");
     if (n_heads % n_kv_heads != 0)
         return fail(FTM_ERR_INVALID_ARG, "n_heads (" + std::to_string(n_heads) +
                                              ") is not a multiple of n_kv_heads (" +
                                              std::to_string(n_kv_heads) + ")");
-    if (prompt_len < 1 || prompt_len > max_seq_len)
-        return fail(FTM_ERR_INVALID_ARG, "prompt_len " + std::to_string(prompt_len) +
-                                             " outside [1, max_seq_len=" + std::to_string(max_seq_len) + "]");
+    if (prompt_len < 1 || prompt_len > cache_rows)
+        return fail(FTM_ERR_INVALID_ARG, "prompt_len " + std::to_string(prompt_len) + " outside [1, " +
+                                             cache_rows_name + "=" + std::to_string(cache_rows) + "]");
     if (kv_dtype < FTM_F32 || kv_dtype > FTM_I8)
         return fail(FTM_ERR_INVALID_ARG, "unknown kv_dtype " + std::to_string(kv_dtype));
     if (kv_dtype != FTM_F16 && kv_dtype != FTM_BF16)
@@ -600,11 +608,12 @@ int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const v
         n_kv_heads > 65535 * 16)
         return fail(FTM_ERR_UNSUPPORTED, "grid too large: batch <= 65535, batch * n_heads < 2^31, "
                                          "prompt_len <= 65535 * 128 and n_kv_heads <= 65535 * 16");
-    if ((size_t)max_seq_len * head_dim * 2 > 0x7fffffffu)
+    if (!block_table && (size_t)cache_rows * head_dim * 2 > 0x7fffffffu)
         return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
     ftm::PrefillParams p{q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, batch, prompt_len,
-                         max_seq_len, n_heads, n_kv_heads,
-                         (float)(1.4426950408889634 / std::sqrt((double)head_dim))};
+                         cache_rows, n_heads, n_kv_heads,
+                         (float)(1.4426950408889634 / std::sqrt((double)head_dim)),
+                         block_table, page_shift, max_pages, n_pages};
     hipStream_t stream = (hipStream_t)stream_ptr;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (stream && hipStreamIsCapturing(stream, &cs) != hipSuccess)
@@ -623,6 +632,41 @@ int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const v
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("prefill attention launch: ") + hipGetErrorString(he));
     g_last_error.clear();
     return FTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                    void* k_cache, void* v_cache, const int32_t* seq_lens, int batch, int max_seq_len,
+                    int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, void* out,
+                    void* stream_ptr) {
+    return prefill_impl(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len, "max_seq_len",
+                        prompt_len, n_heads, n_kv_heads, head_dim, kv_dtype, out, stream_ptr, nullptr, 0, 0, 0);
+}
+
+int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                          void* k_pages, void* v_pages, const int32_t* block_table, int n_pages, int page_size,
+                          int max_pages_per_seq, const int32_t* seq_lens, int batch, int prompt_len, int n_heads,
+                          int n_kv_heads, int head_dim, int kv_dtype, void* out, void* stream_ptr) {
+    if (!block_table) return fail(FTM_ERR_INVALID_ARG, "block_table is NULL");
+    if (((uintptr_t)block_table & 3u) != 0) return fail(FTM_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    if (n_pages < 1 || max_pages_per_seq < 1)
+        return fail(FTM_ERR_INVALID_ARG, "n_pages and max_pages_per_seq must be >= 1");
+    if (page_size < 16 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0)
+        return fail(FTM_ERR_INVALID_ARG, "page_size " + std::to_string(page_size) +
+                                             " must be a power of two in [16, 65536]");
+    const long long cap = (long long)max_pages_per_seq * page_size;
+    if (cap > 0x7fffffffLL)
+        return fail(FTM_ERR_UNSUPPORTED, "max_pages_per_seq * page_size must stay below 2^31");
+    if ((long long)page_size * head_dim * 2 > 0x7fffffffLL)
+        return fail(FTM_ERR_UNSUPPORTED, "one page of one KV head must stay below 2 GiB");
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    return prefill_impl(q, k_new, v_new, qkv_bias, k_pages, v_pages, seq_lens, batch, (int)cap,
+                        "max_pages_per_seq * page_size", prompt_len, n_heads, n_kv_heads, head_dim, kv_dtype, out,
+                        stream_ptr, block_table, shift, max_pages_per_seq, n_pages);
 }
 
 int ftm_graph_begin(void* stream) {

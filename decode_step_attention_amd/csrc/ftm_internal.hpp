@@ -79,6 +79,11 @@ struct PrefillParams {
     void* out;              // [B, S, H, D] act
     int B, S, Lmax, H, Hkv;
     float qscale;           // log2(e) / sqrt(D)
+    // paged cache (block_table non-null): k_cache/v_cache are pools
+    // [n_pages, Hkv, 2^page_shift, D], position t of sequence b is row
+    // t mod P of page block_table[b * max_pages + t / P]
+    const int32_t* block_table;
+    int page_shift, max_pages, n_pages;
 };
 
 hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, int nw, hipStream_t s);

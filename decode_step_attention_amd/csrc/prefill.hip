@@ -33,7 +33,7 @@ constexpr int kPK = 64;                   // key positions per LDS tile
 constexpr float kNegInfP = -__builtin_inff();
 constexpr float kLazy = 8.0f;             // log2 headroom of the softmax reference
 
-template <int KV, int D>
+template <int KV, int D, bool PG>
 __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams p) {
     // grid (S, slices of a row / 256, B): thread c of row (b, t) owns bytes
     // 16 c .. +15 of the row's Hkv D elements, i.e. KV head c / (D / 8)
@@ -47,7 +47,16 @@ __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams
     const int j = c / SL;
     const int e0 = (c % SL) * 8;
     const size_t src = ((size_t)b * p.S + t) * p.Hkv * D + (size_t)c * 8;
-    const size_t dst = (((size_t)b * p.Hkv + j) * p.Lmax + t) * D + e0;
+    size_t dst;
+    if constexpr (PG) {
+        // row t mod P of the page the table names; no append into a page
+        // outside the pool
+        const int pg = p.block_table[(size_t)b * p.max_pages + (t >> p.page_shift)];
+        if (pg < 0 || pg >= p.n_pages) return;
+        dst = ((((size_t)pg * p.Hkv + j) << p.page_shift) + (t & ((1 << p.page_shift) - 1))) * D + e0;
+    } else {
+        dst = (((size_t)b * p.Hkv + j) * p.Lmax + t) * D + e0;
+    }
     const u32x4 kraw = *(const u32x4*)((const uint16_t*)p.k_new + src);
     const u32x4 vraw = *(const u32x4*)((const uint16_t*)p.v_new + src);
     u32x4 kb = u32x4{0u, 0u, 0u, 0u}, vb = kb;
@@ -92,7 +101,7 @@ __device__ __forceinline__ void split_weights(const float* x, typename Mfma<KV>:
     }
 }
 
-template <int KV, int D>
+template <int KV, int D, bool PG>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_attn_kernel(const PrefillParams p) {
     using MF = Mfma<KV>;
@@ -149,12 +158,31 @@ prefill_attn_kernel(const PrefillParams p) {
         return;
     }
     if (t0 >= Sb) return;                   // past the prompt: nothing to do
+    if constexpr (PG) {
+        // a page outside the pool among the sequence's pages: NaN rows
+        const int npg = (Sb + (1 << p.page_shift) - 1) >> p.page_shift;
+        bool bad = false;
+        for (int i = lane; i < npg; i += 64) {
+            const int pg = p.block_table[(size_t)b * p.max_pages + i];
+            bad = bad || pg < 0 || pg >= p.n_pages;
+        }
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+            for (int idx = tid; idx < kPQ * D; idx += 256) {
+                const int t = t0 + idx / D;
+                if (t < Sb) {
+                    const size_t o = (((size_t)b * p.S + t) * p.H + h) * D + idx % D;
+                    ((uint16_t*)p.out)[o] = KV == KV_F16 ? 0x7e00u : 0x7fc0u;
+                }
+            }
+            return;
+        }
+    }
     const int kend = min(t0 + kPQ, Sb);     // keys [0, kend) are needed
     const int tq = t0 + wave * 16 * kQB;    // this wave's first query
 
     // K/V rows [0, kend) of (b, j) from the cache; rows past kend read as
     // zero (and the V rows past kend are cleared below as well)
-    const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;
+    const size_t row0 = PG ? 0 : ((size_t)b * p.Hkv + j) * p.Lmax;
     const auto krs = make_rsrc((const char*)p.k_cache + row0 * ROW, (uint32_t)kend * ROW);
     const auto vrs = make_rsrc((const char*)p.v_cache + row0 * ROW, (uint32_t)kend * ROW);
     // one 64-key tile of K or V into LDS: NI loads per lane; load u of this
@@ -169,10 +197,34 @@ prefill_attn_kernel(const PrefillParams p) {
         koffs[u] = row * ROW + (slot ^ kswz(row)) * 16;
         voffs[u] = row * ROW + (slot ^ vswz(row)) * 16;
     }
-    auto issue = [&](const auto& rs, int k0, unsigned char* dst, const int* offs) {
-        const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * ROW));
+    // Paged: the rows of one load (1 KiB: 4 or 8 rows, page sizes are at
+    // least 16) lie in one page, so each load takes a descriptor over its
+    // page's rows below kend, built from one table entry read through the
+    // scalar cache.  A page past the table or outside the pool reads as
+    // zeros (the sequence's rows are then NaN, see above).
+    const __attribute__((address_space(4))) int32_t* tbl =
+        (const __attribute__((address_space(4))) int32_t*)(PG ? p.block_table + (size_t)b * p.max_pages : nullptr);
+    auto issue = [&](const bool is_v, int k0, unsigned char* dst, const int* offs) {
+        if constexpr (!PG) {
+            const auto rs = is_v ? vrs : krs;
+            const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * ROW));
 #pragma unroll
-        for (int u = 0; u < NI; ++u) buffer_load_lds16(rs, dst + (wave * NI + u) * 1024, offs[u], so);
+            for (int u = 0; u < NI; ++u) buffer_load_lds16(rs, dst + (wave * NI + u) * 1024, offs[u], so);
+        } else {
+            const char* pool = (const char*)(is_v ? p.v_cache : p.k_cache);
+#pragma unroll
+            for (int u = 0; u < NI; ++u) {
+                const int key0 = __builtin_amdgcn_readfirstlane(k0 + (wave * NI + u) * (1024 / ROW));
+                const int pi = key0 >> p.page_shift;
+                const int pg = tbl[min(pi, p.max_pages - 1)];
+                const bool ok = pi < p.max_pages && pg >= 0 && pg < p.n_pages;
+                const int prow0 = pi << p.page_shift;
+                const int nrows = ok ? max(0, min(kend - prow0, 1 << p.page_shift)) : 0;
+                const auto prs = make_rsrc(pool + (((size_t)(ok ? pg : 0) * p.Hkv + j) << p.page_shift) * ROW,
+                                           (uint32_t)nrows * ROW);
+                buffer_load_lds16(prs, dst + (wave * NI + u) * 1024, offs[u] + (k0 - prow0) * ROW, 0);
+            }
+        }
     };
 
     // query operand of S^T, B layout, straight from memory: lane (n, g) of
@@ -193,9 +245,9 @@ prefill_attn_kernel(const PrefillParams p) {
         for (int kk = 0; kk < KK; ++kk)
             qraw[qb][kk] = *(const u32x4*)((const uint16_t*)p.q + (((size_t)b * p.S + tc) * p.H + h) * D + 32 * kk + 8 * g);
     }
-    issue(krs, 0, ktile0, koffs);
-    issue(vrs, 0, vtile0, voffs);
-    issue(krs, kPK, ktile1, koffs);
+    issue(false, 0, ktile0, koffs);
+    issue(true, 0, vtile0, voffs);
+    issue(false, kPK, ktile1, koffs);
     vec8 qh[kQB][KK], ql[kQB][KK];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
@@ -321,12 +373,12 @@ prefill_attn_kernel(const PrefillParams p) {
                 lds_barrier();
                 clear_v_tail(T, vt);
             }
-            issue(vrs, T * kPK + kPK, (u / 2) ? vtile0 : vtile1, voffs);
+            issue(true, T * kPK + kPK, (u / 2) ? vtile0 : vtile1, voffs);
         } else {
             // K(T + 1) must have landed; K(T)'s buffer is free for K(T + 2)
             wait_one_batch_behind();        // V(T + 1) was issued after K(T + 1)
             lds_barrier();
-            issue(krs, T * kPK + 2 * kPK, (u / 2) ? ktile1 : ktile0, koffs);
+            issue(false, T * kPK + 2 * kPK, (u / 2) ? ktile1 : ktile0, koffs);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (j > last_j) return;
@@ -443,14 +495,20 @@ prefill_attn_kernel(const PrefillParams p) {
 template <int KV, int D>
 hipError_t launch_append_t(const PrefillParams& p, hipStream_t s) {
     const dim3 grid((unsigned)p.S, (unsigned)((p.Hkv * (D / 8) + 255) / 256), (unsigned)p.B);
-    hipLaunchKernelGGL((prefill_append_kernel<KV, D>), grid, dim3(256), 0, s, p);
+    if (p.block_table)
+        hipLaunchKernelGGL((prefill_append_kernel<KV, D, true>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_append_kernel<KV, D, false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 template <int KV, int D>
 hipError_t launch_attention_t(const PrefillParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.B * p.H), (p.S + kPQ - 1) / kPQ);
-    hipLaunchKernelGGL((prefill_attn_kernel<KV, D>), grid, dim3(256), 0, s, p);
+    if (p.block_table)
+        hipLaunchKernelGGL((prefill_attn_kernel<KV, D, true>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_attn_kernel<KV, D, false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ _ACT = {FTM_F32: torch.float32, FTM_F16: torch.float16, FTM_BF16: torch.bfloat16
         FTM_I8: torch.float16}
 
 # Every symbol include/ftm.h declares.
-EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_qkv_proj", "ftm_prefill_mha", "ftm_kv_cache_bytes",
+EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_qkv_proj", "ftm_prefill_mha", "ftm_prefill_mha_paged",
+           "ftm_kv_cache_bytes",
            "ftm_last_error",
            "ftm_version", "ftm_set_split_chunk", "ftm_set_workgroup_waves", "ftm_release_workspaces",
            "ftm_graph_begin", "ftm_graph_end", "ftm_graph_launch", "ftm_graph_destroy",
@@ -47,6 +48,9 @@ def _load() -> ctypes.CDLL:
     lib.ftm_qkv_proj.restype = i32
     lib.ftm_prefill_mha.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.ftm_prefill_mha.restype = i32
+    lib.ftm_prefill_mha_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, i32,
+                                          i32, vp, vp]
+    lib.ftm_prefill_mha_paged.restype = i32
     lib.ftm_graph_begin.argtypes = [vp]
     lib.ftm_graph_begin.restype = i32
     lib.ftm_graph_end.argtypes = [vp, ctypes.POINTER(vp)]
@@ -328,6 +332,47 @@ def ftm_prefill_mha_prepared(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_le
     """ftm_prefill_mha with the arguments marshalled once."""
     args = _marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream)
     return _prepared(lib.ftm_prefill_mha, args, (q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out))
+
+
+def _marshal_prefill_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, stream):
+    if q.dim() != 4 or k_pages.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q must be [B, S, H, D], the pools [n_pages, Hkv, P, D] and block_table "
+                         "[B, max_pages_per_seq]")
+    B, S, H, D = q.shape
+    n_pages, Hkv, P, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    kv = _TORCH_TO_KV.get(k_pages.dtype)
+    if kv is None:
+        raise TypeError(f"unsupported cache dtype {k_pages.dtype}")
+    dt = k_pages.dtype
+    tensors = {"q": (q, dt, (B, S, H, D)), "k_new": (k_new, dt, (B, S, Hkv, D)),
+               "v_new": (v_new, dt, (B, S, Hkv, D)), "k_pages": (k_pages, dt, (n_pages, Hkv, P, D)),
+               "v_pages": (v_pages, dt, (n_pages, Hkv, P, D)), "block_table": (block_table, torch.int32, (B, max_pages)),
+               "out": (out, dt, (B, S, H, D))}
+    if qkv_bias is not None:
+        tensors["qkv_bias"] = (qkv_bias, dt, ((H + 2 * Hkv) * D,))
+    if seq_lens is not None:
+        tensors["seq_lens"] = (seq_lens, torch.int32, (B,))
+    _check_tensors(tensors, k_pages.device)
+    return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+            n_pages, P, max_pages, _ptr(seq_lens), B, S, H, Hkv, D, kv, _ptr(out),
+            _stream_ptr(stream, k_pages.device))
+
+
+def ftm_prefill_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out,
+                          stream=None) -> None:
+    """Prefill into a paged cache (see include/ftm.h): pools [n_pages, Hkv, P, D],
+    block_table int32 [B, max_pages_per_seq], the rest as ftm_prefill_mha."""
+    _check(lib.ftm_prefill_mha_paged(*_marshal_prefill_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages,
+                                                             block_table, seq_lens, out, stream)))
+
+
+def ftm_prefill_mha_paged_prepared(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out,
+                                   stream=None) -> Callable[[], None]:
+    """ftm_prefill_mha_paged with the arguments marshalled once."""
+    args = _marshal_prefill_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, stream)
+    return _prepared(lib.ftm_prefill_mha_paged, args,
+                     (q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out))
 
 
 def ftm_graph_begin(stream: int) -> None:

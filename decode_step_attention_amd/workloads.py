@@ -322,6 +322,7 @@ class PrefillCase:
     max_seq_len: int
     lens: Optional[tuple] = None
     seed: int = 3000
+    page_size: int = 0                      # 0: contiguous cache; else a paged one (pages of this many rows)
 
     def with_(self, **kw) -> "PrefillCase":
         return replace(self, **kw)
@@ -331,6 +332,8 @@ class PrefillCase:
 PREFILL_CASES: Dict[str, PrefillCase] = {
     "prefill_7b": PrefillCase("prefill_7b", 4, 2048, 32, 32, 128, "f16", 2048, seed=3001),
     "prefill_gqa": PrefillCase("prefill_gqa", 4, 2048, 64, 8, 128, "bf16", 2048, seed=3003),
+    "prefill_7b_paged": PrefillCase("prefill_7b_paged", 4, 2048, 32, 32, 128, "f16", 2048, seed=3001,
+                                    page_size=256),
 }
 
 
@@ -355,6 +358,37 @@ def make_prefill_inputs(case: PrefillCase, device="cpu", poison: bool = True) ->
         g = torch.Generator().manual_seed(case.seed + 77)
         L = torch.randint(case.lens[0], case.lens[1] + 1, (B,), generator=g, dtype=torch.int32)
     t["seq_lens"] = L.to(device)
+    return t
+
+
+def prefill_to_paged(t: Dict[str, torch.Tensor], case: PrefillCase, page_size: int) -> Dict[str, torch.Tensor]:
+    """Replaces the contiguous caches of ``make_prefill_inputs`` by page pools.
+
+    Sequence b takes ceil(S_b / P) pages; the pool holds those plus
+    max(1, B / 4) spare pages, handed out in a seeded random order.  Adds
+    ``k_pages``/``v_pages`` [n_pages, Hkv, P, D] filled like the caches
+    they replace (NaN or zero) and ``block_table`` int32
+    [B, ceil(max_seq_len / P)] (-1 past a sequence's pages)."""
+    P = page_size
+    k = t.pop("k_cache")
+    t.pop("v_cache")
+    B, Hkv, Lmax, D = k.shape
+    L = t["seq_lens"].cpu().tolist()
+    max_pages = (Lmax + P - 1) // P
+    need = [min(max(0, (int(x) + P - 1) // P), max_pages) for x in L]
+    n_pages = sum(need) + max(1, B // 4)
+    g = torch.Generator().manual_seed((case.seed * 7919 + P) % (2 ** 62))
+    perm = torch.randperm(n_pages, generator=g).tolist()
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    n = 0
+    for b in range(B):
+        for i in range(need[b]):
+            table[b, i] = perm[n]
+            n += 1
+    fill = k.flatten()[0].item()
+    t["k_pages"] = torch.full((n_pages, Hkv, P, D), fill, dtype=k.dtype, device=k.device)
+    t["v_pages"] = torch.full_like(t["k_pages"], fill)
+    t["block_table"] = table.to(k.device)
     return t
 
 

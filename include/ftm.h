@@ -220,6 +220,32 @@ int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const v
                     int max_seq_len, int prompt_len, int n_heads, int n_kv_heads, int head_dim,
                     int kv_dtype, void* out, void* stream);
 
+/*
+ * ftm_prefill_mha_paged -- prefill into a paged KV cache.
+ *
+ * The same prefill as ftm_prefill_mha, with the cache cut into fixed-size
+ * pages located through a block table ([intelliparadigm.com
+ * /article/weixin_32285357/2131745] section 5.1; [framerc.cn/news/4453289]
+ * section 3.2): position t of sequence b is row t mod P of page
+ * block_table[b, t / P], in the layout ftm_decode_mha_paged reads.
+ *
+ *   k_pages, v_pages [n_pages, n_kv_heads, page_size, D]  rows of the
+ *                     prompt positions written, every other row untouched
+ *   block_table [batch, max_pages_per_seq] int32, device; only the entries
+ *                     of pages holding positions < S_b are read
+ * page_size is a power of two in [16, 65536]; prompt_len <= max_pages_per_seq
+ * * page_size.  A table entry outside [0, n_pages) among the pages of
+ * positions [0, S_b) makes the sequence's output rows [0, S_b) NaN, and no
+ * row is appended into such a page (the rows of its valid pages are).
+ * Everything else (shapes of q, k_new, v_new, qkv_bias, seq_lens, out,
+ * numerics, limits, errors, the two kernels) is ftm_prefill_mha's.
+ */
+int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                          void* k_pages, void* v_pages, const int32_t* block_table, int n_pages,
+                          int page_size, int max_pages_per_seq, const int32_t* seq_lens, int batch,
+                          int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
+                          void* out, void* stream);
+
 /* ---- HIP graphs ----------------------------------------------------------
  * A decode step of a model is one call per layer on fixed buffers; its
  * kernel launches can be recorded once and replayed as one graph launch, so
@@ -290,7 +316,7 @@ void ftm_release_workspaces(void);
 
 /* ---- kernel timing -------------------------------------------------------
  * For measurement only.  While enabled, every ftm_decode_mha(_paged) and
- * ftm_prefill_mha call records a HIP event pair around each kernel it
+ * ftm_prefill_mha(_paged) call records a HIP event pair around each kernel it
  * launches, on the call's stream (not while the stream is being captured).
  * ftm_timing_read() waits for the recorded events, returns the number of
  * launches and their summed duration in milliseconds for one kernel kind

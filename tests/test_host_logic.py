@@ -241,3 +241,33 @@ def test_prefill_argument_errors_return_before_any_device_call(kw, status, needl
     rc, msg = call_prefill(**kw)
     assert rc == status
     assert needle in msg
+
+
+def call_prefill_paged(**kw):
+    args = [("q", A), ("k_new", A), ("v_new", A), ("bias", None), ("k_pages", A), ("v_pages", A),
+            ("block_table", A), ("n_pages", 64), ("page_size", 256), ("max_pages", 8), ("seq_lens", None),
+            ("batch", 4), ("prompt_len", 2048), ("n_heads", 32), ("n_kv_heads", 32), ("head_dim", 128),
+            ("kv_dtype", ftm.FTM_F16), ("out", A), ("stream", None)]
+    vals = [kw.get(k, v) for k, v in args]
+    rc = ftm.lib.ftm_prefill_mha_paged(*vals)
+    return rc, ftm.ftm_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(block_table=None), 1, "block_table is NULL"),
+    (dict(block_table=A + 2), 1, "4-byte aligned"),
+    (dict(n_pages=0), 1, "n_pages"),
+    (dict(max_pages=0), 1, "max_pages_per_seq"),
+    (dict(page_size=8), 1, "power of two"),
+    (dict(page_size=96), 1, "power of two"),
+    (dict(page_size=1 << 17), 1, "power of two"),
+    (dict(prompt_len=2049), 1, "prompt_len"),
+    (dict(max_pages=1 << 16, page_size=1 << 16), 2, "2^31"),
+    (dict(kv_dtype=ftm.FTM_I8), 2, "fp16 or bf16"),
+    (dict(q=None), 1, "NULL"),
+    (dict(head_dim=96), 2, "head_dim"),
+])
+def test_paged_prefill_argument_errors_return_before_any_device_call(kw, status, needle):
+    rc, msg = call_prefill_paged(**kw)
+    assert rc == status, msg
+    assert needle in msg
