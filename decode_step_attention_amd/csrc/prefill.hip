@@ -197,11 +197,13 @@ prefill_attn_kernel(const PrefillParams p) {
         koffs[u] = row * ROW + (slot ^ kswz(row)) * 16;
         voffs[u] = row * ROW + (slot ^ vswz(row)) * 16;
     }
-    // Paged: the rows of one load (1 KiB: 4 or 8 rows, page sizes are at
-    // least 16) lie in one page, so each load takes a descriptor over its
-    // page's rows below kend, built from one table entry read through the
-    // scalar cache.  A page past the table or outside the pool reads as
+    // Paged: the rows a wave loads per tile (NI loads of 1 KiB, 16
+    // consecutive rows starting at a multiple of 16; page sizes are at least
+    // 16) lie in one page, so the wave's loads share one descriptor over
+    // that page's rows below kend, built from one table entry read through
+    // the scalar cache.  A page past the table or outside the pool reads as
     // zeros (the sequence's rows are then NaN, see above).
+    static_assert(NI * (1024 / ROW) == 16, "a wave loads 16 rows per tile");
     const __attribute__((address_space(4))) int32_t* tbl =
         (const __attribute__((address_space(4))) int32_t*)(PG ? p.block_table + (size_t)b * p.max_pages : nullptr);
     auto issue = [&](const bool is_v, int k0, unsigned char* dst, const int* offs) {
@@ -212,18 +214,17 @@ prefill_attn_kernel(const PrefillParams p) {
             for (int u = 0; u < NI; ++u) buffer_load_lds16(rs, dst + (wave * NI + u) * 1024, offs[u], so);
         } else {
             const char* pool = (const char*)(is_v ? p.v_cache : p.k_cache);
+            const int key0 = __builtin_amdgcn_readfirstlane(k0 + wave * 16);
+            const int pi = key0 >> p.page_shift;
+            const int pg = tbl[min(pi, p.max_pages - 1)];
+            const bool ok = pi < p.max_pages && pg >= 0 && pg < p.n_pages;
+            const int prow0 = pi << p.page_shift;
+            const int nrows = ok ? max(0, min(kend - prow0, 1 << p.page_shift)) : 0;
+            const auto prs = make_rsrc(pool + (((size_t)(ok ? pg : 0) * p.Hkv + j) << p.page_shift) * ROW,
+                                       (uint32_t)nrows * ROW);
 #pragma unroll
-            for (int u = 0; u < NI; ++u) {
-                const int key0 = __builtin_amdgcn_readfirstlane(k0 + (wave * NI + u) * (1024 / ROW));
-                const int pi = key0 >> p.page_shift;
-                const int pg = tbl[min(pi, p.max_pages - 1)];
-                const bool ok = pi < p.max_pages && pg >= 0 && pg < p.n_pages;
-                const int prow0 = pi << p.page_shift;
-                const int nrows = ok ? max(0, min(kend - prow0, 1 << p.page_shift)) : 0;
-                const auto prs = make_rsrc(pool + (((size_t)(ok ? pg : 0) * p.Hkv + j) << p.page_shift) * ROW,
-                                           (uint32_t)nrows * ROW);
+            for (int u = 0; u < NI; ++u)
                 buffer_load_lds16(prs, dst + (wave * NI + u) * 1024, offs[u] + (k0 - prow0) * ROW, 0);
-            }
         }
     };
 
