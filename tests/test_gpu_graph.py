@@ -155,3 +155,50 @@ def test_capture_refuses_to_grow_the_workspace(ftm):
         assert torch.equal(bits(out_d), bits(ref_d))
     finally:
         ftm.ftm_graph_destroy(graph)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_graph_replays_match_eager_calls(ftm, paged):
+    """A prefill (append + attention) captured into a graph: every replay,
+    with new query values between replays and eager work in between, must
+    give the eager call's outputs and caches bit for bit."""
+    case = W.PrefillCase("t", 2, 200, 8, 2, 128, "bf16", 256, lens=(120, 200), seed=111)
+    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+    if paged:
+        inp = W.prefill_to_paged(inp, case, 64)
+    g = {k: v.cuda() for k, v in inp.items()}
+    ck, cv = ("k_pages", "v_pages") if paged else ("k_cache", "v_cache")
+    out = torch.zeros((case.batch, case.prompt, case.n_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def prefill(o):
+        if paged:
+            ftm.ftm_prefill_mha_paged(g["q"], g["k_new"], g["v_new"], g["bias"], g[ck], g[cv], g["block_table"],
+                                      g["seq_lens"], o, stream=stream.cuda_stream)
+        else:
+            ftm.ftm_prefill_mha(g["q"], g["k_new"], g["v_new"], g["bias"], g[ck], g[cv], g["seq_lens"], o,
+                                stream=stream.cuda_stream)
+
+    ftm.ftm_graph_begin(stream.cuda_stream)
+    try:
+        prefill(out)
+    finally:
+        graph = ftm.ftm_graph_end(stream.cuda_stream)
+    try:
+        gen = torch.Generator().manual_seed(5)
+        for rep in range(3):
+            q_new = (torch.randn(g["q"].shape, generator=gen) / np.sqrt(case.head_dim)).to(torch.bfloat16)
+            g["q"].copy_(q_new.cuda())
+            torch.cuda.synchronize()
+            ftm.ftm_graph_launch(graph, stream.cuda_stream)
+            stream.synchronize()
+            got, got_k = out.clone(), g[ck].clone()
+            _ = (g["q"].float() * 2).sum().item()          # eager work between replays
+            ref = torch.zeros_like(out)
+            with torch.cuda.stream(stream):
+                prefill(ref)
+            stream.synchronize()
+            assert torch.equal(bits(got), bits(ref)), f"replay {rep}: outputs"
+            assert torch.equal(bits(got_k), bits(g[ck])), f"replay {rep}: caches"
+    finally:
+        ftm.ftm_graph_destroy(graph)
