@@ -16,10 +16,12 @@
 //   query's own lanes; and O^T += V^T P^T, with V read down its columns by the
 //   transposing LDS read.  The steps are software-pipelined: the next
 //   step's S^T is computed between this step's exponentials.  The query
-//   (bias added, log2(e)/sqrt(D) folded in, kept in registers) and the
-//   weights enter as hi/lo halves, so about 16 (bf16) or 22 (fp16) bits of
-//   each reach the fp32 accumulators, as in the decode pass.  Workgroups
-//   with the most keys are launched first.
+//   enters exactly as stored (kept in registers) and the bias term b_q . k,
+//   the same for every query of a head, once per key, so every product is
+//   exact in fp32; log2(e)/sqrt(D) scales the fp32 scores.  The weights
+//   enter as hi/lo halves, so about 16 (bf16) or 22 (fp16) bits of each
+//   reach the accumulators, as in the decode pass.  Workgroups with the
+//   most keys are launched first.
 #include <cstdlib>
 
 #include "gfx950.hpp"
@@ -101,7 +103,7 @@ __device__ __forceinline__ void split_weights(const float* x, typename Mfma<KV>:
     }
 }
 
-template <int KV, int D, bool PG>
+template <int KV, int D, bool PG, bool BIAS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_attn_kernel(const PrefillParams p) {
     using MF = Mfma<KV>;
@@ -229,16 +231,20 @@ prefill_attn_kernel(const PrefillParams p) {
     };
 
     // query operand of S^T, B layout, straight from memory: lane (n, g) of
-    // step kk holds elements 32 kk + 8 g .. +7 of query tq + 16 qb + n, as
-    // hi and lo halves of (q + b_q) * log2(e) / sqrt(D); queries past the
-    // prompt are zero.  The loads are unconditional (a query past the
-    // prompt reads the last row, a missing bias reads q, and both are
-    // selected away) so that they are all in flight together.
-    const bool has_bias = p.bias != nullptr;
-    const uint16_t* const bsrc = has_bias ? (const uint16_t*)p.bias + (size_t)h * D : (const uint16_t*)p.q;
+    // step kk holds elements 32 kk + 8 g .. +7 of query tq + 16 qb + n
+    // exactly as stored, so every product on the matrix cores is exact in
+    // fp32; the scale log2(e)/sqrt(D) is applied to the fp32 scores.  Queries
+    // past the prompt are zero.  The bias term b_q . k is the same for every
+    // query of the head: it is computed once per key, with the bias as a
+    // second B operand (the same in every column), and added to the scores
+    // in fp32.  The loads are unconditional (a query past the prompt reads
+    // the last row, selected away) so that they are all in flight together.
     u32x4 qraw[kQB][KK], braw[KK];
+    if constexpr (BIAS) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) braw[kk] = *(const u32x4*)(bsrc + 32 * kk + 8 * g);
+        for (int kk = 0; kk < KK; ++kk)
+            braw[kk] = *(const u32x4*)((const uint16_t*)p.bias + (size_t)h * D + 32 * kk + 8 * g);
+    }
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         const int tc = min(tq + 16 * qb + n, Sb - 1);
@@ -249,35 +255,32 @@ prefill_attn_kernel(const PrefillParams p) {
     issue(false, 0, ktile0, koffs);
     issue(true, 0, vtile0, voffs);
     issue(false, kPK, ktile1, koffs);
-    vec8 qh[kQB][KK], ql[kQB][KK];
+    vec8 qv[kQB][KK], bv[KK];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         const bool live = tq + 16 * qb + n < Sb;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            float x[8], bx[8];
-            Elem16<KV>::unpack(qraw[qb][kk], x);
-            Elem16<KV>::unpack(braw[kk], bx);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float y = has_bias ? x[e] + bx[e] : x[e];
-                x[e] = live ? y * p.qscale : 0.0f;
-            }
-            MF::split8(x, qh[qb][kk], ql[qb][kk]);
-        }
+        for (int kk = 0; kk < KK; ++kk) qv[qb][kk] = MF::bits8(live ? qraw[qb][kk] : u32x4{0u, 0u, 0u, 0u});
     }
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) bv[kk] = MF::bits8(braw[kk]);
+    }
+    const float c = p.qscale;               // log2(e) / sqrt(D)
+    const float inv_c = 1.0f / c;
 
     // online softmax of query tq + 16 qb + n (the lane's column), in the
-    // log2 domain.  m is the reference the weights are taken against; it is
-    // raised only when some query of the wave sees a score more than kLazy
-    // above its own, so a weight never exceeds 2^kLazy and most steps skip
-    // the rescale of O (in exact arithmetic the result does not depend on
-    // the reference).
-    float m[kQB], l[kQB];                   // l: this lane's share of the sum
+    // log2 domain (score x c).  m is the reference the weights are taken
+    // against; it is raised only when some query of the wave sees a score
+    // more than kLazy above its own, so a weight never exceeds 2^kLazy and
+    // most steps skip the rescale of O (in exact arithmetic the result does
+    // not depend on the reference).  thr is that bound in unscaled units.
+    float m[kQB], l[kQB], thr[kQB];         // l: this lane's share of the sum
     f32x4 acc[kQB][DT];                     // O^T[16 tn + 4g + i][query tq + 16 qb + n]
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         m[qb] = kNegInfP;
+        thr[qb] = kNegInfP;
         l[qb] = 0.0f;
 #pragma unroll
         for (int tn = 0; tn < DT; ++tn) acc[qb][tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -332,13 +335,13 @@ prefill_attn_kernel(const PrefillParams p) {
         }
     };
 
-    // S^T for the 32 keys of step jj from K buffer kt: row = key 32 jj + 16 h2
-    // + 4g + i, column = query tq + 16 qb + n (hi and lo products share one
-    // fp32 accumulator)
-    typedef f32x4 Scores[kQB][2];
+    // unscaled S^T for the 32 keys of step jj from K buffer kt: row = key
+    // 32 jj + 16 h2 + 4g + i, column = query tq + 16 qb + n; entry kQB holds
+    // b_q . k (every column alike)
+    typedef f32x4 Scores[kQB + 1][2];
     auto qk = [&](Scores& sa, const unsigned char* kt, int half) {
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
+        for (int qb = 0; qb <= kQB; ++qb)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) sa[qb][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -347,10 +350,8 @@ prefill_attn_kernel(const PrefillParams p) {
             for (int h2 = 0; h2 < 2; ++h2) {
                 const vec8 ka = MF::bits8(*(const u32x4*)(kt + (32 * half + 16 * h2) * ROW + koff[kk]));
 #pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) {
-                    sa[qb][h2] = MF::mma32(ka, qh[qb][kk], sa[qb][h2]);
-                    sa[qb][h2] = MF::mma32(ka, ql[qb][kk], sa[qb][h2]);
-                }
+                for (int qb = 0; qb < kQB; ++qb) sa[qb][h2] = MF::mma32(ka, qv[qb][kk], sa[qb][h2]);
+                if constexpr (BIAS) sa[kQB][h2] = MF::mma32(ka, bv[kk], sa[kQB][h2]);
             }
         }
     };
@@ -391,7 +392,8 @@ prefill_attn_kernel(const PrefillParams p) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[qb][4 * h2 + i] = scur[qb][h2][i];
+                for (int i = 0; i < 4; ++i)
+                    s[qb][4 * h2 + i] = BIAS ? scur[qb][h2][i] + scur[kQB][h2][i] : scur[qb][h2][i];
         if (j == last_j) {                  // the diagonal step: causal mask (also covers
                                             // keys past the prompt)
 #pragma unroll
@@ -404,19 +406,18 @@ prefill_attn_kernel(const PrefillParams p) {
         // kLazy above it; the maxima are taken only then
         bool raise = false;
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-            const float thr = m[qb] + kLazy;
+        for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) raise = raise || s[qb][e] > thr;
-        }
+            for (int e = 0; e < 8; ++e) raise = raise || s[qb][e] > thr[qb];
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) {
                 const float mt = fmaxf(fmaxf(fmaxf(s[qb][0], s[qb][1]), fmaxf(s[qb][2], s[qb][3])),
                                        fmaxf(fmaxf(s[qb][4], s[qb][5]), fmaxf(s[qb][6], s[qb][7])));
-                const float mn = fmaxf(m[qb], column_max(mt));
+                const float mn = fmaxf(m[qb], column_max(mt) * c);
                 const float alpha = fast_exp2(m[qb] - (mn == kNegInfP ? 0.0f : mn));
                 m[qb] = mn;
+                thr[qb] = (mn + kLazy) * inv_c;
                 l[qb] *= alpha;
 #pragma unroll
                 for (int tn = 0; tn < DT; ++tn)
@@ -435,7 +436,7 @@ prefill_attn_kernel(const PrefillParams p) {
             const float ms = m[qb] == kNegInfP ? 0.0f : m[qb];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                s[qb][e] = fast_exp2(s[qb][e] - ms);
+                s[qb][e] = fast_exp2(__builtin_fmaf(s[qb][e], c, -ms));
                 l[qb] += s[qb][e];
             }
             split_weights<KV>(s[qb], ph[qb], pl[qb]);
@@ -460,6 +461,10 @@ prefill_attn_kernel(const PrefillParams p) {
         for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) scur[qb][h2] = snext[qb][h2];
+        if constexpr (BIAS) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) scur[kQB][h2] = snext[kQB][h2];
+        }
     };
     for (int j0 = 0; j0 < nsteps; j0 += 4) {
         step(j0, std::integral_constant<int, 0>{});
@@ -506,10 +511,13 @@ hipError_t launch_append_t(const PrefillParams& p, hipStream_t s) {
 template <int KV, int D>
 hipError_t launch_attention_t(const PrefillParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.B * p.H), (p.S + kPQ - 1) / kPQ);
-    if (p.block_table)
-        hipLaunchKernelGGL((prefill_attn_kernel<KV, D, true>), grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((prefill_attn_kernel<KV, D, false>), grid, dim3(256), 0, s, p);
+    if (p.block_table) {
+        if (p.bias) hipLaunchKernelGGL((prefill_attn_kernel<KV, D, true, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((prefill_attn_kernel<KV, D, true, false>), grid, dim3(256), 0, s, p);
+    } else {
+        if (p.bias) hipLaunchKernelGGL((prefill_attn_kernel<KV, D, false, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((prefill_attn_kernel<KV, D, false, false>), grid, dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -209,9 +209,11 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
  * or 128; S <= max_seq_len.  A sequence whose length lies outside [1, S] is
  * not appended and gets NaN rows.  Two kernels are enqueued (append, then
  * attention).  The attention runs on the matrix cores with fp32
- * accumulation; the query (bias added and scale folded in, in fp32) and the
- * softmax weights enter as hi and lo halves, so about 22 (fp16) or 16
- * (bf16) bits of each reach the accumulators.  Limits: batch up to 65535,
+ * accumulation: the query enters exactly as stored and the bias term
+ * b_q . k separately (once per key and head), so the scores are exact
+ * products summed in fp32 and then scaled; the softmax weights enter as hi
+ * and lo halves, so about 22 (fp16) or 16 (bf16) bits of each reach the
+ * accumulators.  Limits: batch up to 65535,
  * batch * n_heads below 2^31, prompt_len up to 65535 * 128.  Errors as for
  * ftm_decode_mha.
  */
