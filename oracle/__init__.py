@@ -208,7 +208,7 @@ def qkv_proj(x, w, bias, n_heads, n_kv_heads, head_dim, act_dtype):
 
 
 def prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, n_heads, n_kv_heads,
-                head_dim, kv_dtype):
+                head_dim, kv_dtype, kv_scales=None):
     """Prefill: the whole prompt of every sequence in one step.  Writes the
     prompt's K/V rows into the cache in place and returns out[B, S, H, D]
     float64 (rows past a sequence's prompt are 0).
@@ -218,27 +218,34 @@ def prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, n_heads, 
     S_b, position t of every query head attends to positions [0, t] of its
     KV head, causally.  Each position is what a decode step at length t + 1
     computes, with the same readings: the bias added in fp32 before the K/V
-    rows are stored (rounded to the cache type), the stored rows used in the
-    attention, the query with its bias unrounded, scale 1/sqrt(D), the
-    maximum subtracted before exp.
+    rows are stored (rounded to the cache type, or quantised to INT8 codes
+    with one fp32 scale per row by the decode step's rule), the stored rows
+    used in the attention (code x scale for INT8), the query with its bias
+    unrounded, scale 1/sqrt(D), the maximum subtracted before exp.
 
     Layouts: q [B, S, H, D]; k_new, v_new [B, S, Hkv, D]; qkv_bias
     [(H + 2 Hkv) D] or None; caches [B, Hkv, Lmax, D] with Lmax >= S;
-    seq_lens [B] int32 (1 <= S_b <= S) or None for every S_b = S.  fp16 and
-    bf16 caches (bf16 as uint16 bit patterns)."""
+    seq_lens [B] int32 (1 <= S_b <= S) or None for every S_b = S.  fp16,
+    bf16 (as uint16 bit patterns) and INT8 caches; with INT8 the
+    activations are fp16 and kv_scales float32 [2, B, Hkv, Lmax] (K first)
+    is written in place."""
     import torch
-    if kv_dtype not in ("f16", "bf16"):
-        raise ValueError("prefill takes fp16 or bf16")
+    if kv_dtype not in ("f16", "bf16", "i8"):
+        raise ValueError("prefill takes fp16, bf16 or INT8 caches")
+    i8 = kv_dtype == "i8"
+    if i8 and kv_scales is None:
+        raise ValueError("an INT8 cache needs kv_scales")
+    act = act_dtype_of(kv_dtype)
     B, S, H, D = q.shape
     Hkv = n_kv_heads
     G = H // Hkv
     if H != n_heads or D != head_dim or k_new.shape != (B, S, Hkv, D):
         raise ValueError("shapes do not match n_heads / n_kv_heads / head_dim")
     lens = np.full(B, S) if seq_lens is None else np.asarray(seq_lens, dtype=np.int64)
-    tdt = torch.float16 if kv_dtype == "f16" else torch.bfloat16
+    tdt = torch.float16 if act == "f16" else torch.bfloat16
 
     def f32(a):
-        return torch.from_numpy(cache_to_f64(np.asarray(a), kv_dtype).astype(np.float32))
+        return torch.from_numpy(cache_to_f64(np.asarray(a), act).astype(np.float32))
 
     bias = None if qkv_bias is None else f32(qkv_bias)
     out = np.zeros((B, S, H, D), dtype=np.float64)
@@ -252,17 +259,29 @@ def prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, n_heads, 
             x = f32(src[b, :Sb])                              # [Sb, Hkv, D]
             if bias is not None:
                 x = x + bias[(H + which * Hkv) * D:(H + (which + 1) * Hkv) * D].reshape(Hkv, D)
+            if i8:
+                xs = x.numpy()
+                for t in range(Sb):
+                    for j in range(Hkv):
+                        codes, sc = quantize_row_i8(xs[t, j])
+                        cache[b, j, t] = codes
+                        kv_scales[which, b, j, t] = sc
+                continue
             stored = x.to(tdt)                                # round to nearest even
             if kv_dtype == "bf16":
                 cache[b, :, :Sb] = stored.view(torch.int16).numpy().view(np.uint16).transpose(1, 0, 2)
             else:
                 cache[b, :, :Sb] = stored.numpy().transpose(1, 0, 2)
-        K = cache_to_f64(k_cache[b, :, :Sb], kv_dtype)       # [Hkv, Sb, D]
-        V = cache_to_f64(v_cache[b, :, :Sb], kv_dtype)
+        if i8:
+            K = cache_to_f64(k_cache[b, :, :Sb], "i8", kv_scales[0, b, :, :Sb])
+            V = cache_to_f64(v_cache[b, :, :Sb], "i8", kv_scales[1, b, :, :Sb])
+        else:
+            K = cache_to_f64(k_cache[b, :, :Sb], kv_dtype)   # [Hkv, Sb, D]
+            V = cache_to_f64(v_cache[b, :, :Sb], kv_dtype)
         causal = np.tril(np.ones((Sb, Sb), dtype=bool))
         for h in range(H):
             j = h // G
-            qh = cache_to_f64(np.asarray(q[b, :Sb, h]), kv_dtype)
+            qh = cache_to_f64(np.asarray(q[b, :Sb, h]), act)
             if bias is not None:
                 qh = qh + bias[h * D:(h + 1) * D].double().numpy()[None, :]
             s = (qh @ K[j].T) * inv                            # [Sb, Sb]

@@ -74,3 +74,35 @@ def test_identical_keys_give_running_mean(oracle_mod):
     V = oracle_mod.cache_to_f64(vc[0, 0], dt)
     for t in range(S):
         assert np.allclose(out[0, t, 0], V[:t + 1].mean(axis=0), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (6, 2)])
+def test_int8_prefill_is_successive_decode_steps(oracle_mod, H, Hkv):
+    """INT8 cache: the same pin against the decode oracle's INT8 steps (fp16
+    activations, codes and one fp32 scale per stored row); caches and scales
+    must match byte for byte, poison included."""
+    import torch
+    B, D, S, Lmax = 2, 8, 9, 12
+    g = torch.Generator().manual_seed(31 + H)
+    r = lambda *shape: to_np(torch.randn(shape, generator=g).to(torch.float16), "f16")
+    q, kn, vn = r(B, S, H, D), r(B, S, Hkv, D), r(B, S, Hkv, D)
+    bias = r((H + 2 * Hkv) * D)
+    kc = np.full((B, Hkv, Lmax, D), 77, dtype=np.int8)
+    vc = kc.copy()
+    sc = np.full((2, B, Hkv, Lmax), np.nan, dtype=np.float32)
+    kd, vd, sd = kc.copy(), vc.copy(), sc.copy()
+    lens = np.array([S, 5], np.int32)
+    out = oracle_mod.prefill_mha(q, kn, vn, bias, kc, vc, lens, H, Hkv, D, "i8", sc)
+    for t in range(S):
+        step_lens = np.minimum(lens, t + 1).astype(np.int32)
+        idx = np.minimum(t, lens - 1)
+        qt = np.ascontiguousarray(q[np.arange(B), idx])
+        kt = np.ascontiguousarray(kn[np.arange(B), idx])
+        vt = np.ascontiguousarray(vn[np.arange(B), idx])
+        o, _ = oracle_mod.decode_mha(qt, kt, vt, bias, kd, vd, step_lens, int(step_lens.max()), H, Hkv, D, "i8",
+                                     sd)
+        for b in range(B):
+            if lens[b] > t:
+                assert np.allclose(out[b, t], o[b], rtol=1e-12, atol=1e-14), (b, t)
+    assert kd.tobytes() == kc.tobytes() and vd.tobytes() == vc.tobytes()
+    assert np.array_equal(sd, sc, equal_nan=True)
