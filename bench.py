@@ -242,16 +242,18 @@ def run_prefill(args, case):
     print(f"# {case.name}: batch {case.batch} x {case.prompt}-token prompts, {case.n_heads}q/{case.n_kv_heads}kv "
           f"heads x {case.head_dim}, {case.dtype}", file=sys.stderr, flush=True)
     inp = W.make_prefill_inputs(case, dev, poison=False)
-    out = torch.empty((case.batch, case.prompt, case.n_heads, case.head_dim), dtype=W.TORCH_DTYPES[case.dtype],
-                      device=dev)
+    i8 = case.dtype == "i8"                 # INT8 cache: fp16 activations, int8 codes + fp32 row scales
+    out = torch.empty((case.batch, case.prompt, case.n_heads, case.head_dim),
+                      dtype=W.TORCH_DTYPES["f16" if i8 else case.dtype], device=dev)
     if case.page_size:
         inp = W.prefill_to_paged(inp, case, case.page_size)
         call = ftm.ftm_prefill_mha_paged_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"], inp["k_pages"],
                                                   inp["v_pages"], inp["block_table"], inp["seq_lens"], out,
-                                                  stream=stream.cuda_stream)
+                                                  stream=stream.cuda_stream, kv_scales=inp.get("kv_scales"))
     else:
         call = ftm.ftm_prefill_mha_prepared(inp["q"], inp["k_new"], inp["v_new"], inp["bias"], inp["k_cache"],
-                                            inp["v_cache"], inp["seq_lens"], out, stream=stream.cuda_stream)
+                                            inp["v_cache"], inp["seq_lens"], out, stream=stream.cuda_stream,
+                                            kv_scales=inp.get("kv_scales"))
     lens = inp["seq_lens"].cpu().tolist()
     flops = W.prefill_flops(case, lens)
     copy_gbs = device_copy_gbs(dev)
@@ -287,13 +289,14 @@ def run_prefill(args, case):
         "metric": "prefill attention TFLOP/s (causal q.k + p.v, % of the dense fp16/bf16 matrix peak)",
         "value": round(flops * args.steps / elapsed / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16" if i8 else case.dtype,
         "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": f"{case.name}: batch {case.batch} x {case.prompt} tokens, {case.n_heads}q/"
                                f"{case.n_kv_heads}kv heads x {case.head_dim}",
                    "batch": case.batch, "prompt": case.prompt, "n_heads": case.n_heads,
                    "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim,
-                   "cache_layout": f"paged, {case.page_size}-token pages" if case.page_size else "contiguous"},
+                   "cache_layout": f"paged, {case.page_size}-token pages" if case.page_size else "contiguous",
+                   "cache_dtype": case.dtype},
         "tokens_per_s": round(sum(lens) * args.steps / elapsed, 1),
         "gpu_ms_per_step": round(gpu_ms, 5), "flops_per_step": flops, "kernels_per_step": 2,
         "device_copy_GBs": round(copy_gbs, 1),
@@ -321,10 +324,11 @@ def run_prefill(args, case):
         sb = np.concatenate([bb[:G * D], bb[H * D:(H + 1) * D], bb[(H + Hkv) * D:(H + Hkv + 1) * D]])
         runs, total, best = 0, 0.0, float("inf")
         while runs < 2 or (total < args.cpu_budget and runs < 20):
-            kc = np.zeros((1, 1, case.max_seq_len, D), dtype=qh.dtype)
+            kc = np.zeros((1, 1, case.max_seq_len, D), dtype=np.int8 if i8 else qh.dtype)
             vc = kc.copy()
+            sc = np.zeros((2, 1, 1, case.max_seq_len), dtype=np.float32) if i8 else None
             c0 = time.perf_counter()
-            oracle.prefill_mha(qh, kn, vn, sb, kc, vc, None, G, 1, D, case.dtype)
+            oracle.prefill_mha(qh, kn, vn, sb, kc, vc, None, G, 1, D, case.dtype, sc)
             dtm = time.perf_counter() - c0
             best, total, runs = min(best, dtm), total + dtm, runs + 1
         sample_flops = W.prefill_flops(case.with_(batch=1, n_heads=G, n_kv_heads=1))

@@ -576,8 +576,9 @@ namespace {
 // can hold; block_table null for the contiguous cache.
 int prefill_impl(const void* q, const void* k_new, const void* v_new, const void* qkv_bias, void* k_cache,
                  void* v_cache, const int32_t* seq_lens, int batch, int cache_rows, const char* cache_rows_name,
-                 int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, void* out,
-                 void* stream_ptr, const int32_t* block_table, int page_shift, int max_pages, int n_pages) {
+                 int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, float* kv_scales,
+                 void* out, void* stream_ptr, const int32_t* block_table, int page_shift, int max_pages,
+                 int n_pages) {
     if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
         return fail(FTM_ERR_INVALID_ARG, "a required pointer (q, k_new, v_new, k_cache, v_cache, out) is NULL");
     if (batch < 1 || cache_rows < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
@@ -592,8 +593,11 @@ int prefill_impl(const void* q, const void* k_new, const void* v_new, const void
                                              cache_rows_name + "=" + std::to_string(cache_rows) + "]");
     if (kv_dtype < FTM_F32 || kv_dtype > FTM_I8)
         return fail(FTM_ERR_INVALID_ARG, "unknown kv_dtype " + std::to_string(kv_dtype));
-    if (kv_dtype != FTM_F16 && kv_dtype != FTM_BF16)
-        return fail(FTM_ERR_UNSUPPORTED, "prefill takes fp16 or bf16 caches");
+    if (kv_dtype == FTM_F32) return fail(FTM_ERR_UNSUPPORTED, "prefill takes fp16, bf16 or INT8 caches");
+    const bool i8 = kv_dtype == FTM_I8;
+    if (i8 != (kv_scales != nullptr))
+        return fail(FTM_ERR_INVALID_ARG, "kv_scales must be given for an INT8 cache and only then");
+    if (((uintptr_t)kv_scales & 3u) != 0) return fail(FTM_ERR_INVALID_ARG, "kv_scales must be 4-byte aligned");
     {
         const void* vec[] = {q, k_new, v_new, qkv_bias, k_cache, v_cache, out};
         for (const void* v : vec)
@@ -613,21 +617,40 @@ int prefill_impl(const void* q, const void* k_new, const void* v_new, const void
     ftm::PrefillParams p{q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, batch, prompt_len,
                          cache_rows, n_heads, n_kv_heads,
                          (float)(1.4426950408889634 / std::sqrt((double)head_dim)),
-                         block_table, page_shift, max_pages, n_pages};
+                         block_table, page_shift, max_pages, n_pages,
+                         kv_scales, nullptr, nullptr, nullptr, nullptr};
     hipStream_t stream = (hipStream_t)stream_ptr;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (stream && hipStreamIsCapturing(stream, &cs) != hipSuccess)
         return fail(FTM_ERR_HIP, "hipStreamIsCapturing failed");
     const bool capturing = cs != hipStreamCaptureStatusNone;
+    if (i8) {
+        // the staging the attention reads: codes as fp16 and scales, K and V
+        int device = 0;
+        hipError_t e = hipGetDevice(&device);
+        if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+        const size_t rows = (size_t)batch * n_kv_heads * prompt_len;
+        const size_t code_bytes = rows * head_dim * 2;
+        void* ws = nullptr;
+        int st = get_workspace(device, stream, 2 * code_bytes + 2 * rows * sizeof(float), 0, capturing, &ws,
+                               nullptr);
+        if (st != FTM_OK) return st;
+        p.stage_k = ws;
+        p.stage_v = (char*)ws + code_bytes;
+        p.stage_ks = (float*)((char*)ws + 2 * code_bytes);
+        p.stage_vs = p.stage_ks + rows;
+    }
     const auto none = std::pair<hipEvent_t, hipEvent_t>{nullptr, nullptr};
     auto ev = capturing ? none : timing_slot(1);
     if (ev.first) (void)hipEventRecord(ev.first, stream);
-    hipError_t he = ftm::launch_prefill_append(p, kv_dtype, head_dim, stream);
+    hipError_t he = i8 ? ftm::launch_prefill_append_i8(p, head_dim, stream)
+                       : ftm::launch_prefill_append(p, kv_dtype, head_dim, stream);
     if (ev.second) (void)hipEventRecord(ev.second, stream);
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("prefill append launch: ") + hipGetErrorString(he));
     ev = capturing ? none : timing_slot(0);
     if (ev.first) (void)hipEventRecord(ev.first, stream);
-    he = ftm::launch_prefill_attention(p, kv_dtype, head_dim, stream);
+    he = i8 ? ftm::launch_prefill_attention_i8(p, head_dim, stream)
+            : ftm::launch_prefill_attention(p, kv_dtype, head_dim, stream);
     if (ev.second) (void)hipEventRecord(ev.second, stream);
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("prefill attention launch: ") + hipGetErrorString(he));
     g_last_error.clear();
@@ -640,16 +663,18 @@ extern "C" {
 
 int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                     void* k_cache, void* v_cache, const int32_t* seq_lens, int batch, int max_seq_len,
-                    int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, void* out,
-                    void* stream_ptr) {
+                    int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, float* kv_scales,
+                    void* out, void* stream_ptr) {
     return prefill_impl(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len, "max_seq_len",
-                        prompt_len, n_heads, n_kv_heads, head_dim, kv_dtype, out, stream_ptr, nullptr, 0, 0, 0);
+                        prompt_len, n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales, out, stream_ptr, nullptr, 0,
+                        0, 0);
 }
 
 int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                           void* k_pages, void* v_pages, const int32_t* block_table, int n_pages, int page_size,
                           int max_pages_per_seq, const int32_t* seq_lens, int batch, int prompt_len, int n_heads,
-                          int n_kv_heads, int head_dim, int kv_dtype, void* out, void* stream_ptr) {
+                          int n_kv_heads, int head_dim, int kv_dtype, float* kv_scales, void* out,
+                          void* stream_ptr) {
     if (!block_table) return fail(FTM_ERR_INVALID_ARG, "block_table is NULL");
     if (((uintptr_t)block_table & 3u) != 0) return fail(FTM_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
     if (n_pages < 1 || max_pages_per_seq < 1)
@@ -665,8 +690,8 @@ int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, c
     int shift = 0;
     while ((1 << shift) < page_size) ++shift;
     return prefill_impl(q, k_new, v_new, qkv_bias, k_pages, v_pages, seq_lens, batch, (int)cap,
-                        "max_pages_per_seq * page_size", prompt_len, n_heads, n_kv_heads, head_dim, kv_dtype, out,
-                        stream_ptr, block_table, shift, max_pages_per_seq, n_pages);
+                        "max_pages_per_seq * page_size", prompt_len, n_heads, n_kv_heads, head_dim, kv_dtype,
+                        kv_scales, out, stream_ptr, block_table, shift, max_pages_per_seq, n_pages);
 }
 
 int ftm_graph_begin(void* stream) {

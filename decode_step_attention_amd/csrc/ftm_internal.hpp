@@ -84,6 +84,14 @@ struct PrefillParams {
     // t mod P of page block_table[b * max_pages + t / P]
     const int32_t* block_table;
     int page_shift, max_pages, n_pages;
+    // INT8 cache: its scales ([2, B, Hkv, Lmax], or [2, n_pages, Hkv, P]
+    // paged), and the staging the attention reads: the prompt's codes as
+    // fp16 [B, Hkv, S, D] and their scales [B, Hkv, S], K and V
+    float* kv_scales;
+    void* stage_k;
+    void* stage_v;
+    float* stage_ks;
+    float* stage_vs;
 };
 
 hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, int nw, hipStream_t s);
@@ -91,6 +99,10 @@ hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, in
 // The prompt's K/V rows into the cache, then the causal attention over them.
 hipError_t launch_prefill_append(const PrefillParams& p, int kv, int head_dim, hipStream_t s);
 hipError_t launch_prefill_attention(const PrefillParams& p, int kv, int head_dim, hipStream_t s);
+// INT8: the append quantises the prompt's rows into the cache and the
+// staging; the attention then runs on the staging (p.stage_*).
+hipError_t launch_prefill_append_i8(const PrefillParams& p, int head_dim, hipStream_t s);
+hipError_t launch_prefill_attention_i8(const PrefillParams& p, int head_dim, hipStream_t s);
 // act: KV_F16 or KV_BF16; B <= 64, hidden a multiple of 256, (H + 2 Hkv) D a multiple of 16.
 hipError_t launch_qkv_proj(const QkvParams& p, int act, int n_cu, hipStream_t s);
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);

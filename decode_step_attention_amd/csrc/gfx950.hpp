@@ -58,6 +58,12 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
 }
 
+// 4 bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes bytes lds + 4 i .. +3.
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rsrc, void* lds, int voffset, int soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 4, voffset, soffset, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Eight fp16 or bf16 values in a 16-byte vector, as fp32.

@@ -82,6 +82,79 @@ __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams
     }
 }
 
+// INT8 cache: the prompt's rows, bias added in fp32 and quantised by the
+// decode step's rule (s = absmax / 127 by IEEE division, code = rint(x / s)
+// clamped to [-127, 127], a zero row keeps s = 0), into the cache and its
+// scales, and into the staging the attention reads: the codes as fp16 (exact)
+// and the scales, contiguous.  Grid (S, row slices / 256, B): a thread owns
+// 16 elements of one row, the SL threads of a row are adjacent lanes.
+template <int D, bool PG>
+__global__ void __launch_bounds__(256) prefill_append_i8_kernel(const PrefillParams p) {
+    constexpr int SL = D / 16;              // threads per head row
+    const int t = blockIdx.x;
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    const int b = blockIdx.z;
+    if (c >= p.Hkv * SL) return;            // whole rows: Hkv SL is a multiple of SL
+    const int Sb = p.seq_lens ? p.seq_lens[b] : p.S;
+    if (Sb < 1 || Sb > p.S || t >= Sb) return;         // invalid length: no append
+    const int j = c / SL;
+    const int e0 = (c % SL) * 16;
+    const size_t src = (((size_t)b * p.S + t) * p.Hkv + j) * D + e0;
+    // destination row in the cache (-1: a page outside the pool, no append)
+    long long crow;                         // row index in rows of D codes
+    size_t srow;                            // scale index within K's (or V's) half
+    if constexpr (PG) {
+        const int pg = p.block_table[(size_t)b * p.max_pages + (t >> p.page_shift)];
+        const bool ok = pg >= 0 && pg < p.n_pages;
+        const size_t r = (((size_t)(ok ? pg : 0) * p.Hkv + j) << p.page_shift) + (t & ((1 << p.page_shift) - 1));
+        crow = ok ? (long long)r : -1;
+        srow = r;
+    } else {
+        crow = (long long)(((size_t)b * p.Hkv + j) * p.Lmax + t);
+        srow = (size_t)crow;
+    }
+    const size_t half = PG ? (size_t)p.n_pages * p.Hkv << p.page_shift : (size_t)p.B * p.Hkv * p.Lmax;
+    const size_t stage_row = ((size_t)b * p.Hkv + j) * p.S + t;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const uint16_t* in = (const uint16_t*)(which ? p.v_new : p.k_new) + src;
+        float x[16];
+        Elem16<KV_F16>::unpack(*(const u32x4*)in, x);
+        Elem16<KV_F16>::unpack(*(const u32x4*)(in + 8), x + 8);
+        if (p.bias) {
+            const uint16_t* bb = (const uint16_t*)p.bias + (size_t)(p.H + which * p.Hkv + j) * D + e0;
+            float bx[16];
+            Elem16<KV_F16>::unpack(*(const u32x4*)bb, bx);
+            Elem16<KV_F16>::unpack(*(const u32x4*)(bb + 8), bx + 8);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = x[e] + bx[e];   // one fp32 rounding
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+        for (int off = 1; off < SL; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        const float scale = amax / 127.0f;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        uint32_t hq[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float q = 0.0f;
+            if (scale != 0.0f) q = fminf(fmaxf(rintf(x[e] / scale), -127.0f), 127.0f);
+            w[e / 4] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (e % 4));
+            hq[e / 2] |= float_to_half_bits(q) << (16 * (e % 2));
+        }
+        if (crow >= 0) {
+            *(u32x4*)((int8_t*)(which ? p.v_cache : p.k_cache) + (size_t)crow * D + e0) = u32x4{w[0], w[1], w[2], w[3]};
+            if (c % SL == 0) p.kv_scales[which * half + srow] = scale;
+        }
+        uint16_t* st = (uint16_t*)(which ? p.stage_v : p.stage_k) + stage_row * D + e0;
+        *(u32x4*)st = u32x4{hq[0], hq[1], hq[2], hq[3]};
+        *(u32x4*)(st + 8) = u32x4{hq[4], hq[5], hq[6], hq[7]};
+        if (c % SL == 0) (which ? p.stage_vs : p.stage_ks)[stage_row] = scale;
+    }
+}
+
 // hi + lo halves of eight softmax weights (0 <= x <= 2^kLazy): hi keeps the
 // leading 11 (fp16) or 8 (bf16) significant bits by truncation, so it
 // converts exactly (for x at least 2^-14 in fp16) and the fp32 residual
@@ -103,7 +176,11 @@ __device__ __forceinline__ void split_weights(const float* x, typename Mfma<KV>:
     }
 }
 
-template <int KV, int D, bool PG, bool BIAS>
+// SC: the K/V rows are INT8 codes staged as fp16 (p.k_cache / p.v_cache
+// point at the staging, p.Lmax = S) with one scale per key: each raw score
+// is multiplied by its key's K scale and each weight, for O only, by its
+// key's V scale (the sum of the weights is taken unscaled).
+template <int KV, int D, bool PG, bool BIAS, bool SC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_attn_kernel(const PrefillParams p) {
     using MF = Mfma<KV>;
@@ -128,6 +205,13 @@ prefill_attn_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char vtile0[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char ktile1[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char vtile1[TILE];
+    // SC: each wave's own copy of a tile's 64 key scales (one 4-byte load
+    // per lane), loaded with the K (or V) tile
+    constexpr int SCB = SC ? 4 * 64 * 4 : 16;
+    __shared__ __attribute__((aligned(16))) unsigned char kscl0[SCB];
+    __shared__ __attribute__((aligned(16))) unsigned char vscl0[SCB];
+    __shared__ __attribute__((aligned(16))) unsigned char kscl1[SCB];
+    __shared__ __attribute__((aligned(16))) unsigned char vscl1[SCB];
     auto kswz = [](int r) { return (r * NCH / 16) & (NCH - 1); };
     auto vswz = [](int r) { return 2 * ((r * NCH / 16) & (NCH / 2 - 1)); };
 
@@ -160,8 +244,10 @@ prefill_attn_kernel(const PrefillParams p) {
         return;
     }
     if (t0 >= Sb) return;                   // past the prompt: nothing to do
-    if constexpr (PG) {
-        // a page outside the pool among the sequence's pages: NaN rows
+    if (PG || (SC && p.block_table != nullptr)) {
+        // a page outside the pool among the sequence's pages: NaN rows (the
+        // staged INT8 path reads contiguous staging but keeps the table for
+        // this check)
         const int npg = (Sb + (1 << p.page_shift) - 1) >> p.page_shift;
         bool bad = false;
         for (int i = lane; i < npg; i += 64) {
@@ -187,6 +273,9 @@ prefill_attn_kernel(const PrefillParams p) {
     const size_t row0 = PG ? 0 : ((size_t)b * p.Hkv + j) * p.Lmax;
     const auto krs = make_rsrc((const char*)p.k_cache + row0 * ROW, (uint32_t)kend * ROW);
     const auto vrs = make_rsrc((const char*)p.v_cache + row0 * ROW, (uint32_t)kend * ROW);
+    const size_t srow0 = ((size_t)b * p.Hkv + j) * p.Lmax;
+    const auto ksr = make_rsrc(SC ? (const char*)(p.stage_ks + srow0) : nullptr, SC ? (uint32_t)kend * 4 : 0u);
+    const auto vsr = make_rsrc(SC ? (const char*)(p.stage_vs + srow0) : nullptr, SC ? (uint32_t)kend * 4 : 0u);
     // one 64-key tile of K or V into LDS: NI loads per lane; load u of this
     // wave fills tile bytes base(u) .. +1023, lane i bytes base + 16 i .. +15,
     // which hold chunk slot ^ swz(row) of cache row k0 + row
@@ -208,7 +297,9 @@ prefill_attn_kernel(const PrefillParams p) {
     static_assert(NI * (1024 / ROW) == 16, "a wave loads 16 rows per tile");
     const __attribute__((address_space(4))) int32_t* tbl =
         (const __attribute__((address_space(4))) int32_t*)(PG ? p.block_table + (size_t)b * p.max_pages : nullptr);
-    auto issue = [&](const bool is_v, int k0, unsigned char* dst, const int* offs) {
+    auto issue = [&](const bool is_v, int k0, unsigned char* dst, const int* offs, unsigned char* sdst) {
+        if constexpr (SC)
+            buffer_load_lds4(is_v ? vsr : ksr, sdst + wave * 256, lane * 4, __builtin_amdgcn_readfirstlane(k0 * 4));
         if constexpr (!PG) {
             const auto rs = is_v ? vrs : krs;
             const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * ROW));
@@ -252,9 +343,9 @@ prefill_attn_kernel(const PrefillParams p) {
         for (int kk = 0; kk < KK; ++kk)
             qraw[qb][kk] = *(const u32x4*)((const uint16_t*)p.q + (((size_t)b * p.S + tc) * p.H + h) * D + 32 * kk + 8 * g);
     }
-    issue(false, 0, ktile0, koffs);
-    issue(true, 0, vtile0, voffs);
-    issue(false, kPK, ktile1, koffs);
+    issue(false, 0, ktile0, koffs, kscl0);
+    issue(true, 0, vtile0, voffs, vscl0);
+    issue(false, kPK, ktile1, koffs, kscl1);
     vec8 qv[kQB][KK], bv[KK];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
@@ -317,7 +408,8 @@ prefill_attn_kernel(const PrefillParams p) {
     // s_waitcnt vmcnt(NI): the gfx9 encoding puts vmcnt in bits 3:0, expcnt
     // (7) in 6:4 and lgkmcnt (15) in 11:8; through the builtin the compiler
     // sees the wait too.
-    auto wait_one_batch_behind = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70 | NI); };
+    constexpr int NB = NI + (SC ? 1 : 0);  // loads per lane per refill
+    auto wait_one_batch_behind = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70 | NB); };
     // A workgroup barrier for LDS that leaves the newest tile loads in
     // flight (__syncthreads would wait for every load into LDS): this wave's
     // LDS accesses complete (lgkmcnt(0); vmcnt 63, expcnt 7 untouched), then
@@ -356,11 +448,29 @@ prefill_attn_kernel(const PrefillParams p) {
         }
     };
 
+    // SC: the key's K scale goes on its raw score (bias term included) as
+    // soon as the scores are complete, while K's scale buffer still holds
+    // that tile (the odd step after refills it); slot kQB is then unused
+    auto fold_k_scale = [&](Scores& sa, const unsigned char* sbuf, int half) {
+        const float* ks = (const float*)(sbuf + wave * 256) + 32 * half + 4 * g;
+        const f32x4 k0s = *(const f32x4*)ks, k1s = *(const f32x4*)(ks + 16);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sa[qb][0][i] = (BIAS ? sa[qb][0][i] + sa[kQB][0][i] : sa[qb][0][i]) * k0s[i];
+                sa[qb][1][i] = (BIAS ? sa[qb][1][i] + sa[kQB][1][i] : sa[qb][1][i]) * k1s[i];
+            }
+    };
+
     Scores scur, snext;
     __builtin_amdgcn_s_waitcnt(0x0F70);     // the first tiles (and the query) landed
     __syncthreads();
     clear_v_tail(0, vtile0);
-    if (0 <= last_j) qk(scur, ktile0, 0);
+    if (0 <= last_j) {
+        qk(scur, ktile0, 0);
+        if constexpr (SC) fold_k_scale(scur, kscl0, 0);
+    }
 
     // step j = j0 + U of a 4-step (two-tile) group: buffers by U
     auto step = [&](const int j0, auto U) {
@@ -375,12 +485,12 @@ prefill_attn_kernel(const PrefillParams p) {
                 lds_barrier();
                 clear_v_tail(T, vt);
             }
-            issue(true, T * kPK + kPK, (u / 2) ? vtile0 : vtile1, voffs);
+            issue(true, T * kPK + kPK, (u / 2) ? vtile0 : vtile1, voffs, (u / 2) ? vscl0 : vscl1);
         } else {
             // K(T + 1) must have landed; K(T)'s buffer is free for K(T + 2)
             wait_one_batch_behind();        // V(T + 1) was issued after K(T + 1)
             lds_barrier();
-            issue(false, T * kPK + 2 * kPK, (u / 2) ? ktile1 : ktile0, koffs);
+            issue(false, T * kPK + 2 * kPK, (u / 2) ? ktile1 : ktile0, koffs, (u / 2) ? kscl1 : kscl0);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (j > last_j) return;
@@ -393,7 +503,7 @@ prefill_attn_kernel(const PrefillParams p) {
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    s[qb][4 * h2 + i] = BIAS ? scur[qb][h2][i] + scur[kQB][h2][i] : scur[qb][h2][i];
+                    s[qb][4 * h2 + i] = BIAS && !SC ? scur[qb][h2][i] + scur[kQB][h2][i] : scur[qb][h2][i];
         if (j == last_j) {                  // the diagonal step: causal mask (also covers
                                             // keys past the prompt)
 #pragma unroll
@@ -439,6 +549,15 @@ prefill_attn_kernel(const PrefillParams p) {
                 s[qb][e] = fast_exp2(__builtin_fmaf(s[qb][e], c, -ms));
                 l[qb] += s[qb][e];
             }
+            if constexpr (SC) {             // code x scale: the key's V scale on its weight
+                const float* vs = (const float*)(((u / 2) ? vscl1 : vscl0) + wave * 256) + 32 * (j % 2) + 4 * g;
+                const f32x4 v0s = *(const f32x4*)vs, v1s = *(const f32x4*)(vs + 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s[qb][i] *= v0s[i];
+                    s[qb][4 + i] *= v1s[i];
+                }
+            }
             split_weights<KV>(s[qb], ph[qb], pl[qb]);
         }
         // O^T += V^T P^T: A = V^T (row 16 tn + n, the slots' keys, read
@@ -457,11 +576,12 @@ prefill_attn_kernel(const PrefillParams p) {
                 acc[qb][tn] = MF::mma32(va, pl[qb], acc[qb][tn]);
             }
         }
+        if constexpr (SC) fold_k_scale(snext, (u == 0 || u == 3) ? kscl0 : kscl1, (j + 1) % 2);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) scur[qb][h2] = snext[qb][h2];
-        if constexpr (BIAS) {
+        if constexpr (BIAS && !SC) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) scur[kQB][h2] = snext[kQB][h2];
         }
@@ -512,16 +632,48 @@ template <int KV, int D>
 hipError_t launch_attention_t(const PrefillParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.B * p.H), (p.S + kPQ - 1) / kPQ);
     if (p.block_table) {
-        if (p.bias) hipLaunchKernelGGL((prefill_attn_kernel<KV, D, true, true>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((prefill_attn_kernel<KV, D, true, false>), grid, dim3(256), 0, s, p);
+        if (p.bias) hipLaunchKernelGGL((prefill_attn_kernel<KV, D, true, true, false>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((prefill_attn_kernel<KV, D, true, false, false>), grid, dim3(256), 0, s, p);
     } else {
-        if (p.bias) hipLaunchKernelGGL((prefill_attn_kernel<KV, D, false, true>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((prefill_attn_kernel<KV, D, false, false>), grid, dim3(256), 0, s, p);
+        if (p.bias) hipLaunchKernelGGL((prefill_attn_kernel<KV, D, false, true, false>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((prefill_attn_kernel<KV, D, false, false, false>), grid, dim3(256), 0, s, p);
     }
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_append_i8_t(const PrefillParams& p, hipStream_t s) {
+    const dim3 grid((unsigned)p.S, (unsigned)((p.Hkv * (D / 16) + 255) / 256), (unsigned)p.B);
+    if (p.block_table)
+        hipLaunchKernelGGL((prefill_append_i8_kernel<D, true>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_append_i8_kernel<D, false>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// the attention over the INT8 staging: contiguous rows of S positions,
+// fp16 codes with per-key scales
+template <int D>
+hipError_t launch_attention_i8_t(const PrefillParams& p0, hipStream_t s) {
+    PrefillParams p = p0;
+    p.k_cache = p.stage_k;
+    p.v_cache = p.stage_v;
+    p.Lmax = p.S;                           // block_table stays: the page check
+    const dim3 grid((unsigned)(p.B * p.H), (p.S + kPQ - 1) / kPQ);
+    if (p.bias) hipLaunchKernelGGL((prefill_attn_kernel<KV_F16, D, false, true, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((prefill_attn_kernel<KV_F16, D, false, false, true>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_prefill_append_i8(const PrefillParams& p, int head_dim, hipStream_t s) {
+    return head_dim == 64 ? launch_append_i8_t<64>(p, s) : launch_append_i8_t<128>(p, s);
+}
+
+hipError_t launch_prefill_attention_i8(const PrefillParams& p, int head_dim, hipStream_t s) {
+    return head_dim == 64 ? launch_attention_i8_t<64>(p, s) : launch_attention_i8_t<128>(p, s);
+}
 
 hipError_t launch_prefill_append(const PrefillParams& p, int kv, int head_dim, hipStream_t s) {
     if (kv == KV_F16) return head_dim == 64 ? launch_append_t<KV_F16, 64>(p, s) : launch_append_t<KV_F16, 128>(p, s);

@@ -46,10 +46,10 @@ def _load() -> ctypes.CDLL:
     lib.ftm_decode_mha_paged.restype = i32
     lib.ftm_qkv_proj.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.ftm_qkv_proj.restype = i32
-    lib.ftm_prefill_mha.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.ftm_prefill_mha.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.ftm_prefill_mha.restype = i32
     lib.ftm_prefill_mha_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, i32,
-                                          i32, vp, vp]
+                                          i32, vp, vp, vp]
     lib.ftm_prefill_mha_paged.restype = i32
     lib.ftm_graph_begin.argtypes = [vp]
     lib.ftm_graph_begin.restype = i32
@@ -299,80 +299,93 @@ def ftm_qkv_proj_prepared(x, w, bias, q, k_new, v_new, stream=None) -> Callable[
     return _prepared(lib.ftm_qkv_proj, args, (x, w, bias, q, k_new, v_new))
 
 
-def _marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream):
+def _prefill_types(cache):
+    kv = _TORCH_TO_KV.get(cache.dtype)
+    if kv is None:
+        raise TypeError(f"unsupported cache dtype {cache.dtype}")
+    act = torch.float16 if cache.dtype == torch.int8 else cache.dtype
+    return kv, act
+
+
+def _marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream, kv_scales=None):
     if q.dim() != 4 or k_cache.dim() != 4:
         raise ValueError("q must be [B, S, H, D] and the caches [B, Hkv, Lmax, D]")
     B, S, H, D = q.shape
     _, Hkv, Lmax, _ = k_cache.shape
-    kv = _TORCH_TO_KV.get(k_cache.dtype)
-    if kv is None:
-        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
-    dt = k_cache.dtype
-    tensors = {"q": (q, dt, (B, S, H, D)), "k_new": (k_new, dt, (B, S, Hkv, D)),
-               "v_new": (v_new, dt, (B, S, Hkv, D)), "k_cache": (k_cache, dt, (B, Hkv, Lmax, D)),
-               "v_cache": (v_cache, dt, (B, Hkv, Lmax, D)), "out": (out, dt, (B, S, H, D))}
+    kv, act = _prefill_types(k_cache)
+    tensors = {"q": (q, act, (B, S, H, D)), "k_new": (k_new, act, (B, S, Hkv, D)),
+               "v_new": (v_new, act, (B, S, Hkv, D)), "k_cache": (k_cache, k_cache.dtype, (B, Hkv, Lmax, D)),
+               "v_cache": (v_cache, k_cache.dtype, (B, Hkv, Lmax, D)), "out": (out, act, (B, S, H, D))}
     if qkv_bias is not None:
-        tensors["qkv_bias"] = (qkv_bias, dt, ((H + 2 * Hkv) * D,))
+        tensors["qkv_bias"] = (qkv_bias, act, ((H + 2 * Hkv) * D,))
     if seq_lens is not None:
         tensors["seq_lens"] = (seq_lens, torch.int32, (B,))
+    if kv_scales is not None:
+        tensors["kv_scales"] = (kv_scales, torch.float32, (2, B, Hkv, Lmax))
     _check_tensors(tensors, k_cache.device)
     return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_cache), _ptr(v_cache),
-            _ptr(seq_lens), B, Lmax, S, H, Hkv, D, kv, _ptr(out), _stream_ptr(stream, k_cache.device))
+            _ptr(seq_lens), B, Lmax, S, H, Hkv, D, kv, _ptr(kv_scales), _ptr(out),
+            _stream_ptr(stream, k_cache.device))
 
 
-def ftm_prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream=None) -> None:
+def ftm_prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream=None,
+                    kv_scales=None) -> None:
     """Prefill (see include/ftm.h): q/out [B, S, H, D], k_new/v_new
-    [B, S, Hkv, D], caches [B, Hkv, Lmax, D], seq_lens int32 [B] or None."""
+    [B, S, Hkv, D], caches [B, Hkv, Lmax, D], seq_lens int32 [B] or None;
+    an int8 cache takes fp16 activations and kv_scales fp32 [2, B, Hkv, Lmax]."""
     _check(lib.ftm_prefill_mha(*_marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens,
-                                                 out, stream)))
+                                                 out, stream, kv_scales)))
 
 
 def ftm_prefill_mha_prepared(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out,
-                             stream=None) -> Callable[[], None]:
+                             stream=None, kv_scales=None) -> Callable[[], None]:
     """ftm_prefill_mha with the arguments marshalled once."""
-    args = _marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream)
-    return _prepared(lib.ftm_prefill_mha, args, (q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out))
+    args = _marshal_prefill(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, stream, kv_scales)
+    return _prepared(lib.ftm_prefill_mha, args,
+                     (q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, kv_scales))
 
 
-def _marshal_prefill_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, stream):
+def _marshal_prefill_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, stream,
+                           kv_scales=None):
     if q.dim() != 4 or k_pages.dim() != 4 or block_table.dim() != 2:
         raise ValueError("q must be [B, S, H, D], the pools [n_pages, Hkv, P, D] and block_table "
                          "[B, max_pages_per_seq]")
     B, S, H, D = q.shape
     n_pages, Hkv, P, _ = k_pages.shape
     max_pages = block_table.shape[1]
-    kv = _TORCH_TO_KV.get(k_pages.dtype)
-    if kv is None:
-        raise TypeError(f"unsupported cache dtype {k_pages.dtype}")
-    dt = k_pages.dtype
-    tensors = {"q": (q, dt, (B, S, H, D)), "k_new": (k_new, dt, (B, S, Hkv, D)),
-               "v_new": (v_new, dt, (B, S, Hkv, D)), "k_pages": (k_pages, dt, (n_pages, Hkv, P, D)),
-               "v_pages": (v_pages, dt, (n_pages, Hkv, P, D)), "block_table": (block_table, torch.int32, (B, max_pages)),
-               "out": (out, dt, (B, S, H, D))}
+    kv, act = _prefill_types(k_pages)
+    tensors = {"q": (q, act, (B, S, H, D)), "k_new": (k_new, act, (B, S, Hkv, D)),
+               "v_new": (v_new, act, (B, S, Hkv, D)), "k_pages": (k_pages, k_pages.dtype, (n_pages, Hkv, P, D)),
+               "v_pages": (v_pages, k_pages.dtype, (n_pages, Hkv, P, D)),
+               "block_table": (block_table, torch.int32, (B, max_pages)), "out": (out, act, (B, S, H, D))}
     if qkv_bias is not None:
-        tensors["qkv_bias"] = (qkv_bias, dt, ((H + 2 * Hkv) * D,))
+        tensors["qkv_bias"] = (qkv_bias, act, ((H + 2 * Hkv) * D,))
     if seq_lens is not None:
         tensors["seq_lens"] = (seq_lens, torch.int32, (B,))
+    if kv_scales is not None:
+        tensors["kv_scales"] = (kv_scales, torch.float32, (2, n_pages, Hkv, P))
     _check_tensors(tensors, k_pages.device)
     return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(qkv_bias), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
-            n_pages, P, max_pages, _ptr(seq_lens), B, S, H, Hkv, D, kv, _ptr(out),
+            n_pages, P, max_pages, _ptr(seq_lens), B, S, H, Hkv, D, kv, _ptr(kv_scales), _ptr(out),
             _stream_ptr(stream, k_pages.device))
 
 
 def ftm_prefill_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out,
-                          stream=None) -> None:
+                          stream=None, kv_scales=None) -> None:
     """Prefill into a paged cache (see include/ftm.h): pools [n_pages, Hkv, P, D],
-    block_table int32 [B, max_pages_per_seq], the rest as ftm_prefill_mha."""
+    block_table int32 [B, max_pages_per_seq], kv_scales fp32 [2, n_pages, Hkv, P]
+    for an int8 pool, the rest as ftm_prefill_mha."""
     _check(lib.ftm_prefill_mha_paged(*_marshal_prefill_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages,
-                                                             block_table, seq_lens, out, stream)))
+                                                             block_table, seq_lens, out, stream, kv_scales)))
 
 
 def ftm_prefill_mha_paged_prepared(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out,
-                                   stream=None) -> Callable[[], None]:
+                                   stream=None, kv_scales=None) -> Callable[[], None]:
     """ftm_prefill_mha_paged with the arguments marshalled once."""
-    args = _marshal_prefill_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, stream)
+    args = _marshal_prefill_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, stream,
+                                  kv_scales)
     return _prepared(lib.ftm_prefill_mha_paged, args,
-                     (q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out))
+                     (q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, out, kv_scales))
 
 
 def ftm_graph_begin(stream: int) -> None:

@@ -334,24 +334,37 @@ PREFILL_CASES: Dict[str, PrefillCase] = {
     "prefill_gqa": PrefillCase("prefill_gqa", 4, 2048, 64, 8, 128, "bf16", 2048, seed=3003),
     "prefill_7b_paged": PrefillCase("prefill_7b_paged", 4, 2048, 32, 32, 128, "f16", 2048, seed=3001,
                                     page_size=256),
+    # the INT8 decode workload's layer (40 heads x 128, fp16 activations)
+    "prefill_int8": PrefillCase("prefill_int8", 4, 2048, 40, 40, 128, "i8", 2048, seed=3005),
 }
 
 
 def make_prefill_inputs(case: PrefillCase, device="cpu", poison: bool = True) -> Dict[str, torch.Tensor]:
-    """Inputs of one prefill step; caches are NaN (poison) or zero before it."""
+    """Inputs of one prefill step; caches are NaN (poison) or zero before it.
+
+    INT8 caches follow the INT8 decode workload: fp16 activations drawn
+    N(0, 1) without the 1/sqrt(D) factor, codes poisoned with 99 and
+    ``kv_scales`` [2, B, Hkv, Lmax] with NaN (or all zero)."""
     dt = TORCH_DTYPES[case.dtype]
+    i8 = case.dtype == "i8"
+    act = torch.float16 if i8 else dt
     B, S, H, Hkv, D = case.batch, case.prompt, case.n_heads, case.n_kv_heads, case.head_dim
+    scale = 1.0 if i8 else 1.0 / math.sqrt(D)
 
     def draw(tag, shape):
         g = torch.Generator(device=device)
         g.manual_seed((case.seed * 1_000_003 + tag * 10_007) % (2 ** 62))
-        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) / math.sqrt(D)).to(dt)
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * scale).to(act)
 
     t = {"q": draw(1, (B, S, H, D)), "k_new": draw(2, (B, S, Hkv, D)), "v_new": draw(3, (B, S, Hkv, D)),
          "bias": draw(4, ((H + 2 * Hkv) * D,))}
     fill = float("nan") if poison else 0.0
-    t["k_cache"] = torch.full((B, Hkv, case.max_seq_len, D), fill, dtype=dt, device=device)
-    t["v_cache"] = torch.full_like(t["k_cache"], fill)
+    if i8:
+        t["k_cache"] = torch.full((B, Hkv, case.max_seq_len, D), 99 if poison else 0, dtype=dt, device=device)
+        t["kv_scales"] = torch.full((2, B, Hkv, case.max_seq_len), fill, dtype=torch.float32, device=device)
+    else:
+        t["k_cache"] = torch.full((B, Hkv, case.max_seq_len, D), fill, dtype=dt, device=device)
+    t["v_cache"] = torch.full_like(t["k_cache"], t["k_cache"].flatten()[0].item())
     if case.lens is None:
         L = torch.full((B,), S, dtype=torch.int32)
     else:
@@ -389,6 +402,9 @@ def prefill_to_paged(t: Dict[str, torch.Tensor], case: PrefillCase, page_size: i
     t["k_pages"] = torch.full((n_pages, Hkv, P, D), fill, dtype=k.dtype, device=k.device)
     t["v_pages"] = torch.full_like(t["k_pages"], fill)
     t["block_table"] = table.to(k.device)
+    if "kv_scales" in t:                    # INT8: the scale pool [2, n_pages, Hkv, P]
+        sfill = t.pop("kv_scales").flatten()[0].item()
+        t["kv_scales"] = torch.full((2, n_pages, Hkv, P), sfill, dtype=torch.float32, device=k.device)
     return t
 
 
@@ -396,6 +412,8 @@ def prefill_append_bytes(case: PrefillCase, lens: Optional[List[int]] = None) ->
     """Bytes the append moves: every prompt row of K and V read once (bias
     aside) and written once to the cache."""
     L = [case.prompt] * case.batch if lens is None else list(lens)
+    if case.dtype == "i8":                  # fp16 rows in, codes and one fp32 scale per row out
+        return sum(L) * case.n_kv_heads * (case.head_dim * 3 + 4) * 2
     return sum(L) * case.n_kv_heads * case.head_dim * ELEM_BYTES[case.dtype] * 2 * 2
 
 

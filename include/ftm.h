@@ -205,9 +205,18 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
  *   k_cache, v_cache [batch, n_kv_heads, max_seq_len, D]  rows [0, S_b) written
  *   seq_lens  [batch] int32 prompt lengths S_b in [1, S], or NULL (all S)
  *   out       [batch, S, n_heads, D]      rows t < S_b written, the rest untouched
- * kv_dtype FTM_F16 or FTM_BF16 (activations of the same type); head_dim 64
- * or 128; S <= max_seq_len.  A sequence whose length lies outside [1, S] is
- * not appended and gets NaN rows.  Two kernels are enqueued (append, then
+ * kv_dtype FTM_F16 or FTM_BF16 (activations of the same type) or FTM_I8
+ * (fp16 activations); head_dim 64 or 128; S <= max_seq_len.  A sequence
+ * whose length lies outside [1, S] is not appended and gets NaN rows.
+ *
+ * INT8 cache: kv_scales [2, batch, n_kv_heads, max_seq_len] fp32 (K first),
+ * NULL otherwise.  Each prompt row is quantised as a decode step quantises
+ * its new row (s = absmax / 127, code = round-to-nearest-even of x / s
+ * clamped to [-127, 127]) and the attention uses code x scale, as decode
+ * does.  The library then stages the prompt's codes (as fp16) and scales
+ * in its per-stream workspace (4 batch n_kv_heads S (head_dim + 2) bytes),
+ * allocated on the first call of a larger shape; under stream capture a
+ * call that would grow it is refused, as for ftm_decode_mha.  Two kernels are enqueued (append, then
  * attention).  The attention runs on the matrix cores with fp32
  * accumulation: the query enters exactly as stored and the bias term
  * b_q . k separately (once per key and head), so the scores are exact
@@ -220,7 +229,7 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
 int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                     void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
                     int max_seq_len, int prompt_len, int n_heads, int n_kv_heads, int head_dim,
-                    int kv_dtype, void* out, void* stream);
+                    int kv_dtype, float* kv_scales, void* out, void* stream);
 
 /*
  * ftm_prefill_mha_paged -- prefill into a paged KV cache.
@@ -239,6 +248,8 @@ int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const v
  * * page_size.  A table entry outside [0, n_pages) among the pages of
  * positions [0, S_b) makes the sequence's output rows [0, S_b) NaN, and no
  * row is appended into such a page (the rows of its valid pages are).
+ * INT8: kv_scales [2, n_pages, n_kv_heads, page_size] fp32 (K first), the
+ * scales of the pooled rows, in the layout ftm_decode_mha_paged reads.
  * Everything else (shapes of q, k_new, v_new, qkv_bias, seq_lens, out,
  * numerics, limits, errors, the two kernels) is ftm_prefill_mha's.
  */
@@ -246,7 +257,7 @@ int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, c
                           void* k_pages, void* v_pages, const int32_t* block_table, int n_pages,
                           int page_size, int max_pages_per_seq, const int32_t* seq_lens, int batch,
                           int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
-                          void* out, void* stream);
+                          float* kv_scales, void* out, void* stream);
 
 /* ---- HIP graphs ----------------------------------------------------------
  * A decode step of a model is one call per layer on fixed buffers; its

@@ -294,7 +294,7 @@ def prefill_mha(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, n_heads, 
 
 
 def prefill_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, seq_lens, n_heads,
-                      n_kv_heads, head_dim, kv_dtype):
+                      n_kv_heads, head_dim, kv_dtype, kv_scales=None):
     """Prefill into a paged cache: writes the prompt's K/V rows into their
     pages in place and returns out[B, S, H, D] float64.
 
@@ -310,7 +310,8 @@ def prefill_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, 
     only the rows whose page is valid are appended.
 
     Layouts: k_pages/v_pages [n_pages, Hkv, P, D]; block_table int32
-    [B, max_pages] with max_pages P >= S."""
+    [B, max_pages] with max_pages P >= S; INT8: kv_scales float32
+    [2, n_pages, Hkv, P] (K first), written with the codes."""
     n_pages, Hkv, P, D = k_pages.shape
     B, S = q.shape[0], q.shape[1]
     _, max_pages = block_table.shape
@@ -321,7 +322,8 @@ def prefill_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, 
     lens = np.full(B, S) if seq_lens is None else np.asarray(seq_lens, dtype=np.int64)
     kc = np.zeros((B, Hkv, S, D), dtype=k_pages.dtype)
     vc = np.zeros_like(kc)
-    out = prefill_mha(q, k_new, v_new, qkv_bias, kc, vc, seq_lens, n_heads, n_kv_heads, head_dim, kv_dtype)
+    sc = None if kv_scales is None else np.zeros((2, B, Hkv, S), dtype=np.float32)
+    out = prefill_mha(q, k_new, v_new, qkv_bias, kc, vc, seq_lens, n_heads, n_kv_heads, head_dim, kv_dtype, sc)
     tbl = np.asarray(block_table, dtype=np.int64)
     for b in range(B):
         Sb = int(lens[b])
@@ -336,6 +338,8 @@ def prefill_mha_paged(q, k_new, v_new, qkv_bias, k_pages, v_pages, block_table, 
                 pg = int(entries[t // P])
                 k_pages[pg, :, t % P] = kc[b, :, t]
                 v_pages[pg, :, t % P] = vc[b, :, t]
+                if sc is not None:
+                    kv_scales[:, pg, :, t % P] = sc[:, b, :, t]
     return out
 
 

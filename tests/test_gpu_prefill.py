@@ -157,7 +157,7 @@ def test_prefill_last_position_matches_a_decode_step(ftm):
     assert torch.equal(kc.view(torch.int16), g["k_cache"].view(torch.int16))
 
 
-@pytest.mark.parametrize("name", sorted(W.PREFILL_CASES))
+@pytest.mark.parametrize("name", sorted(n for n, c in W.PREFILL_CASES.items() if c.dtype != "i8"))
 def test_full_size_prefill_sampled_heads(ftm, name):
     """The benchmark's prefill at full size; the appended caches are checked
     whole against a float32/torch recomputation of the append rule, and two

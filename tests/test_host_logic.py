@@ -213,7 +213,8 @@ def test_binding_rejects_mismatched_projection_tensors():
 def call_prefill(**kw):
     args = [("q", A), ("k_new", A), ("v_new", A), ("bias", None), ("k_cache", A), ("v_cache", A),
             ("seq_lens", None), ("batch", 4), ("max_seq_len", 2048), ("prompt_len", 2048), ("n_heads", 32),
-            ("n_kv_heads", 32), ("head_dim", 128), ("kv_dtype", ftm.FTM_F16), ("out", A), ("stream", None)]
+            ("n_kv_heads", 32), ("head_dim", 128), ("kv_dtype", ftm.FTM_F16), ("kv_scales", None), ("out", A),
+            ("stream", None)]
     vals = [kw.get(k, v) for k, v in args]
     rc = ftm.lib.ftm_prefill_mha(*vals)
     return rc, ftm.ftm_last_error()
@@ -226,8 +227,10 @@ def call_prefill(**kw):
     (dict(n_heads=31), 1, "multiple"),
     (dict(prompt_len=0), 1, "prompt_len"),
     (dict(prompt_len=2049), 1, "prompt_len"),
-    (dict(kv_dtype=ftm.FTM_F32), 2, "fp16 or bf16"),
-    (dict(kv_dtype=ftm.FTM_I8), 2, "fp16 or bf16"),
+    (dict(kv_dtype=ftm.FTM_F32), 2, "fp16, bf16 or INT8"),
+    (dict(kv_dtype=ftm.FTM_I8), 1, "kv_scales"),
+    (dict(kv_scales=A), 1, "kv_scales"),
+    (dict(kv_dtype=ftm.FTM_I8, kv_scales=A + 2), 1, "4-byte aligned"),
     (dict(kv_dtype=7), 1, "kv_dtype"),
     (dict(k_cache=A + 8), 1, "aligned"),
     (dict(seq_lens=A + 2), 1, "aligned"),
@@ -247,7 +250,7 @@ def call_prefill_paged(**kw):
     args = [("q", A), ("k_new", A), ("v_new", A), ("bias", None), ("k_pages", A), ("v_pages", A),
             ("block_table", A), ("n_pages", 64), ("page_size", 256), ("max_pages", 8), ("seq_lens", None),
             ("batch", 4), ("prompt_len", 2048), ("n_heads", 32), ("n_kv_heads", 32), ("head_dim", 128),
-            ("kv_dtype", ftm.FTM_F16), ("out", A), ("stream", None)]
+            ("kv_dtype", ftm.FTM_F16), ("kv_scales", None), ("out", A), ("stream", None)]
     vals = [kw.get(k, v) for k, v in args]
     rc = ftm.lib.ftm_prefill_mha_paged(*vals)
     return rc, ftm.ftm_last_error()
@@ -263,7 +266,8 @@ def call_prefill_paged(**kw):
     (dict(page_size=1 << 17), 1, "power of two"),
     (dict(prompt_len=2049), 1, "prompt_len"),
     (dict(max_pages=1 << 16, page_size=1 << 16), 2, "2^31"),
-    (dict(kv_dtype=ftm.FTM_I8), 2, "fp16 or bf16"),
+    (dict(kv_dtype=ftm.FTM_I8), 1, "kv_scales"),
+    (dict(kv_dtype=ftm.FTM_F32), 2, "fp16, bf16 or INT8"),
     (dict(q=None), 1, "NULL"),
     (dict(head_dim=96), 2, "head_dim"),
 ])
