@@ -614,6 +614,10 @@ int prefill_impl(const void* q, const void* k_new, const void* v_new, const void
                                          "prompt_len <= 65535 * 128 and n_kv_heads <= 65535 * 16");
     if (!block_table && (size_t)cache_rows * head_dim * 2 > 0x7fffffffu)
         return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
+    if (i8 && ((size_t)prompt_len * head_dim * 2 > 0x7fffffffu ||
+               (size_t)prompt_len * n_kv_heads * (head_dim / 16) > 0x7fffffffu))
+        return fail(FTM_ERR_UNSUPPORTED, "INT8 prefill: prompt_len * head_dim * 2 bytes (one staged slab) and "
+                                         "prompt_len * n_kv_heads * head_dim / 16 must stay below 2^31");
     ftm::PrefillParams p{q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, out, batch, prompt_len,
                          cache_rows, n_heads, n_kv_heads,
                          (float)(1.4426950408889634 / std::sqrt((double)head_dim)),

@@ -82,24 +82,68 @@ __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams
     }
 }
 
+// The decode step's INT8 codes of 16 elements of a row with scale s:
+// rint(x / s) with the IEEE quotient, clamped to [-127, 127]; s = 0 gives
+// zeros.  Fast path: with r = 1/s (one IEEE division) the product x r lies
+// within 3 |x/s| 2^-24 <= 2.3e-5 of the rounded quotient (|x/s| <= 127), so
+// where x r is more than 2^-14 away from every half-integer both round to
+// the same integer.  A thread with any element closer than that (or a
+// non-finite product) takes the IEEE quotients for all 16.
+__device__ __forceinline__ void quantize16_i8(const float* x, float scale, float* cq) {
+    if (scale != 0.0f) {
+        const float r = 1.0f / scale;
+        bool fast = true;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float q0 = x[e] * r;
+            cq[e] = rintf(q0);
+            fast = fast && fabsf(q0 - cq[e]) < 0.5f - 0x1p-14f;   // false for NaN
+        }
+        if (!fast) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) cq[e] = rintf(x[e] / scale);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cq[e] = fminf(fmaxf(cq[e], -127.0f), 127.0f);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cq[e] = 0.0f;
+    }
+}
+
 // INT8 cache: the prompt's rows, bias added in fp32 and quantised by the
 // decode step's rule (s = absmax / 127 by IEEE division, code = rint(x / s)
 // clamped to [-127, 127], a zero row keeps s = 0), into the cache and its
 // scales, and into the staging the attention reads: the codes as fp16 (exact)
-// and the scales, contiguous.  Grid (S, row slices / 256, B): a thread owns
-// 16 elements of one row, the SL threads of a row are adjacent lanes.
+// and the scales, contiguous.  Grid (ceil(S / RPB) Hkv, B): a block owns RPB
+// consecutive positions of one (sequence, KV head), so its code rows,
+// staging rows and scales are each one contiguous run; a thread owns 16
+// elements of one row, the SL threads of a row are adjacent lanes.  All of
+// a thread's loads are issued before any store.
 template <int D, bool PG>
 __global__ void __launch_bounds__(256) prefill_append_i8_kernel(const PrefillParams p) {
     constexpr int SL = D / 16;              // threads per head row
-    const int t = blockIdx.x;
-    const int c = blockIdx.y * 256 + threadIdx.x;
-    const int b = blockIdx.z;
-    if (c >= p.Hkv * SL) return;            // whole rows: Hkv SL is a multiple of SL
+    constexpr int RPB = 256 / SL;           // rows per block
+    const int b = blockIdx.y;
+    const int nt = (p.S + RPB - 1) / RPB;
+    const int j = (int)blockIdx.x / nt;
+    const int t = ((int)blockIdx.x - j * nt) * RPB + (int)threadIdx.x / SL;
+    const int e0 = ((int)threadIdx.x % SL) * 16;
     const int Sb = p.seq_lens ? p.seq_lens[b] : p.S;
     if (Sb < 1 || Sb > p.S || t >= Sb) return;         // invalid length: no append
-    const int j = c / SL;
-    const int e0 = (c % SL) * 16;
     const size_t src = (((size_t)b * p.S + t) * p.Hkv + j) * D + e0;
+    u32x4 raw[2][2], braw[2][2];
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const uint16_t* in = (const uint16_t*)(which ? p.v_new : p.k_new) + src;
+        raw[which][0] = *(const u32x4*)in;
+        raw[which][1] = *(const u32x4*)(in + 8);
+        if (p.bias) {
+            const uint16_t* bb = (const uint16_t*)p.bias + (size_t)(p.H + which * p.Hkv + j) * D + e0;
+            braw[which][0] = *(const u32x4*)bb;
+            braw[which][1] = *(const u32x4*)(bb + 8);
+        }
+    }
     // destination row in the cache (-1: a page outside the pool, no append)
     long long crow;                         // row index in rows of D codes
     size_t srow;                            // scale index within K's (or V's) half
@@ -117,15 +161,13 @@ __global__ void __launch_bounds__(256) prefill_append_i8_kernel(const PrefillPar
     const size_t stage_row = ((size_t)b * p.Hkv + j) * p.S + t;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        const uint16_t* in = (const uint16_t*)(which ? p.v_new : p.k_new) + src;
         float x[16];
-        Elem16<KV_F16>::unpack(*(const u32x4*)in, x);
-        Elem16<KV_F16>::unpack(*(const u32x4*)(in + 8), x + 8);
+        Elem16<KV_F16>::unpack(raw[which][0], x);
+        Elem16<KV_F16>::unpack(raw[which][1], x + 8);
         if (p.bias) {
-            const uint16_t* bb = (const uint16_t*)p.bias + (size_t)(p.H + which * p.Hkv + j) * D + e0;
             float bx[16];
-            Elem16<KV_F16>::unpack(*(const u32x4*)bb, bx);
-            Elem16<KV_F16>::unpack(*(const u32x4*)(bb + 8), bx + 8);
+            Elem16<KV_F16>::unpack(braw[which][0], bx);
+            Elem16<KV_F16>::unpack(braw[which][1], bx + 8);
 #pragma unroll
             for (int e = 0; e < 16; ++e) x[e] = x[e] + bx[e];   // one fp32 rounding
         }
@@ -135,23 +177,28 @@ __global__ void __launch_bounds__(256) prefill_append_i8_kernel(const PrefillPar
 #pragma unroll
         for (int off = 1; off < SL; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
         const float scale = amax / 127.0f;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        uint32_t hq[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        float cq[16];
+        quantize16_i8(x, scale, cq);
+        uint32_t w[4], hq[8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            float q = 0.0f;
-            if (scale != 0.0f) q = fminf(fmaxf(rintf(x[e] / scale), -127.0f), 127.0f);
-            w[e / 4] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (e % 4));
-            hq[e / 2] |= float_to_half_bits(q) << (16 * (e % 2));
+        for (int k = 0; k < 4; ++k) {       // bytes 0 of four codes -> one word
+            const uint32_t lo = __builtin_amdgcn_perm((uint32_t)(int32_t)cq[4 * k + 1], (uint32_t)(int32_t)cq[4 * k],
+                                                      0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm((uint32_t)(int32_t)cq[4 * k + 3], (uint32_t)(int32_t)cq[4 * k + 2],
+                                                      0x0c0c0400u);
+            w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
         }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)         // integers of at most 8 bits: exact in fp16 under any rounding
+            hq[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cq[2 * k], cq[2 * k + 1]));
         if (crow >= 0) {
             *(u32x4*)((int8_t*)(which ? p.v_cache : p.k_cache) + (size_t)crow * D + e0) = u32x4{w[0], w[1], w[2], w[3]};
-            if (c % SL == 0) p.kv_scales[which * half + srow] = scale;
+            if (e0 == 0) p.kv_scales[which * half + srow] = scale;
         }
         uint16_t* st = (uint16_t*)(which ? p.stage_v : p.stage_k) + stage_row * D + e0;
         *(u32x4*)st = u32x4{hq[0], hq[1], hq[2], hq[3]};
         *(u32x4*)(st + 8) = u32x4{hq[4], hq[5], hq[6], hq[7]};
-        if (c % SL == 0) (which ? p.stage_vs : p.stage_ks)[stage_row] = scale;
+        if (e0 == 0) (which ? p.stage_vs : p.stage_ks)[stage_row] = scale;
     }
 }
 
@@ -643,7 +690,8 @@ hipError_t launch_attention_t(const PrefillParams& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_append_i8_t(const PrefillParams& p, hipStream_t s) {
-    const dim3 grid((unsigned)p.S, (unsigned)((p.Hkv * (D / 16) + 255) / 256), (unsigned)p.B);
+    constexpr int RPB = 256 / (D / 16);
+    const dim3 grid((unsigned)((p.S + RPB - 1) / RPB * p.Hkv), (unsigned)p.B);
     if (p.block_table)
         hipLaunchKernelGGL((prefill_append_i8_kernel<D, true>), grid, dim3(256), 0, s, p);
     else

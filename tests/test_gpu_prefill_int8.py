@@ -195,3 +195,21 @@ def test_full_size_int8_prefill_sampled_heads(ftm):
         ac = W.Case("p", 1, 1, 1, D, "i8", ctx=S, max_seq_len=case.max_seq_len, value_scale=1.0)
         check(ac, out_to_f64(out[b:b + 1, :, h:h + 1]).reshape(S, 1, D), ref.reshape(S, 1, D),
               f"full prefill_int8 b{b} h{h}")
+
+
+def test_int8_prefill_quantisation_ties(ftm):
+    """Rows whose quotients x / s fall exactly on half-integers (absmax 127,
+    so s = 1) or within a few ulps of them (absmax 127 (1 + 2^-10)): the
+    codes must still equal the oracle's, which rounds the IEEE quotient to
+    even."""
+    case = W.PrefillCase("t", 2, 96, 4, 2, 128, "i8", 96, seed=181)
+    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+    inp["bias"].zero_()                     # x = the stored value exactly
+    g = torch.Generator().manual_seed(5)
+    for name in ("k_new", "v_new"):
+        t = inp[name]
+        for pos in range(0, 96, 3):
+            row = (torch.randint(-126, 126, (128,), generator=g).float() + 0.5)
+            row[pos % 128] = 127.0 if pos % 2 == 0 else 127.0 * (1 + 2 ** -10)
+            t[pos % 2, pos, pos % 2] = row.to(torch.float16)
+    run_and_compare(ftm, case, inp, "int8 prefill quantisation ties", paged=False)

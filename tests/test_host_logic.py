@@ -239,6 +239,8 @@ def call_prefill(**kw):
     (dict(batch=40000, n_heads=65536, n_kv_heads=1), 2, "grid"),
     (dict(max_seq_len=1 << 23, prompt_len=1), 2, "2 GiB"),
     (dict(max_seq_len=1 << 23, prompt_len=(1 << 23) - 64), 2, "grid"),
+    (dict(kv_dtype=ftm.FTM_I8, kv_scales=A, max_seq_len=1 << 22, prompt_len=1 << 22, n_heads=64, n_kv_heads=64),
+     2, "INT8 prefill"),
 ])
 def test_prefill_argument_errors_return_before_any_device_call(kw, status, needle):
     rc, msg = call_prefill(**kw)
@@ -267,6 +269,8 @@ def call_prefill_paged(**kw):
     (dict(prompt_len=2049), 1, "prompt_len"),
     (dict(max_pages=1 << 16, page_size=1 << 16), 2, "2^31"),
     (dict(kv_dtype=ftm.FTM_I8), 1, "kv_scales"),
+    (dict(kv_dtype=ftm.FTM_I8, kv_scales=A, max_pages=1 << 15, prompt_len=(1 << 23) - 128, n_heads=64,
+          n_kv_heads=64), 2, "INT8 prefill"),
     (dict(kv_dtype=ftm.FTM_F32), 2, "fp16, bf16 or INT8"),
     (dict(q=None), 1, "NULL"),
     (dict(head_dim=96), 2, "head_dim"),
