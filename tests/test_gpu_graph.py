@@ -157,28 +157,36 @@ def test_capture_refuses_to_grow_the_workspace(ftm):
         ftm.ftm_graph_destroy(graph)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "i8"])
 @pytest.mark.parametrize("paged", [False, True])
-def test_prefill_graph_replays_match_eager_calls(ftm, paged):
+def test_prefill_graph_replays_match_eager_calls(ftm, paged, dt):
     """A prefill (append + attention) captured into a graph: every replay,
     with new query values between replays and eager work in between, must
-    give the eager call's outputs and caches bit for bit."""
-    case = W.PrefillCase("t", 2, 200, 8, 2, 128, "bf16", 256, lens=(120, 200), seed=111)
+    give the eager call's outputs and caches bit for bit.  An INT8 prefill
+    stages its codes in the stream's workspace, so one eager call on the
+    stream sizes it before the capture."""
+    case = W.PrefillCase("t", 2, 200, 8, 2, 128, dt, 256, lens=(120, 200), seed=111)
     inp = W.make_prefill_inputs(case, "cpu", poison=True)
     if paged:
         inp = W.prefill_to_paged(inp, case, 64)
     g = {k: v.cuda() for k, v in inp.items()}
     ck, cv = ("k_pages", "v_pages") if paged else ("k_cache", "v_cache")
-    out = torch.zeros((case.batch, case.prompt, case.n_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
+    act = torch.float16 if dt == "i8" else torch.bfloat16
+    out = torch.zeros((case.batch, case.prompt, case.n_heads, case.head_dim), dtype=act, device="cuda")
     stream = torch.cuda.Stream()
 
     def prefill(o):
+        sc = g.get("kv_scales")
         if paged:
             ftm.ftm_prefill_mha_paged(g["q"], g["k_new"], g["v_new"], g["bias"], g[ck], g[cv], g["block_table"],
-                                      g["seq_lens"], o, stream=stream.cuda_stream)
+                                      g["seq_lens"], o, stream=stream.cuda_stream, kv_scales=sc)
         else:
             ftm.ftm_prefill_mha(g["q"], g["k_new"], g["v_new"], g["bias"], g[ck], g[cv], g["seq_lens"], o,
-                                stream=stream.cuda_stream)
+                                stream=stream.cuda_stream, kv_scales=sc)
 
+    if dt == "i8":
+        prefill(torch.zeros_like(out))
+        stream.synchronize()
     ftm.ftm_graph_begin(stream.cuda_stream)
     try:
         prefill(out)
@@ -187,12 +195,14 @@ def test_prefill_graph_replays_match_eager_calls(ftm, paged):
     try:
         gen = torch.Generator().manual_seed(5)
         for rep in range(3):
-            q_new = (torch.randn(g["q"].shape, generator=gen) / np.sqrt(case.head_dim)).to(torch.bfloat16)
+            scale = 1.0 if dt == "i8" else 1.0 / np.sqrt(case.head_dim)
+            q_new = (torch.randn(g["q"].shape, generator=gen) * scale).to(act)
             g["q"].copy_(q_new.cuda())
             torch.cuda.synchronize()
             ftm.ftm_graph_launch(graph, stream.cuda_stream)
             stream.synchronize()
             got, got_k = out.clone(), g[ck].clone()
+            got_s = g["kv_scales"].clone() if dt == "i8" else None
             _ = (g["q"].float() * 2).sum().item()          # eager work between replays
             ref = torch.zeros_like(out)
             with torch.cuda.stream(stream):
@@ -200,5 +210,7 @@ def test_prefill_graph_replays_match_eager_calls(ftm, paged):
             stream.synchronize()
             assert torch.equal(bits(got), bits(ref)), f"replay {rep}: outputs"
             assert torch.equal(bits(got_k), bits(g[ck])), f"replay {rep}: caches"
+            if dt == "i8":
+                assert torch.equal(got_s.view(torch.int32), g["kv_scales"].view(torch.int32)), f"replay {rep}: scales"
     finally:
         ftm.ftm_graph_destroy(graph)
