@@ -268,9 +268,9 @@ int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, c
  * section 2.3).
  *
  * ftm_graph_begin starts capturing `stream` (a created stream, not the null
- * stream; capture mode thread-local).  The ftm_decode_mha, ftm_decode_mha_paged
- * and ftm_qkv_proj calls that follow on that stream and host thread are
- * recorded, not run.  They allocate nothing: each needs a workspace that an
+ * stream; capture mode thread-local).  The ftm_decode_mha, ftm_decode_mha_paged,
+ * ftm_qkv_proj, ftm_prefill_mha and ftm_prefill_mha_paged calls that follow
+ * on that stream and host thread are recorded, not run.  They allocate nothing: each needs a workspace that an
  * earlier call of the same or a larger shape on the same stream has already
  * grown, or it fails with FTM_ERR_INVALID_ARG and records nothing (the
  * capture stays valid).  FTM_VALIDATE and kernel timing do not apply while
