@@ -216,8 +216,15 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
  * does.  The library then stages the prompt's codes (as fp16) and scales
  * in its per-stream workspace (4 batch n_kv_heads S (head_dim + 2) bytes),
  * allocated on the first call of a larger shape; under stream capture a
- * call that would grow it is refused, as for ftm_decode_mha.  Two kernels are enqueued (append, then
- * attention).  The attention runs on the matrix cores with fp32
+ * call that would grow it is refused, as for ftm_decode_mha.  The attention
+ * multiplies each raw score by its key's K scale and each softmax weight
+ * (at most 2^8 against the running reference) by its key's V scale in
+ * fp32 before the weight enters the matrix cores in fp16: a V row's
+ * absolute maximum must stay below about 32500 (256 s_v within the fp16
+ * range).  INT8 limits: prompt_len * head_dim * 2 and
+ * prompt_len * n_kv_heads * head_dim / 16 below 2^31 (FTM_ERR_UNSUPPORTED).
+ * Two kernels are enqueued (append, then attention).  The attention runs on
+ * the matrix cores with fp32
  * accumulation: the query enters exactly as stored and the bias term
  * b_q . k separately (once per key and head), so the scores are exact
  * products summed in fp32 and then scaled; the softmax weights enter as hi
