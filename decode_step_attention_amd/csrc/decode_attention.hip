@@ -640,8 +640,8 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 // in flight (register sets in rotation).
 constexpr int kGqaDepth = 2;
 
-// Largest batch the balanced schedule handles (its per-sequence work
-// offsets live in LDS); larger batches take the vector-ALU pass.
+// Largest batch the range schedule handles (each lane of a wave holds up to
+// four sequences' lengths); larger batches take the vector-ALU pass.
 constexpr int kGqaMaxBatch = 256;
 
 // LDS layout of the grouped-query pass, per wave: a K tile and a V tile of
@@ -658,19 +658,35 @@ template <int D> struct GqaLds {
     static constexpr int QBYTES = 2 * 16 * KPITCH;
 };
 
-// One segment [pos0, pos1) of one unit (sequence b, KV head j, head group
-// hgi) streamed by the whole workgroup.  On return the workgroup's states
-// sit in LDS: n_states softmax states (m, l, o[HP][D]), one per wave (o in
-// `tiles`) plus, when the segment holds the new row, the appended row's
-// (m and l in slot NW, o in sm_newo).
+// Segments one workgroup streams together, each wave moving from one to the
+// next on its own, with no barrier between them.
+constexpr int kGqaMaxSeg = 2;
+
+// One segment: positions [pos0, pos1) of unit (b, j, hgi), and what the
+// merge of its pieces needs.
+struct GqaSeg {
+    int b, j, hgi, L, pos0, pos1;
+};
+
+// Streams up to kGqaMaxSeg segments with the whole workgroup.  Each wave
+// takes the 16-position tiles wave, wave + NW, ... of every segment in
+// turn, with its K/V loads running DEPTH tiles ahead across segment
+// boundaries and one softmax state per segment in registers; a wave that
+// reaches the next segment starts on it at once.  At the end, per segment,
+// the waves' states and the appended row's (when the segment holds it) are
+// merged through LDS into `out` (a whole unit) or the piece's partial slot.
 template <int KV, int D, int HP, int NW, bool PG>
-__device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles, unsigned char* qbuf,
-                                           float (*sm_m)[HP], float (*sm_l)[HP], float* sm_newo,
-                                           int b, int j, int hgi, int L, int pos0, int pos1) {
+__device__ __forceinline__ void gqa_group(const Params& p, unsigned char* tiles, unsigned char* qbufs,
+                                          float (*sm_m)[NW][HP], float (*sm_l)[NW][HP], float (*sm_nm)[HP],
+                                          float (*sm_nl)[HP], float* sm_newo,
+                                          const GqaSeg (&sg)[kGqaMaxSeg], const int (&npieces)[kGqaMaxSeg],
+                                          int nseg, int blk, bool first_group) {
     using MF = Mfma<KV>;
     using LD = GqaLds<D>;
+    using A = Act<KV>;
     typedef typename MF::vec8 vec8;
     typedef typename MF::vec4 vec4;
+    constexpr int S = kGqaMaxSeg;
     constexpr int NTH = 64 * NW;
     constexpr int ROW_BYTES = D * 2;
     constexpr int KK = D / 32;              // S^T: MFMA steps over the head dim
@@ -679,7 +695,7 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
     constexpr int LPR = D / EPL;            // loads: lanes per row
     constexpr int RPI = 64 / LPR;           // loads: rows per wave-wide load
     constexpr int VL = 16 / RPI;            // loads per 16-position tile, each of K and V
-    constexpr int BLOCK_ROWS = NW * 16;
+    constexpr int DEPTH = kGqaDepth;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -687,105 +703,173 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
     const int n = lane & 15;                // MFMA layout: K row / head column / V column
     const int r = lane / LPR;               // load layout: row slot
     const int c = lane % LPR;               // load layout: 16-byte column slice
-    const int h0 = j * p.G + hgi * HP;
-    const int heads_here = min(HP, p.G - hgi * HP);
-    const int stream_end = min(pos1, L - 1);
-    const bool owns_new = pos1 == L;
-
-    // contiguous cache: one descriptor per stream over rows [0, stream_end)
-    // of this (b, j); paged: one per 16-position tile (tiles start at
-    // multiples of 16 and never straddle a page, P >= 16)
-    const size_t row0 = ((size_t)b * p.Hkv + j) * p.Lmax;
-    const uint32_t valid_bytes = PG ? 0u : (uint32_t)max(stream_end, 0) * ROW_BYTES;
-    const auto krs = make_rsrc(PG ? nullptr : (const char*)p.k_cache + row0 * ROW_BYTES, valid_bytes);
-    const auto vrs = make_rsrc(PG ? nullptr : (const char*)p.v_cache + row0 * ROW_BYTES, valid_bytes);
-    const int32_t* tbl = PG ? p.block_table + (size_t)b * p.max_pages : nullptr;
-    bool bad = false;                       // paged: the table named a page outside the pool
     unsigned char* ktile = tiles + wave * LD::WAVE;
     unsigned char* vtile = ktile + 16 * LD::KPITCH;
 
+    // The group's tiles: segment 0's 16-position tiles, then segment 1's,
+    // numbered 0 .. ntot - 1.  Wave w takes tiles w, w + NW, w + 2 NW, ...
+    // in that order, across the segment boundary without a pause: a fixed
+    // assignment, so every call sums the same positions in the same order
+    // (the results do not depend on timing).  Per segment: the streamed end
+    // (the appended row is handled apart), its tiles, and the descriptor
+    // inputs: contiguous, one descriptor per stream over rows [0, end) of the
+    // unit; paged, one per tile (tiles never straddle a page, P >= 16).
+    static_assert(S == 2, "the tile numbering covers two segments");
+    int send[S], ntl[S];
+    size_t row0[S];                         // contiguous: the unit's first cache row
+    const int32_t* tbl[S];                  // paged: the sequence's block-table row
+    bool bad[S];                            // paged: the table named a page outside the pool
+    static_for<S>([&](auto si) {
+        constexpr int s = decltype(si)::value;
+        bad[s] = false;
+        send[s] = 0;
+        ntl[s] = 0;
+        row0[s] = 0;
+        tbl[s] = p.block_table;
+        if (s < nseg) {
+            send[s] = min(sg[s].pos1, sg[s].L - 1);
+            ntl[s] = send[s] > sg[s].pos0 ? (send[s] - sg[s].pos0 + 15) >> 4 : 0;
+            if constexpr (PG)
+                tbl[s] = p.block_table + (size_t)sg[s].b * p.max_pages;
+            else
+                row0[s] = ((size_t)sg[s].b * p.Hkv + sg[s].j) * p.Lmax;
+        }
+    });
+    const int n0 = ntl[0];
+    const int ntot = n0 + ntl[1];
+
     // K and V rows in the load layout: one wave-wide load is RPI whole rows.
     // DEPTH register sets rotate, so each wave has the loads of DEPTH tiles
-    // in flight while it works on one (set indices are compile-time).
-    constexpr int DEPTH = kGqaDepth;
+    // in flight while it works on one (set indices are compile-time).  The
+    // descriptor's inputs are selected by segment (scalar selects, no
+    // branch), so that every path issues the same loads in the same order
+    // and the compiler's waits before each tile stay partial.  A tile number
+    // past the end loads past segment 0's end: nothing is fetched.
     u32x4 kr[DEPTH][VL], vr[DEPTH][VL];
-    auto issue = [&](auto set, int base) {
-        constexpr int S = decltype(set)::value;
+    auto issue = [&](auto set, int i) {
+        constexpr int SET = decltype(set)::value;
+        const bool valid = i < ntot;
+        const bool nxt = valid && i >= n0;
+        const int end = nxt ? send[1] : send[0];
+        const int base = !valid ? max(send[0], 0) : (nxt ? sg[1].pos0 + 16 * (i - n0) : sg[0].pos0 + 16 * i);
         if constexpr (PG) {
-            const auto kps = page_rsrc(p.k_cache, ROW_BYTES, tbl, p, j, base, stream_end, bad);
-            const auto vps = page_rsrc(p.v_cache, ROW_BYTES, tbl, p, j, base, stream_end, bad);
+            const int32_t* tb = nxt ? tbl[1] : tbl[0];
+            const int jj = nxt ? sg[1].j : sg[0].j;
+            bool bf = false;
+            const auto kps = page_rsrc(p.k_cache, ROW_BYTES, tb, p, jj, base, end, bf);
+            const auto vps = page_rsrc(p.v_cache, ROW_BYTES, tb, p, jj, base, end, bf);
+            bad[1] = bad[1] || (nxt && bf);
+            bad[0] = bad[0] || (!nxt && bf);
 #pragma unroll
             for (int u = 0; u < VL; ++u) {
                 const int off = (u * RPI + r) * ROW_BYTES + c * 16;
-                kr[S][u] = __builtin_amdgcn_raw_buffer_load_b128(kps, off, 0, kStream);
-                vr[S][u] = __builtin_amdgcn_raw_buffer_load_b128(vps, off, 0, kStream);
+                kr[SET][u] = __builtin_amdgcn_raw_buffer_load_b128(kps, off, 0, kStream);
+                vr[SET][u] = __builtin_amdgcn_raw_buffer_load_b128(vps, off, 0, kStream);
             }
         } else {
+            const size_t row = nxt ? row0[1] : row0[0];
+            const uint32_t vb = (uint32_t)max(end, 0) * ROW_BYTES;
+            const auto krs = make_rsrc((const char*)p.k_cache + row * ROW_BYTES, vb);
+            const auto vrs = make_rsrc((const char*)p.v_cache + row * ROW_BYTES, vb);
 #pragma unroll
             for (int u = 0; u < VL; ++u) {
                 const int off = (base + u * RPI + r) * ROW_BYTES + c * 16;
-                kr[S][u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStream);
-                vr[S][u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStream);
+                kr[SET][u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStream);
+                vr[SET][u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStream);
             }
         }
     };
-    // query operand of S^T, shared by the workgroup: column n = head h0 + n
-    // (zero past the group), hi and lo halves, in the K tile's layout; one
-    // 16-byte piece of one head per thread.  Its loads go out first, so that
-    // waiting for them leaves the K/V loads issued next in flight.
+
+    // query operands of S^T, one per segment, shared by the workgroup:
+    // column n = head h0 + n (zero past the group), hi and lo halves, in the
+    // K tile's layout; one 16-byte piece of one head per thread.  Their
+    // loads go out first, so that waiting for them leaves the K/V loads
+    // issued next in flight.
     static_assert(16 * LPR <= NTH, "one query piece per thread");
     const int qcol = threadIdx.x / LPR;
     const int qpc = threadIdx.x - qcol * LPR;
-    const bool qload = threadIdx.x < 16 * LPR && qcol < heads_here;
-    const size_t qh_idx = (size_t)h0 + min(qcol, heads_here - 1);
     // (without a bias the same offset is read from q, in bounds, and unused:
     // no branch, so nothing waits for these loads before the K/V issue)
     const uint16_t* bsrc = (const uint16_t*)(p.bias ? p.bias : p.q);
-    u32x4 qraw = u32x4{0u, 0u, 0u, 0u}, braw = u32x4{0u, 0u, 0u, 0u};
-    if (qload) {
-        qraw = *(const u32x4*)((const uint16_t*)p.q + ((size_t)b * p.H + qh_idx) * D + qpc * 8);
-        braw = *(const u32x4*)(bsrc + qh_idx * D + qpc * 8);
-    }
-    // the appended row's inputs (the piece holding position L-1, wave 0):
-    // loaded now, so the row is stored and scored while the first tiles are
-    // in flight (without a bias the offsets fall back to valid ones, unused)
-    const bool new_here = owns_new && wave == 0;
+    u32x4 qraw[S], braw[S];
+    bool qload[S];
+    static_for<S>([&](auto si) {
+        constexpr int s = decltype(si)::value;
+        qraw[s] = u32x4{0u, 0u, 0u, 0u};
+        braw[s] = u32x4{0u, 0u, 0u, 0u};
+        qload[s] = false;
+        if (s < nseg) {
+            const int hh = min(HP, p.G - sg[s].hgi * HP);
+            qload[s] = threadIdx.x < 16 * LPR && qcol < hh;
+            const size_t qh = (size_t)sg[s].j * p.G + sg[s].hgi * HP + min(qcol, hh - 1);
+            if (qload[s]) {
+                qraw[s] = *(const u32x4*)((const uint16_t*)p.q + ((size_t)sg[s].b * p.H + qh) * D + qpc * 8);
+                braw[s] = *(const u32x4*)(bsrc + qh * D + qpc * 8);
+            }
+        }
+    });
+    // the appended rows' inputs: wave s takes segment s's when the segment
+    // holds its unit's last position; loaded now, so that the row is stored
+    // and scored while the first tiles are in flight (without a bias the
+    // offsets fall back to valid ones, unused)
+    bool new_here = false;
+    int nb = 0, nj = 0, nhgi = 0, nL = 1;
+    static_for<S>([&](auto si) {
+        constexpr int s = decltype(si)::value;
+        if (s < nseg && wave == s && sg[s].pos1 == sg[s].L) {
+            new_here = true;
+            nb = sg[s].b;
+            nj = sg[s].j;
+            nhgi = sg[s].hgi;
+            nL = sg[s].L;
+        }
+    });
     u32x4 nk = u32x4{0u, 0u, 0u, 0u}, nv = nk, nbk = nk, nbv = nk;
     if (new_here) {
-        const size_t src = ((size_t)b * p.Hkv + j) * D + c * EPL;
+        const size_t src = ((size_t)nb * p.Hkv + nj) * D + c * EPL;
         nk = *(const u32x4*)((const uint16_t*)p.k_new + src);
         nv = *(const u32x4*)((const uint16_t*)p.v_new + src);
         const uint16_t* bb = (const uint16_t*)(p.bias ? p.bias : p.k_new);
-        nbk = *(const u32x4*)(bb + (p.bias ? (size_t)(p.H + j) * D : 0) + c * EPL);
-        nbv = *(const u32x4*)(bb + (p.bias ? (size_t)(p.H + p.Hkv + j) * D : 0) + c * EPL);
+        nbk = *(const u32x4*)(bb + (p.bias ? (size_t)(p.H + nj) * D : 0) + c * EPL);
+        nbv = *(const u32x4*)(bb + (p.bias ? (size_t)(p.H + p.Hkv + nj) * D : 0) + c * EPL);
     }
 
-    int base = pos0 + wave * 16;
-    static_for<DEPTH>([&](auto set) { issue(set, base + decltype(set)::value * BLOCK_ROWS); });
+    // the tile in each register set
+    int tidx[DEPTH];
+    static_for<DEPTH>([&](auto set) {
+        tidx[decltype(set)::value] = wave + NW * decltype(set)::value;
+        issue(set, tidx[decltype(set)::value]);
+    });
     __builtin_amdgcn_sched_barrier(0);
 
     if (threadIdx.x < 16 * LPR) {
-        float x[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        if (qload) {
-            Elem<KV>::unpack(qraw, x);
-            if (p.bias) {
-                float bx[8];
-                Elem<KV>::unpack(braw, bx);
+        static_for<S>([&](auto si) {
+            constexpr int s = decltype(si)::value;
+            if (s < nseg) {
+                float x[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+                if (qload[s]) {
+                    Elem<KV>::unpack(qraw[s], x);
+                    if (p.bias) {
+                        float bx[8];
+                        Elem<KV>::unpack(braw[s], bx);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = x[e] + bx[e];
+                        for (int e = 0; e < 8; ++e) x[e] = x[e] + bx[e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] *= p.qscale;
+                }
+                vec8 hi, lo;
+                MF::split8(x, hi, lo);
+                unsigned char* qb = qbufs + s * LD::QBYTES;
+                *(vec8*)(qb + qcol * LD::KPITCH + qpc * 16) = hi;
+                *(vec8*)(qb + 16 * LD::KPITCH + qcol * LD::KPITCH + qpc * 16) = lo;
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] *= p.qscale;
-        }
-        vec8 hi, lo;
-        MF::split8(x, hi, lo);
-        *(vec8*)(qbuf + qcol * LD::KPITCH + qpc * 16) = hi;
-        *(vec8*)(qbuf + 16 * LD::KPITCH + qcol * LD::KPITCH + qpc * 16) = lo;
+        });
     }
     __syncthreads();
 
-    // the appended row: stored, and kept as one more softmax state (score
-    // from the staged query halves, as for every other row of the pass)
+    // the appended row: stored, and kept as one more softmax state of its
+    // segment (score from the staged query halves, as for every other row)
     if (new_here) {
         float kx[EPL], vx[EPL], bx[EPL], ks, vs;
         Elem<KV>::unpack(nk, kx);
@@ -802,52 +886,48 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
         store_new_row<KV, EPL, LPR>(kx, kx, ks, kpk);
         store_new_row<KV, EPL, LPR>(vx, vx, vs, vpk);
         size_t nrow, splane;
-        const bool ok = new_row_index<PG>(p, b, j, L - 1, nrow, splane);
-        if (ok && hgi == 0 && r == 0) {
+        const bool ok = new_row_index<PG>(p, nb, nj, nL - 1, nrow, splane);
+        if (ok && nhgi == 0 && r == 0) {
             *(u32x4*)((char*)p.k_cache + nrow * ROW_BYTES + c * 16) = kpk;
             *(u32x4*)((char*)p.v_cache + nrow * ROW_BYTES + c * 16) = vpk;
         }
+        const unsigned char* qb = qbufs + wave * LD::QBYTES;
+        float* newo = sm_newo + wave * HP * D;
 #pragma unroll
         for (int h = 0; h < HP; ++h) {
             float qh[8], ql[8];
-            Elem<KV>::unpack(*(const u32x4*)(qbuf + h * LD::KPITCH + c * 16), qh);
-            Elem<KV>::unpack(*(const u32x4*)(qbuf + 16 * LD::KPITCH + h * LD::KPITCH + c * 16), ql);
+            Elem<KV>::unpack(*(const u32x4*)(qb + h * LD::KPITCH + c * 16), qh);
+            Elem<KV>::unpack(*(const u32x4*)(qb + 16 * LD::KPITCH + h * LD::KPITCH + c * 16), ql);
             float d = 0.0f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) d = fmaf(qh[e] + ql[e], kx[e], d);
             d = group_sum<LPR>(d);
             if (r == 0) {
                 if (c == 0) {
-                    sm_m[NW][h] = d;
-                    sm_l[NW][h] = ok ? 1.0f : __builtin_nanf("");
+                    sm_nm[wave][h] = d;
+                    sm_nl[wave][h] = ok ? 1.0f : __builtin_nanf("");
                 }
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) sm_newo[h * D + c * EPL + e] = vx[e];
+                for (int e = 0; e < EPL; ++e) newo[h * D + c * EPL + e] = vx[e];
             }
         }
     }
 
-    float m = kNegInf;                      // head n: running max (same in all four quads)
-    float l = 0.0f;                         // head n: this lane's share of the sum
-    f32x4 acc[DT];                          // O[head 4g+i][16*tn + n]
+    float m[S], l[S];                       // head n: running max (same in all four quads), this lane's share of the sum
+    f32x4 acc[S][DT];                       // O[head 4g+i][16*tn + n]
+    static_for<S>([&](auto si) {
+        constexpr int s = decltype(si)::value;
+        m[s] = kNegInf;
+        l[s] = 0.0f;
 #pragma unroll
-    for (int tn = 0; tn < DT; ++tn) acc[tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int tn = 0; tn < DT; ++tn) acc[s][tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    });
 
-    // one 16-position tile starting at tb, from register set `set`
-    auto tile = [&](auto set, int tb) {
-        constexpr int S = decltype(set)::value;
-        // stage the tile in LDS, then send the loads DEPTH tiles ahead out
-        lds_wave_fence();
-#pragma unroll
-        for (int u = 0; u < VL; ++u) {
-            *(u32x4*)(ktile + (u * RPI + r) * LD::KPITCH + c * 16) = kr[S][u];
-            *(u32x4*)(vtile + (u * RPI + r) * LD::VPITCH + c * 16) = vr[S][u];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        issue(set, tb + DEPTH * BLOCK_ROWS);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_wave_fence();
-
+    // the softmax of one 16-position tile of segment s starting at tb,
+    // staged in this wave's LDS tiles
+    auto compute = [&](auto si, int tb) {
+        constexpr int s = decltype(si)::value;
+        const unsigned char* qbuf = qbufs + s * LD::QBYTES;
         // S^T: row = position 4g+i of the tile, column = head n
         f32x4 st = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -864,148 +944,218 @@ __device__ __forceinline__ int gqa_segment(const Params& p, unsigned char* tiles
         }
 
         // online softmax per head (column n) over the positions of the tile
-        float s[4];
+        float sc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = tb + 4 * g + i < stream_end ? st[i] : kNegInf;
-        float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        for (int i = 0; i < 4; ++i) sc[i] = tb + 4 * g + i < send[s] ? st[i] : kNegInf;
+        float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m, mt);
+        const float mn = fmaxf(m[s], mt);
         const float ms = mn == kNegInf ? 0.0f : mn;
-        const float alpha = fast_exp2(m - ms);
-        m = mn;
+        const float alpha = fast_exp2(m[s] - ms);
+        m[s] = mn;
         float ls = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s[i] = fast_exp2(s[i] - ms);
-            ls += s[i];
+            sc[i] = fast_exp2(sc[i] - ms);
+            ls += sc[i];
         }
-        l = l * alpha + ls;
+        l[s] = l[s] * alpha + ls;
         // P as the A operand of O += P.V: row = head n, k = positions 4g+i
         vec4 ph, pl;
-        MF::split4(s, ph, pl);
+        MF::split4(sc, ph, pl);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float ai = __shfl(alpha, 4 * g + i);
 #pragma unroll
-            for (int tn = 0; tn < DT; ++tn) acc[tn][i] *= ai;
+            for (int tn = 0; tn < DT; ++tn) acc[s][tn][i] *= ai;
         }
         // B operand V[position 4g+i][16*tn + n]: one transposing read per
         // 16 columns; lane n of group g names row 4g + n/4, columns 4(n%4)..+3
         const unsigned char* vrow = vtile + (4 * g + (n >> 2)) * LD::VPITCH + (n & 3) * 8;
 #pragma unroll
         for (int tn = 0; tn < DT; ++tn) {
-            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            const s16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4*)(vrow + tn * 32));
-            const vec4 vb = __builtin_bit_cast(vec4, t);
-            acc[tn] = MF::mma16(ph, vb, acc[tn]);
-            acc[tn] = MF::mma16(pl, vb, acc[tn]);
+            const vec4 vb = __builtin_bit_cast(vec4, tv);
+            acc[s][tn] = MF::mma16(ph, vb, acc[s][tn]);
+            acc[s][tn] = MF::mma16(pl, vb, acc[s][tn]);
             if (tn & 1) __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // DEPTH tiles per trip with no exit in between, so that the waits the
-    // compiler places before each tile's registers stay partial (a tile
-    // past the end is all masked: its loads fetch nothing, its weights are 0)
-    for (; base < stream_end; base += DEPTH * BLOCK_ROWS)
-        static_for<DEPTH>([&](auto set) { tile(set, base + decltype(set)::value * BLOCK_ROWS); });
-
-    // l over the four quads of the column
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    __syncthreads();                        // every wave is done with its tiles
-    float* sm_o = (float*)tiles;            // [NW][HP][D]
+    // one tile from register set `set`: stage it in LDS, send the loads of
+    // this wave's tile DEPTH tiles ahead, then compute (a number past the
+    // end only stages and issues: it fetches nothing)
+    auto tile = [&](auto set) {
+        constexpr int SET = decltype(set)::value;
+        lds_wave_fence();
+        const int cur = tidx[SET];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int h = 4 * g + i;
-        if (h < HP) {
-#pragma unroll
-            for (int tn = 0; tn < DT; ++tn) sm_o[(wave * HP + h) * D + tn * 16 + n] = acc[tn][i];
+        for (int u = 0; u < VL; ++u) {
+            *(u32x4*)(ktile + (u * RPI + r) * LD::KPITCH + c * 16) = kr[SET][u];
+            *(u32x4*)(vtile + (u * RPI + r) * LD::VPITCH + c * 16) = vr[SET][u];
         }
-    }
-    if (g == 0 && n < HP) {
-        sm_m[wave][n] = m;
-        sm_l[wave][n] = bad ? __builtin_nanf("") : l;   // a page outside the pool: NaN result
+        __builtin_amdgcn_sched_barrier(0);
+        const int ni = cur + NW * DEPTH;
+        issue(set, ni);
+        tidx[SET] = ni;
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wave_fence();
+        if (cur < n0)
+            compute(std::integral_constant<int, 0>{}, sg[0].pos0 + 16 * cur);
+        else if (cur < ntot)
+            compute(std::integral_constant<int, 1>{}, sg[1].pos0 + 16 * (cur - n0));
+    };
+    // DEPTH tiles per trip with no exit in between, so that the waits the
+    // compiler places before each tile's registers stay partial; the trips
+    // go on while a set holds a tile of the group
+    for (;;) {
+        bool any = false;
+        static_for<DEPTH>([&](auto set) { any = any || tidx[decltype(set)::value] < ntot; });
+        if (!any) break;
+        static_for<DEPTH>([&](auto set) { tile(set); });
     }
 
+    // per segment: merge the waves' states and the appended row's; write
+    // out, or the piece's partial slot (the workgroup's first segment takes
+    // its first slot, any later piece its second).  Every segment's states
+    // go to LDS at once, so one barrier serves them all.
+    __syncthreads();                        // every wave is done with its tiles
+    float* sm_o = (float*)tiles;            // [S][NW][HP][D]
+    static_for<S>([&](auto si) {
+        constexpr int s = decltype(si)::value;
+        if (s < nseg) {
+            // l over the four quads of the column
+            float ls = l[s];
+            ls += __shfl_xor(ls, 16);
+            ls += __shfl_xor(ls, 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 4 * g + i;
+                if (h < HP) {
+#pragma unroll
+                    for (int tn = 0; tn < DT; ++tn)
+                        sm_o[((s * NW + wave) * HP + h) * D + tn * 16 + n] = acc[s][tn][i];
+                }
+            }
+            if (g == 0 && n < HP) {
+                sm_m[s][wave][n] = m[s];
+                sm_l[s][wave][n] = bad[s] ? __builtin_nanf("") : ls;   // a page outside the pool: NaN result
+            }
+        }
+    });
     __syncthreads();
-    return owns_new ? NW + 1 : NW;
+    static_for<S>([&](auto si) {
+        constexpr int s = decltype(si)::value;
+        if (s < nseg) {
+            const bool own = sg[s].pos1 == sg[s].L;
+            const int h0 = sg[s].j * p.G + sg[s].hgi * HP;
+            const int heads_here = min(HP, p.G - sg[s].hgi * HP);
+            const int slot = 2 * blk + (first_group && s == 0 ? 0 : 1);
+            const float* newo = sm_newo + s * HP * D;
+            for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
+                const int h = idx / D;
+                const int d = idx - h * D;
+                if (h >= heads_here) continue;
+                float M = own ? sm_nm[s][h] : kNegInf;
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[s][w][h]);
+                const float ms = M == kNegInf ? 0.0f : M;
+                float lsum = 0.0f, o = 0.0f;
+                for (int w = 0; w < NW; ++w) {
+                    const float a = fast_exp2(sm_m[s][w][h] - ms);
+                    lsum += a * sm_l[s][w][h];
+                    o += a * sm_o[((s * NW + w) * HP + h) * D + d];
+                }
+                if (own) {
+                    const float a = fast_exp2(sm_nm[s][h] - ms);
+                    lsum += a * sm_nl[s][h];
+                    o += a * newo[h * D + d];
+                }
+                if (npieces[s] == 1) {
+                    A::st(p.out, ((size_t)sg[s].b * p.H + h0 + h) * D + d, o / lsum);
+                } else {
+                    const size_t sl = (size_t)slot * HP + h;
+                    coherent_store(&p.ws_o[sl * D + d], o);
+                    if (d == 0) {
+                        coherent_store(&p.ws_ml[sl * 2], M);
+                        coherent_store(&p.ws_ml[sl * 2 + 1], lsum);
+                    }
+                }
+            }
+        }
+    });
+    __syncthreads();                        // the merge buffers are reused next
 }
 
-// Grouped-query pass with a balanced schedule.  The work of a step is L_b
-// positions for each unit u = (b, j, hgi).  With W = max(seg_min,
-// ceil(total / target)) the units of sequence b are cut into
-// n_b = max(1, round(L_b / W)) near-equal pieces, one workgroup per piece,
-// so every workgroup streams about W rows whatever the lengths, and each
-// streams a single piece (one prologue, one epilogue).  The grid has
-// target + units workgroups, at least the number of pieces; the rest exit.
-// A unit in one piece writes `out` directly.  Otherwise each piece writes
-// its state to the unit's partial slot, and the last piece to finish (an
-// atomic count per unit) merges the slots into `out` and clears the count
-// for the next call.  Partials move between XCDs as device-coherent
-// accesses, so no cache-wide writeback or invalidate is needed.
+// Streamed 16-row tiles of a unit of length L: rows [0, L - 1) come from the
+// cache, the appended row is handled apart; at least one tile, so that a
+// unit of length 1 still has a place in the schedule.
+__device__ __forceinline__ int gqa_tiles(int L) { return max(1, (L + 14) >> 4); }
+
+// Grouped-query pass with a range schedule.  The work of a step is the
+// 16-row tiles of every unit u = (b, j, hgi) plus `unit_cost` virtual tiles
+// per unit that stand for a segment's fixed costs.  Units lie end to end in
+// (b, j, hgi) order, and workgroup k takes the tiles [k tpw, (k + 1) tpw),
+// tpw = max(ceil(total / grid), range_min), so every workgroup streams about
+// the same number of rows whatever the lengths.  A range may cross units:
+// the workgroup streams its part of each unit (a segment), up to
+// kGqaMaxSeg segments at a time with no barrier between them.  A unit
+// inside one range writes `out` directly.  Otherwise each piece writes its
+// state to a partial slot (two per workgroup: its first and its last
+// segment, the only ones that can be pieces), and the workgroup that
+// completes the unit's count merges them.  Partials move between XCDs as
+// device-coherent accesses, so no cache-wide writeback or invalidate is
+// needed.
 template <int KV, int D, int HP, int NW, bool PG>
 __global__ void __launch_bounds__(64 * NW) gqa_kernel(const Params p) {
     using A = Act<KV>;
     using LD = GqaLds<D>;
     constexpr int NTH = 64 * NW;
+    constexpr int S = kGqaMaxSeg;
     constexpr int O_BYTES = NW * HP * D * 4;
+    constexpr int SMEM = cmax(NW * LD::WAVE, O_BYTES);
     static_assert(HP == 4 || HP == 8, "4 or 8 heads per pass");
+    static_assert(S <= NW, "one wave per segment handles its appended row");
+    static_assert(S * O_BYTES <= SMEM, "every segment's wave states fit in the tile buffers");
 
     // per-wave tiles while streaming; the merge buffers afterwards
-    __shared__ __attribute__((aligned(16))) unsigned char smem[cmax(NW * LD::WAVE, O_BYTES)];
-    __shared__ __attribute__((aligned(16))) unsigned char qbuf[LD::QBYTES];
-    __shared__ float sm_m[NW + 1][HP];      // slot NW: the appended row
-    __shared__ float sm_l[NW + 1][HP];
-    __shared__ float sm_newo[HP * D];       // the appended row's values
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    __shared__ __attribute__((aligned(16))) unsigned char qbufs[S * LD::QBYTES];
+    __shared__ float sm_m[S][NW][HP];       // the waves' states, per segment
+    __shared__ float sm_l[S][NW][HP];
+    __shared__ float sm_nm[S][HP];          // the appended rows' states, per segment
+    __shared__ float sm_nl[S][HP];
+    __shared__ float sm_newo[S * HP * D];
     __shared__ int sm_last;
 
     const int lane = threadIdx.x & 63;
     const int upb = p.Hkv * p.n_hg;         // units per sequence
-    const int target = gridDim.x - p.B * upb;
+    const int cost = p.unit_cost;
+    const int blk = blockIdx.x;
+    const int nwg = gridDim.x;
 
     // Every wave derives the schedule on its own, in registers (no LDS, no
-    // barrier): lane l holds sequences l, l + 64, ...; valid lengths, total
-    // work, slice length W, pieces per sequence n_b * upb and their prefix,
-    // then the sequence whose pieces include this workgroup's.
+    // barrier): lane l holds sequences l, l + 64, ...; valid lengths, then
+    // the total tiles and the range length tpw.
     constexpr int NCH = kGqaMaxBatch / 64;
     int len[NCH];
     int tot = 0;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-        const int idx = ch * 64 + lane;
-        int Lb = 0;
-        if (idx < p.B) {
-            Lb = p.seq_lens ? p.seq_lens[idx] : p.step;
-            Lb = (Lb >= 1 && Lb <= p.step) ? Lb : 0;
+        len[ch] = 0;
+        if (ch * 64 < p.B) {
+            const int idx = ch * 64 + lane;
+            int Lb = 0;
+            if (idx < p.B) {
+                Lb = p.seq_lens ? p.seq_lens[idx] : p.step;
+                Lb = (Lb >= 1 && Lb <= p.step) ? Lb : 0;
+            }
+            len[ch] = Lb;
+            tot += Lb > 0 ? gqa_tiles(Lb) + cost : 0;
         }
-        len[ch] = Lb;
-        tot += Lb;
     }
-    tot = __builtin_amdgcn_readfirstlane(wave_sum_int(tot));
-    const long long total = (long long)tot * upb;
-    const int W = max((int)((total + target - 1) / max(target, 1)), p.seg_min);
-    const int blk = blockIdx.x;
-    int carry = 0, b = -1, first = 0, npc = 0, L = 0;
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-        const int v = len[ch] > 0 ? max(1, (len[ch] + W / 2) / W) * upb : 0;
-        int incl = v;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(incl, off);
-            if (lane >= off) incl += t;
-        }
-        const bool hit = blk >= carry + incl - v && blk < carry + incl;
-        const unsigned long long m = __ballot(hit);
-        if (m) {
-            const int l = __builtin_ctzll(m);
-            b = ch * 64 + l;
-            first = carry + __builtin_amdgcn_readlane(incl - v, l);
-            npc = __builtin_amdgcn_readlane(v, l);
-            L = __builtin_amdgcn_readlane(len[ch], l);
-        }
-        carry += __builtin_amdgcn_readlane(incl, 63);
-    }
+    tot = __builtin_amdgcn_readfirstlane(wave_sum_int(tot)) * upb;
+    const int tpw = max((tot + nwg - 1) / nwg, p.range_min);
 
     // NaN rows for sequences whose length is invalid (no append for them):
     // block bb < B checks sequence bb (the grid has at least B blocks)
@@ -1018,108 +1168,181 @@ __global__ void __launch_bounds__(64 * NW) gqa_kernel(const Params p) {
             for (int idx = threadIdx.x; idx < p.H * D; idx += NTH)
                 A::st(p.out, (size_t)blk * p.H * D + idx, __builtin_nanf(""));
     }
-    if (b < 0) return;                      // no piece for this workgroup
+    const int t0 = blk * tpw;
+    if (t0 >= tot) return;                  // no range for this workgroup
+    const int t1 = min(t0 + tpw, tot);
 
-    // the piece, the same in every wave: scalar registers, so that the loop
-    // bounds, the descriptors and block-table reads stay scalar
-    b = __builtin_amdgcn_readfirstlane(b);
-    L = __builtin_amdgcn_readfirstlane(L);
-    const int nseg = __builtin_amdgcn_readfirstlane(npc / upb);
-    const int local = __builtin_amdgcn_readfirstlane(blk - first);
-    const int ub = local / nseg;            // unit within the sequence: j * n_hg + hgi
-    const int seg = local - ub * nseg;
-    // piece boundaries on multiples of 16 (a tile never straddles a page)
-    const int pos0 = __builtin_amdgcn_readfirstlane(seg == 0 ? 0 : (int)((long long)seg * L / nseg) & ~15);
-    const int pos1 = __builtin_amdgcn_readfirstlane(seg == nseg - 1 ? L
-                                                    : (int)((long long)(seg + 1) * L / nseg) & ~15);
-    const int j = ub / p.n_hg;
-    const int hgi = ub - j * p.n_hg;
-    const int h0 = j * p.G + hgi * HP;
-    const int heads_here = min(HP, p.G - hgi * HP);
-    const int unit = b * upb + ub;
-
-    const int n_states = gqa_segment<KV, D, HP, NW, PG>(p, smem, qbuf, sm_m, sm_l, sm_newo, b, j, hgi,
-                                                        L, pos0, pos1);
-    float* sm_o = (float*)smem;
-
-    // merge this workgroup's states; write out, or the unit's partial slot
-    for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
-        const int h = idx / D;
-        const int d = idx - h * D;
-        if (h >= heads_here) continue;
-        float M = sm_m[0][h];
-        for (int w = 1; w < n_states; ++w) M = fmaxf(M, sm_m[w][h]);
-        const float ms = M == kNegInf ? 0.0f : M;
-        float lsum = 0.0f, o = 0.0f;
-        for (int w = 0; w < n_states; ++w) {
-            const float a = fast_exp2(sm_m[w][h] - ms);
-            lsum += a * sm_l[w][h];
-            o += a * (w < NW ? sm_o[(w * HP + h) * D + d] : sm_newo[h * D + d]);
-        }
-        if (nseg == 1) {
-            A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o / lsum);
-        } else {
-            const size_t slot = ((size_t)unit * p.seg_max + seg) * HP + h;
-            coherent_store(&p.ws_o[slot * D + d], o);
-            if (d == 0) {
-                coherent_store(&p.ws_ml[slot * 2], M);
-                coherent_store(&p.ws_ml[slot * 2 + 1], lsum);
+    // the sequence whose units hold tile t0: a scan over the sequences' spans
+    int carry = 0, b = -1, pre = 0, L = 0;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (ch * 64 < p.B) {
+            const int v = len[ch] > 0 ? (gqa_tiles(len[ch]) + cost) * upb : 0;
+            int incl = v;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(incl, off);
+                if (lane >= off) incl += t;
             }
+            const bool hit = t0 >= carry + incl - v && t0 < carry + incl;
+            const unsigned long long m = __ballot(hit);
+            if (m) {
+                const int l = __builtin_ctzll(m);
+                b = ch * 64 + l;
+                pre = carry + __builtin_amdgcn_readlane(incl - v, l);
+                L = __builtin_amdgcn_readlane(len[ch], l);
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
         }
     }
-    if (nseg == 1) return;
+    // the schedule, the same in every wave: scalar registers, so that the
+    // loop bounds, the descriptors and block-table reads stay scalar
+    b = __builtin_amdgcn_readfirstlane(b);
+    if (b < 0) return;
+    L = __builtin_amdgcn_readfirstlane(L);
+    pre = __builtin_amdgcn_readfirstlane(pre);
+    int nt = gqa_tiles(L);
+    int ub = (t0 - pre) / (nt + cost);      // unit within the sequence: j * n_hg + hgi
+    int vu = pre + ub * (nt + cost);        // the unit's first (virtual) tile
+    bool done = false;
+
+    // the pieces among this workgroup's segments: unit, its first virtual
+    // tile, its first piece's workgroup, its number of pieces
+    int np = 0;
+    int pu0 = 0, pv0 = 0, pk0 = 0, pn0 = 0, pu1 = 0, pv1 = 0, pk1 = 0, pn1 = 0;
+    for (bool first_group = true;; first_group = false) {
+        // the next (up to) kGqaMaxSeg segments of the range
+        GqaSeg sg[S];
+        int npc[S];
+        int nseg = 0;
+        static_for<S>([&](auto si) {
+            constexpr int s = decltype(si)::value;
+            sg[s] = GqaSeg{0, 0, 0, 1, 0, 0};
+            npc[s] = 1;
+            if (!done) {
+                const int rs = vu + cost;   // the unit's streamed tiles [rs, re)
+                const int re = rs + nt;
+                if (rs >= t1) {
+                    done = true;
+                } else {
+                    const int s0 = max(rs, t0), s1 = min(re, t1);
+                    const int j = ub / p.n_hg;
+                    sg[s] = GqaSeg{b, j, ub - j * p.n_hg, L, (s0 - rs) * 16, s1 == re ? L : (s1 - rs) * 16};
+                    const int kf = rs / tpw;
+                    npc[s] = (re - 1) / tpw - kf + 1;
+                    if (npc[s] > 1) {
+                        if (np == 0) {
+                            pu0 = b * upb + ub; pv0 = vu; pk0 = kf; pn0 = npc[s];
+                        } else {
+                            pu1 = b * upb + ub; pv1 = vu; pk1 = kf; pn1 = npc[s];
+                        }
+                        ++np;
+                    }
+                    nseg = s + 1;
+                    // the next unit: the next head group or KV head, else
+                    // the next valid sequence
+                    vu = re;
+                    if (++ub == upb) {
+                        ub = 0;
+                        int nb = -1, nl = 0;
+#pragma unroll
+                        for (int ch = 0; ch < NCH; ++ch) {
+                            if (ch * 64 < p.B && nb < 0) {
+                                const unsigned long long m = __ballot(ch * 64 + lane > b && len[ch] > 0);
+                                if (m) {
+                                    const int l = __builtin_ctzll(m);
+                                    nb = ch * 64 + l;
+                                    nl = __builtin_amdgcn_readlane(len[ch], l);
+                                }
+                            }
+                        }
+                        if (nb < 0) {
+                            done = true;
+                        } else {
+                            b = __builtin_amdgcn_readfirstlane(nb);
+                            L = __builtin_amdgcn_readfirstlane(nl);
+                            nt = gqa_tiles(L);
+                        }
+                    }
+                }
+            }
+        });
+        if (nseg == 0) break;
+        gqa_group<KV, D, HP, NW, PG>(p, smem, qbufs, sm_m, sm_l, sm_nm, sm_nl, sm_newo, sg, npc, nseg, blk,
+                                     first_group);
+        if (done) break;
+    }
+    if (np == 0) return;
+
     // partials are written through to the device coherence point; once every
-    // thread's stores are acknowledged the unit's count goes up, and the
-    // workgroup that completes it reads the partials back coherently
+    // thread's stores are acknowledged the units' counts go up, and the
+    // workgroup that completes a count reads the unit's partials back
+    // coherently and merges them
     wait_stores();
     __syncthreads();
-    if (threadIdx.x == 0)
-        sm_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == nseg - 1;
-    __syncthreads();
-    if (!sm_last) return;
-    // one parallel round for the pieces' (m, l), kept in LDS as rescale
-    // factors; then each output sums its pieces with independent loads
-    const size_t slot0 = (size_t)unit * p.seg_max * HP;
-    float* sm_a = (float*)smem;             // [seg_max][HP]: l_k, then the weights 2^(m_k - M)
-    float* sm_ls = sm_a + p.seg_max * HP;   // [HP]: 1 / sum_k 2^(m_k - M) l_k
-    float* sm_ms = sm_ls + HP;              // [seg_max][HP]: m_k
-    for (int t = threadIdx.x; t < nseg * HP; t += NTH) {
-        sm_ms[t] = coherent_load(&p.ws_ml[(slot0 + t) * 2]);
-        sm_a[t] = coherent_load(&p.ws_ml[(slot0 + t) * 2 + 1]);
-    }
-    __syncthreads();
-    if (threadIdx.x < HP) {
-        const int h = threadIdx.x;
-        float M = kNegInf;
-        for (int k = 0; k < nseg; ++k) M = fmaxf(M, sm_ms[k * HP + h]);
-        float lsum = 0.0f;
-        for (int k = 0; k < nseg; ++k) {
-            const float a = fast_exp2(sm_ms[k * HP + h] - M);
-            lsum += a * sm_a[k * HP + h];
-            sm_a[k * HP + h] = a;
-        }
-        sm_ls[h] = 1.0f / lsum;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
-        const int h = idx / D;
-        const int d = idx - h * D;
-        if (h >= heads_here) continue;
-        float o = 0.0f;
-        int k = 0;
-        for (; k + 4 <= nseg; k += 4) {
-            float v[4];
+    for (int i = 0; i < np; ++i) {
+        const int unit = i == 0 ? pu0 : pu1;
+        const int uv = i == 0 ? pv0 : pv1;
+        const int kf = i == 0 ? pk0 : pk1;
+        const int npieces = i == 0 ? pn0 : pn1;
+        if (threadIdx.x == 0)
+            sm_last = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
+        __syncthreads();
+        const bool last = sm_last;
+        __syncthreads();                    // sm_last is written again for the next unit
+        if (!last) continue;
+        const int ub2 = unit % upb;
+        const int b2 = unit / upb;
+        const int j = ub2 / p.n_hg;
+        const int hgi = ub2 - j * p.n_hg;
+        const int h0 = j * p.G + hgi * HP;
+        const int heads_here = min(HP, p.G - hgi * HP);
+        // piece k of the unit sits in workgroup kf + k, in that workgroup's
+        // first slot, except the first piece when the workgroup's range
+        // began in an earlier unit (then it is the workgroup's last segment)
+        const int slot_first = 2 * kf + (uv > kf * tpw ? 1 : 0);
+        // each output reads every piece's (m, l, o) with independent loads,
+        // four pieces per round, and merges them with a running maximum
+        for (int idx = threadIdx.x; idx < HP * D; idx += NTH) {
+            const int h = idx / D;
+            const int d = idx - h * D;
+            if (h >= heads_here) continue;
+            float M = kNegInf, lsum = 0.0f, o = 0.0f;
+            for (int k0 = 0; k0 < npieces; k0 += 4) {
+                float mk[4], lk[4], ok[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = coherent_load(&p.ws_o[(slot0 + (size_t)(k + q) * HP + h) * D + d]);
+                for (int q = 0; q < 4; ++q) {
+                    const int k = min(k0 + q, npieces - 1);
+                    const size_t sl = (size_t)(k == 0 ? slot_first : 2 * (kf + k)) * HP + h;
+                    mk[q] = coherent_load(&p.ws_ml[sl * 2]);
+                    lk[q] = coherent_load(&p.ws_ml[sl * 2 + 1]);
+                    ok[q] = coherent_load(&p.ws_o[sl * D + d]);
+                }
+                float Mn = M;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o += sm_a[(k + q) * HP + h] * v[q];
+                for (int q = 0; q < 4; ++q)
+                    if (k0 + q < npieces) Mn = fmaxf(Mn, mk[q]);
+                const float ms = Mn == kNegInf ? 0.0f : Mn;
+                const float a = fast_exp2(M - ms);
+                lsum *= a;
+                o *= a;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (k0 + q < npieces) {
+                        const float w = fast_exp2(mk[q] - ms);
+                        lsum += w * lk[q];
+                        o += w * ok[q];
+                    }
+                }
+                M = Mn;
+            }
+            A::st(p.out, ((size_t)b2 * p.H + h0 + h) * D + d, o / lsum);
         }
-        for (; k < nseg; ++k) o += sm_a[k * HP + h] * coherent_load(&p.ws_o[(slot0 + (size_t)k * HP + h) * D + d]);
-        A::st(p.out, ((size_t)b * p.H + h0 + h) * D + d, o * sm_ls[h]);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();                    // LDS is reused by the next unit's merge
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1167,7 +1390,11 @@ constexpr int unroll_for(int gt) { return gt <= 2 ? 8 : 4; }
 constexpr bool wide_built(int kv, int gt) { return gt == 1 && kv != KV_I8; }
 
 constexpr int kGqaWaves = 8;
-constexpr int kGqaBlocksPerCu = 1;   // target pieces per CU (one 8-wave workgroup: about 83 KiB of LDS)
+constexpr int kGqaBlocksPerCu = 1;   // ranges per CU (one 8-wave workgroup: about 98 KiB of LDS at D = 128)
+// Virtual tiles charged per unit for a segment's fixed costs (a tile is 16
+// rows, about 0.3 us of one CU's share of the bandwidth); 16 measured best
+// over 0..32 on ragged lengths.
+constexpr int kGqaUnitCost = 16;
 
 template <int KV, int D, int HP, bool PG>
 hipError_t launch_gqa_t(const Params& p, hipStream_t s) {
@@ -1234,6 +1461,12 @@ int gqa_blocks_per_cu() {
     const char* e = std::getenv("FTM_GQA_BLOCKS_PER_CU");
     const int v = e ? std::atoi(e) : 0;
     return v > 0 && v <= 16 ? v : kGqaBlocksPerCu;
+}
+
+int gqa_unit_cost() {
+    const char* e = std::getenv("FTM_GQA_UNIT_COST");
+    const int v = e ? std::atoi(e) : -1;
+    return v >= 0 && v <= 64 ? v : kGqaUnitCost;
 }
 
 bool use_gqa_mfma(int kv, int gtile, int batch) {

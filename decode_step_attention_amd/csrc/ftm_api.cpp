@@ -426,22 +426,29 @@ int decode_impl(const Call& a) {
 
     const int kv_dtype = a.kv_dtype, head_dim = a.head_dim;
     const int units = a.batch * a.n_kv_heads * n_hg;
+    // the range schedule counts tiles (units x (tiles + charge)) in 32-bit
+    // integers: well inside that range, or the vector pass takes the step
+    const int unit_cost = ftm::gqa_unit_cost();
+    const int max_tiles = std::max(1, (a.step + 14) / 16);
     const bool balanced = ftm::use_gqa_mfma(kv_dtype, gtile, a.batch) &&
-                          (long long)a.batch * a.step * a.n_kv_heads * n_hg < (1LL << 31);
+                          (long long)a.batch * a.step * a.n_kv_heads * n_hg < (1LL << 31) &&
+                          (long long)units * (max_tiles + unit_cost) < (1LL << 30);
     Shape shape{4, 0};
     p.balanced = balanced;
     if (balanced) {
-        // grouped heads on the matrix cores: a fixed grid sharing the total
-        // work evenly; partial slots per unit, merged in the same launch
-        // target pieces (about W rows each) plus one spare per unit for rounding
-        p.S = cu_count(device) * ftm::gqa_blocks_per_cu() + units;
+        // grouped heads on the matrix cores: equal ranges of the units' tiles,
+        // one workgroup per CU (and at least one per sequence, which checks
+        // that sequence's length); two partial slots per workgroup, merged
+        // in the same launch
+        p.S = std::max(cu_count(device) * ftm::gqa_blocks_per_cu(), a.batch);
         p.chunk = 0;
         p.direct = 0;
-        // pieces of at least 256 positions, and at most 200 per unit (the
-        // merge keeps a unit's piece statistics in LDS)
-        p.seg_min = std::max(256, (a.step + 198) / 199);
-        p.seg_max = (a.step + p.seg_min - 1) / p.seg_min + 1;
-        const size_t slots = (size_t)units * p.seg_max * gtile;
+        p.unit_cost = unit_cost;
+        // ranges of at least 16 tiles, and long enough that no unit is cut
+        // into more than kGqaMaxPieces pieces
+        p.range_min = std::max(std::max(16, p.unit_cost + 1),
+                               (max_tiles + ftm::kGqaMaxPieces - 3) / (ftm::kGqaMaxPieces - 2));
+        const size_t slots = (size_t)2 * p.S * gtile;
         void* ws = nullptr;
         int st = get_workspace(device, stream, slots * (head_dim + 2) * sizeof(float), units, capturing,
                                &ws, &p.counters);

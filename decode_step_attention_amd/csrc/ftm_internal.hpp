@@ -32,9 +32,9 @@ struct Params {
     float qscale;           // log2(e) / sqrt(D), folded into the query
     // balanced grouped-query schedule (grid of S workgroups)
     int balanced;           // 1: grouped-query pass on the matrix cores
-    int* counters;          // [units] finished-segment counts, zero between calls
-    int seg_min;            // shortest slice a workgroup takes, in positions
-    int seg_max;            // partial slots per unit
+    int* counters;          // [units] finished-piece counts, zero between calls
+    int range_min;          // fewest 16-row tiles a workgroup's range holds
+    int unit_cost;          // virtual tiles charged per unit (segment prologue and epilogue)
     // paged cache (block_table null: contiguous [B, Hkv, Lmax, D] cache)
     const int32_t* block_table;   // [B, max_pages]: page of positions [i P, (i+1) P)
     int page_shift;         // log2(P), P >= 16
@@ -53,6 +53,11 @@ int tile_rows(int kv, int head_dim, int group_tile, int nw);
 bool use_gqa_mfma(int kv, int group_tile, int batch);
 // Workgroups per CU of the grouped-query pass.
 int gqa_blocks_per_cu();
+// Virtual tiles the range schedule charges per unit.
+int gqa_unit_cost();
+// Most pieces one unit is cut into by the range schedule (the merge of a
+// unit's pieces reads them four per round).
+constexpr int kGqaMaxPieces = 128;
 // Whether the 16-wave workgroup is built for this cache type and group tile.
 bool wide_ok(int kv, int group_tile);
 

@@ -191,6 +191,24 @@ def test_grouped_heads_balanced_schedule(ftm, B, Lmax, lens, kv):
         assert torch.equal(bits(o), bits(outs[0]))
 
 
+@pytest.mark.parametrize("cost,per_cu", [(0, 1), (5, 1), (14, 2), (3, 3)])
+def test_grouped_heads_range_boundaries(ftm, monkeypatch, cost, per_cu):
+    """The grouped-query schedule hands equal tile ranges to the workgroups;
+    the per-unit charge and the workgroups per CU move the range boundaries
+    inside units, so that ranges start and end mid-unit, hold several whole
+    units, or begin in one unit's charge.  Every placement meets the bar and
+    repeated calls give identical bits."""
+    monkeypatch.setenv("FTM_GQA_UNIT_COST", str(cost))
+    monkeypatch.setenv("FTM_GQA_BLOCKS_PER_CU", str(per_cu))
+    case = small("bf16", B=23, H=16, Hkv=2, Lmax=2500, lens=(1, 2500), seed=70 + cost)
+    run_and_compare(ftm, case, tag=f"ranges cost{cost} per_cu{per_cu}")
+    inp = W.make_inputs(case, "cuda")
+    outs = [gpu_call(ftm, inp, case) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(bits(o), bits(outs[0]))
+
+
 def test_grouped_heads_invalid_lengths(ftm):
     case = small("bf16", B=6, H=16, Hkv=2, Lmax=900, lens=(100, 800), seed=61)
     lens = W.seq_lens(case).clone()
