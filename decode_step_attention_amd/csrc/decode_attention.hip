@@ -22,6 +22,7 @@
 // ([pptc.cn/news/144085] section 3.4) and an INT8 cache converted back at
 // compute time ([pptc.cn/news/144085] section 3.1; [intelliparadigm.com
 // .../2131745] section 2.1).  Scores never leave registers.
+#include <cstdio>
 #include <cstdlib>
 
 #include "gfx950.hpp"
@@ -707,10 +708,13 @@ __device__ __forceinline__ void gqa_group(const Params& p, unsigned char* tiles,
     unsigned char* vtile = ktile + 16 * LD::KPITCH;
 
     // The group's tiles: segment 0's 16-position tiles, then segment 1's,
-    // numbered 0 .. ntot - 1.  Wave w takes tiles w, w + NW, w + 2 NW, ...
-    // in that order, across the segment boundary without a pause: a fixed
-    // assignment, so every call sums the same positions in the same order
-    // (the results do not depend on timing).  Per segment: the streamed end
+    // numbered 0 .. ntot - 1, dealt out in rounds of 4 (A + B) tiles: each
+    // of the four older waves (the first wave on each SIMD, which the SIMD
+    // serves first) takes A consecutive tiles of a round, each younger wave
+    // B.  A wave goes through its tiles in order, across the segment
+    // boundary without a pause.  A fixed assignment: every call sums the
+    // same positions in the same order (the results do not depend on
+    // timing).  Per segment: the streamed end
     // (the appended row is handled apart), its tiles, and the descriptor
     // inputs: contiguous, one descriptor per stream over rows [0, end) of the
     // unit; paged, one per tile (tiles never straddle a page, P >= 16).
@@ -834,10 +838,19 @@ __device__ __forceinline__ void gqa_group(const Params& p, unsigned char* tiles,
         nbv = *(const u32x4*)(bb + (p.bias ? (size_t)(p.H + p.Hkv + nj) * D : 0) + c * EPL);
     }
 
-    // the tile in each register set
-    int tidx[DEPTH];
+    // this wave's share of a round and where it starts; the tile of its
+    // k-th turn
+    static_assert(NW == 8, "four older and four younger waves");
+    const bool older = wave < 4;
+    const int share = older ? p.skew_a : p.skew_b;
+    const int first = older ? wave * p.skew_a : 4 * p.skew_a + (wave - 4) * p.skew_b;
+    const int round = 4 * (p.skew_a + p.skew_b);
+    auto tile_of = [&](int k) { return (k / share) * round + first + k % share; };
+    // the turn and tile in each register set
+    int turn[DEPTH], tidx[DEPTH];
     static_for<DEPTH>([&](auto set) {
-        tidx[decltype(set)::value] = wave + NW * decltype(set)::value;
+        turn[decltype(set)::value] = decltype(set)::value;
+        tidx[decltype(set)::value] = tile_of(decltype(set)::value);
         issue(set, tidx[decltype(set)::value]);
     });
     __builtin_amdgcn_sched_barrier(0);
@@ -996,7 +1009,8 @@ __device__ __forceinline__ void gqa_group(const Params& p, unsigned char* tiles,
             *(u32x4*)(vtile + (u * RPI + r) * LD::VPITCH + c * 16) = vr[SET][u];
         }
         __builtin_amdgcn_sched_barrier(0);
-        const int ni = cur + NW * DEPTH;
+        turn[SET] += DEPTH;
+        const int ni = tile_of(turn[SET]);
         issue(set, ni);
         tidx[SET] = ni;
         __builtin_amdgcn_sched_barrier(0);
@@ -1395,6 +1409,11 @@ constexpr int kGqaBlocksPerCu = 1;   // ranges per CU (one 8-wave workgroup: abo
 // rows, about 0.3 us of one CU's share of the bandwidth); 16 measured best
 // over 0..32 on ragged lengths.
 constexpr int kGqaUnitCost = 16;
+// Tiles per round for each older and each younger wave: a SIMD serves its
+// older wave first, and a younger wave left alone at the end streams more
+// slowly; 3:2 measured best of 1:1, 2:1, 3:2, 4:3 and 8:7 on ragged lengths.
+constexpr int kGqaSkewA = 3;
+constexpr int kGqaSkewB = 2;
 
 template <int KV, int D, int HP, bool PG>
 hipError_t launch_gqa_t(const Params& p, hipStream_t s) {
@@ -1461,6 +1480,17 @@ int gqa_blocks_per_cu() {
     const char* e = std::getenv("FTM_GQA_BLOCKS_PER_CU");
     const int v = e ? std::atoi(e) : 0;
     return v > 0 && v <= 16 ? v : kGqaBlocksPerCu;
+}
+
+void gqa_skew(int& a, int& b) {
+    a = kGqaSkewA;
+    b = kGqaSkewB;
+    const char* e = std::getenv("FTM_GQA_SKEW");
+    int x = 0, y = 0;
+    if (e && std::sscanf(e, "%d,%d", &x, &y) == 2 && x >= 1 && x <= 16 && y >= 1 && y <= 16) {
+        a = x;
+        b = y;
+    }
 }
 
 int gqa_unit_cost() {

@@ -444,6 +444,7 @@ int decode_impl(const Call& a) {
         p.chunk = 0;
         p.direct = 0;
         p.unit_cost = unit_cost;
+        ftm::gqa_skew(p.skew_a, p.skew_b);
         // ranges of at least 16 tiles, and long enough that no unit is cut
         // into more than kGqaMaxPieces pieces
         p.range_min = std::max(std::max(16, p.unit_cost + 1),

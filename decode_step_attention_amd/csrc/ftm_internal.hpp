@@ -35,6 +35,7 @@ struct Params {
     int* counters;          // [units] finished-piece counts, zero between calls
     int range_min;          // fewest 16-row tiles a workgroup's range holds
     int unit_cost;          // virtual tiles charged per unit (segment prologue and epilogue)
+    int skew_a, skew_b;     // tiles per round for each older / younger wave of a workgroup
     // paged cache (block_table null: contiguous [B, Hkv, Lmax, D] cache)
     const int32_t* block_table;   // [B, max_pages]: page of positions [i P, (i+1) P)
     int page_shift;         // log2(P), P >= 16
@@ -55,6 +56,8 @@ bool use_gqa_mfma(int kv, int group_tile, int batch);
 int gqa_blocks_per_cu();
 // Virtual tiles the range schedule charges per unit.
 int gqa_unit_cost();
+// Tiles per round for an older and a younger wave of the grouped-query pass.
+void gqa_skew(int& a, int& b);
 // Most pieces one unit is cut into by the range schedule (the merge of a
 // unit's pieces reads them four per round).
 constexpr int kGqaMaxPieces = 128;

@@ -209,6 +209,21 @@ def test_grouped_heads_range_boundaries(ftm, monkeypatch, cost, per_cu):
         assert torch.equal(bits(o), bits(outs[0]))
 
 
+@pytest.mark.parametrize("skew", ["1,1", "2,1", "8,7", "1,4"])
+def test_grouped_heads_wave_shares(ftm, monkeypatch, skew):
+    """The grouped-query pass deals each round of tiles out unevenly between
+    the older and the younger waves of a workgroup; every split covers each
+    tile once, meets the bar and gives identical bits on repeated calls."""
+    monkeypatch.setenv("FTM_GQA_SKEW", skew)
+    case = small("f16", B=9, H=16, Hkv=2, Lmax=3000, lens=(1, 3000), seed=80)
+    run_and_compare(ftm, case, tag=f"wave shares {skew}")
+    inp = W.make_inputs(case, "cuda")
+    outs = [gpu_call(ftm, inp, case) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(bits(o), bits(outs[0]))
+
+
 def test_grouped_heads_invalid_lengths(ftm):
     case = small("bf16", B=6, H=16, Hkv=2, Lmax=900, lens=(100, 800), seed=61)
     lens = W.seq_lens(case).clone()
