@@ -18,10 +18,12 @@
 //   step's S^T is computed between this step's exponentials.  The query
 //   enters exactly as stored (kept in registers) and the bias term b_q . k,
 //   the same for every query of a head, once per key, so every product is
-//   exact in fp32; log2(e)/sqrt(D) scales the fp32 scores.  The weights
-//   enter as hi/lo halves, so about 16 (bf16) or 22 (fp16) bits of each
-//   reach the accumulators, as in the decode pass.  Workgroups with the
-//   most keys are launched first.
+//   exact in fp32; log2(e)/sqrt(D) scales the fp32 scores.  fp16 weights
+//   are rounded once to nearest (11 significant bits, a relative error of
+//   at most 2^-12 each); bf16 weights, and those over INT8 codes, enter as
+//   hi/lo halves, so about 16 (bf16) or 22 (fp16) bits of each reach the
+//   accumulators, as in the decode pass.  Workgroups with the most keys are
+//   launched first.
 #include <cstdlib>
 
 #include "gfx950.hpp"
@@ -202,21 +204,34 @@ __global__ void __launch_bounds__(256) prefill_append_i8_kernel(const PrefillPar
     }
 }
 
-// hi + lo halves of eight softmax weights (0 <= x <= 2^kLazy): hi keeps the
-// leading 11 (fp16) or 8 (bf16) significant bits by truncation, so it
-// converts exactly (for x at least 2^-14 in fp16) and the fp32 residual
-// x - hi is exact; lo is that residual rounded to the half type.
-template <int KV>
+// Whether the softmax weights enter P.V as hi + lo halves.  bf16 keeps 8
+// significant bits, too few for the output bar when one key dominates.
+// fp16 keeps 11, enough with one rounding for values of the prompt's size;
+// the INT8 staging (SC) multiplies each weight by its key's V scale and
+// then by codes up to 127 (outputs of a few units, a sharp softmax), where
+// one rounding measured 2.9e-3 against the 2e-3 bar, so it keeps the split.
+template <int KV, bool SC> constexpr bool kWeightSplit = KV == KV_BF16 || SC;
+
+// The softmax weights (0 <= x <= 2^kLazy) as P operands.  Without a split
+// (fp16): x rounded to nearest, lo unused.  With one: hi keeps the leading
+// 11 (fp16) or 8 (bf16) significant bits by truncation, so it converts
+// exactly (for x at least 2^-14 in fp16) and the fp32 residual x - hi is
+// exact; lo is that residual rounded to the half type.
+template <int KV, bool SPLIT>
 __device__ __forceinline__ void split_weights(const float* x, typename Mfma<KV>::vec8& hi,
                                               typename Mfma<KV>::vec8& lo) {
     constexpr uint32_t kKeep = KV == KV_F16 ? 0xFFFFE000u : 0xFFFF0000u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float h = __uint_as_float(__float_as_uint(x[i]) & kKeep);
-        if constexpr (KV == KV_F16) {
+        if constexpr (KV == KV_F16 && !SPLIT) {
+            hi[i] = (_Float16)x[i];
+            lo[i] = (_Float16)0.0f;
+        } else if constexpr (KV == KV_F16) {
+            const float h = __uint_as_float(__float_as_uint(x[i]) & kKeep);
             hi[i] = (_Float16)h;
             lo[i] = (_Float16)(x[i] - h);
         } else {
+            const float h = __uint_as_float(__float_as_uint(x[i]) & kKeep);
             hi[i] = (__bf16)h;
             lo[i] = (__bf16)(x[i] - h);
         }
@@ -605,7 +620,7 @@ prefill_attn_kernel(const PrefillParams p) {
                     s[qb][4 + i] *= v1s[i];
                 }
             }
-            split_weights<KV>(s[qb], ph[qb], pl[qb]);
+            split_weights<KV, kWeightSplit<KV, SC>>(s[qb], ph[qb], pl[qb]);
         }
         // O^T += V^T P^T: A = V^T (row 16 tn + n, the slots' keys, read
         // down V's columns), B = P^T (this lane's slots for its query)
@@ -620,7 +635,7 @@ prefill_attn_kernel(const PrefillParams p) {
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) {
                 acc[qb][tn] = MF::mma32(va, ph[qb], acc[qb][tn]);
-                acc[qb][tn] = MF::mma32(va, pl[qb], acc[qb][tn]);
+                if constexpr (kWeightSplit<KV, SC>) acc[qb][tn] = MF::mma32(va, pl[qb], acc[qb][tn]);
             }
         }
         if constexpr (SC) fold_k_scale(snext, (u == 0 || u == 3) ? kscl0 : kscl1, (j + 1) % 2);

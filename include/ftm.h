@@ -227,9 +227,10 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
  * the matrix cores with fp32
  * accumulation: the query enters exactly as stored and the bias term
  * b_q . k separately (once per key and head), so the scores are exact
- * products summed in fp32 and then scaled; the softmax weights enter as hi
- * and lo halves, so about 22 (fp16) or 16 (bf16) bits of each reach the
- * accumulators.  Limits: batch up to 65535,
+ * products summed in fp32 and then scaled.  fp16 softmax weights are
+ * rounded once to nearest (11 significant bits); bf16 weights, and those
+ * over INT8 codes, enter as hi and lo halves, so about 16 (bf16) or 22
+ * (fp16) bits of each reach the accumulators.  Limits: batch up to 65535,
  * batch * n_heads below 2^31, prompt_len up to 65535 * 128.  Errors as for
  * ftm_decode_mha.
  */
