@@ -108,7 +108,7 @@ def cpu_baseline(case, inputs, lens, budget_s: float):
     sample_bytes = int(W.kv_bytes(case.with_(batch=nb), sl.tolist()))
     runs, total = 0, 0.0
     best = float("inf")
-    while runs < 3 or (total < budget_s and runs < 50):
+    while runs < 3 or (total < budget_s and runs < 1000):
         kc, vc = kc0.copy(), vc0.copy()
         sc = sc0.copy() if sc0 is not None else None
         t0 = time.perf_counter()
