@@ -663,19 +663,18 @@ template <int D> struct GqaLds {
 // next on its own, with no barrier between them.
 constexpr int kGqaMaxSeg = 2;
 
-// One segment: positions [pos0, pos1) of unit (b, j, hgi), and what the
-// merge of its pieces needs.
+// One segment: positions [pos0, pos1) of unit (b, j, hgi) of length L.
 struct GqaSeg {
     int b, j, hgi, L, pos0, pos1;
 };
 
 // Streams up to kGqaMaxSeg segments with the whole workgroup.  Each wave
-// takes the 16-position tiles wave, wave + NW, ... of every segment in
-// turn, with its K/V loads running DEPTH tiles ahead across segment
-// boundaries and one softmax state per segment in registers; a wave that
-// reaches the next segment starts on it at once.  At the end, per segment,
-// the waves' states and the appended row's (when the segment holds it) are
-// merged through LDS into `out` (a whole unit) or the piece's partial slot.
+// takes a fixed share of the segments' 16-position tiles, in order, with
+// its K/V loads running DEPTH tiles ahead across the segment boundary and
+// one softmax state per segment in registers; a wave that reaches the next
+// segment starts on it at once.  At the end, per segment, the waves' states
+// and the appended row's (when the segment holds it) are merged through LDS
+// into `out` (a whole unit) or the piece's partial slot.
 template <int KV, int D, int HP, int NW, bool PG>
 __device__ __forceinline__ void gqa_group(const Params& p, unsigned char* tiles, unsigned char* qbufs,
                                           float (*sm_m)[NW][HP], float (*sm_l)[NW][HP], float (*sm_nm)[HP],
@@ -714,10 +713,10 @@ __device__ __forceinline__ void gqa_group(const Params& p, unsigned char* tiles,
     // B.  A wave goes through its tiles in order, across the segment
     // boundary without a pause.  A fixed assignment: every call sums the
     // same positions in the same order (the results do not depend on
-    // timing).  Per segment: the streamed end
-    // (the appended row is handled apart), its tiles, and the descriptor
-    // inputs: contiguous, one descriptor per stream over rows [0, end) of the
-    // unit; paged, one per tile (tiles never straddle a page, P >= 16).
+    // timing).  Per segment: the streamed end (the appended row is handled
+    // apart), its tiles, and the descriptor inputs: contiguous, one
+    // descriptor per stream over rows [0, end) of the unit; paged, one per
+    // tile (tiles never straddle a page, P >= 16).
     static_assert(S == 2, "the tile numbering covers two segments");
     int send[S], ntl[S];
     size_t row0[S];                         // contiguous: the unit's first cache row
@@ -1411,9 +1410,10 @@ constexpr int kGqaBlocksPerCu = 1;   // ranges per CU (one 8-wave workgroup: abo
 constexpr int kGqaUnitCost = 16;
 // Tiles per round for each older and each younger wave: a SIMD serves its
 // older wave first, and a younger wave left alone at the end streams more
-// slowly; 3:2 measured best of 1:1, 2:1, 3:2, 4:3 and 8:7 on ragged lengths.
-constexpr int kGqaSkewA = 3;
-constexpr int kGqaSkewB = 2;
+// slowly; 2:1 and 3:2 measured best of 1:1, 2:1, 3:2, 4:3 and 8:7 on ragged
+// lengths, 2:1 by a little with the charge of 16.
+constexpr int kGqaSkewA = 2;
+constexpr int kGqaSkewB = 1;
 
 template <int KV, int D, int HP, bool PG>
 hipError_t launch_gqa_t(const Params& p, hipStream_t s) {
