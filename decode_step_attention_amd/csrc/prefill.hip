@@ -211,6 +211,11 @@ __global__ void __launch_bounds__(256) prefill_append_i8_kernel(const PrefillPar
 // then by codes up to 127 (outputs of a few units, a sharp softmax), where
 // one rounding measured 2.9e-3 against the 2e-3 bar, so it keeps the split.
 template <int KV, bool SC> constexpr bool kWeightSplit = KV == KV_BF16 || SC;
+// Whether the running sum of the weights is taken on the matrix cores, as
+// P.1 (an all-ones A operand) accumulated beside O: when the weights enter
+// P.V once rounded, the sum then uses the very weights the output does,
+// and it costs one MFMA per query block and step instead of 16 adds.
+template <int KV, bool SC> constexpr bool kSumOnMfma = !kWeightSplit<KV, SC>;
 
 // The softmax weights (0 <= x <= 2^kLazy) as P operands.  Without a split
 // (fp16): x rounded to nearest, lo unused.  With one: hi keeps the leading
@@ -430,11 +435,13 @@ prefill_attn_kernel(const PrefillParams p) {
     // not depend on the reference).  thr is that bound in unscaled units.
     float m[kQB], l[kQB], thr[kQB];         // l: this lane's share of the sum
     f32x4 acc[kQB][DT];                     // O^T[16 tn + 4g + i][query tq + 16 qb + n]
+    f32x4 lsum[kQB];                        // on the matrix cores: the sum for query tq + 16 qb + n
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         m[qb] = kNegInfP;
         thr[qb] = kNegInfP;
         l[qb] = 0.0f;
+        lsum[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int tn = 0; tn < DT; ++tn) acc[qb][tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -590,7 +597,12 @@ prefill_attn_kernel(const PrefillParams p) {
                 const float alpha = fast_exp2(m[qb] - (mn == kNegInfP ? 0.0f : mn));
                 m[qb] = mn;
                 thr[qb] = (mn + kLazy) * inv_c;
-                l[qb] *= alpha;
+                if constexpr (kSumOnMfma<KV, SC>) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) lsum[qb][i] *= alpha;
+                } else {
+                    l[qb] *= alpha;
+                }
 #pragma unroll
                 for (int tn = 0; tn < DT; ++tn)
 #pragma unroll
@@ -609,7 +621,7 @@ prefill_attn_kernel(const PrefillParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 s[qb][e] = fast_exp2(__builtin_fmaf(s[qb][e], c, -ms));
-                l[qb] += s[qb][e];
+                if constexpr (!kSumOnMfma<KV, SC>) l[qb] += s[qb][e];
             }
             if constexpr (SC) {             // code x scale: the key's V scale on its weight
                 const float* vs = (const float*)(((u / 2) ? vscl1 : vscl0) + wave * 256) + 32 * (j % 2) + 4 * g;
@@ -638,6 +650,13 @@ prefill_attn_kernel(const PrefillParams p) {
                 if constexpr (kWeightSplit<KV, SC>) acc[qb][tn] = MF::mma32(va, pl[qb], acc[qb][tn]);
             }
         }
+        if constexpr (kSumOnMfma<KV, SC>) {
+            vec8 ones;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) lsum[qb] = MF::mma32(ones, ph[qb], lsum[qb]);
+        }
         if constexpr (SC) fold_k_scale(snext, (u == 0 || u == 3) ? kscl0 : kscl1, (j + 1) % 2);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
@@ -662,7 +681,7 @@ prefill_attn_kernel(const PrefillParams p) {
     // (8 bytes) per lane and tile
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-        const float inv = 1.0f / column_sum(l[qb]);
+        const float inv = 1.0f / (kSumOnMfma<KV, SC> ? lsum[qb][0] : column_sum(l[qb]));
         const int t = tq + 16 * qb + n;
         if (t < Sb) {
             uint16_t* orow = (uint16_t*)p.out + (((size_t)b * p.S + t) * p.H + h) * D + 4 * g;
