@@ -49,18 +49,22 @@ template <int ACT> struct QMma {
 // MT: batch tiles of 16 rows (B <= 16 MT).  FT: 16-feature column tiles
 // per workgroup, each wave computing all of them over its k range, so that
 // one load of x serves FT products (FT = MT keeps the bytes of x read per
-// weight byte at one).  A wave iteration covers KIT = 256 / FT k: 8 KiB of
-// weights whatever FT.
+// weight byte at one).  A wave iteration covers KIT = 256 / FT k (8 KiB of
+// weights in 8 loads) for FT = 1, 2, 4, and KIT = 128 for FT = 3 (12 KiB in
+// 12 loads).  The last workgroup may hold fewer than 16 FT features: its
+// weight rows past the end read as zero and its tiles past the end are not
+// written.
 template <int ACT, int MT, int FT>
 __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p) {
     using M = QMma<ACT>;
     constexpr int COLS = 16 * FT;           // output features per workgroup
-    constexpr int KIT = 256 / FT;           // k per wave iteration
+    constexpr int KIT = FT == 3 ? 128 : 256 / FT;   // k per wave iteration
     constexpr int KS = KIT / 32;            // MFMA k-steps per iteration
     constexpr int PITCH = KIT * 2 + 16;     // LDS row pitch: 16-byte reads of 16 rows hit distinct banks
     constexpr int LPRW = KIT / 8;           // weight loads: lanes per row (16 bytes each)
-    constexpr int RPIW = 64 / LPRW;         // weight loads: rows per instruction (8 instructions)
-    static_assert(8 * RPIW == COLS, "8 loads cover the workgroup's rows");
+    constexpr int RPIW = 64 / LPRW;         // weight loads: rows per instruction
+    constexpr int NLD = COLS / RPIW;        // weight loads per iteration
+    static_assert(NLD * RPIW == COLS, "the loads cover the workgroup's rows");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;                // MFMA operands: k group
@@ -68,12 +72,13 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
     const int lrow = lane / LPRW;           // weight loads: row within an instruction's rows
     const int lcol = lane % LPRW;           // weight loads: 16-byte chunk within the row
     const int f0 = blockIdx.x * COLS;
+    const int n_out = (p.H + 2 * p.Hkv) * p.D;
     const int nit = p.hidden / KIT;
     const int it0 = wave * nit / kWaves;
     const int it1 = (wave + 1) * nit / kWaves;
     const uint32_t row_bytes = (uint32_t)p.hidden * 2;
     // the workgroup's weight rows; x rows past the batch read as zero
-    const auto wrs = make_rsrc((const char*)p.w + (size_t)f0 * row_bytes, COLS * row_bytes);
+    const auto wrs = make_rsrc((const char*)p.w + (size_t)f0 * row_bytes, (uint32_t)min(COLS, n_out - f0) * row_bytes);
     const auto xrs = make_rsrc(p.x, (uint32_t)p.B * row_bytes);
 
     // per-wave weight tiles; after the loop, the partial sums of the
@@ -86,11 +91,11 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
     // iterations outside [it0, it1) take an offset past the descriptor's
     // range: their loads fetch nothing, so the prefetch needs no branch
     // (a branch around it makes the compiler wait for every load in flight)
-    u32x4 wr[8];
+    u32x4 wr[NLD];
     auto issue_w = [&](int it) {
         const uint32_t koff = it < it1 ? (uint32_t)it * (KIT * 2) : 0x40000000u;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < NLD; ++u)
             wr[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (RPIW * u + lrow) * row_bytes + koff + lcol * 16,
                                                           0, kStream);
     };
@@ -116,7 +121,7 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
         // stage this iteration's weights, then send the next iteration's out
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int u = 0; u < 8; ++u) *(u32x4*)(tile + (RPIW * u + lrow) * PITCH + lcol * 16) = wr[u];
+        for (int u = 0; u < NLD; ++u) *(u32x4*)(tile + (RPIW * u + lrow) * PITCH + lcol * 16) = wr[u];
         __builtin_amdgcn_sched_barrier(0);
         issue_w(it + 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -165,6 +170,7 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
     for (int ft = 0; ft < FT; ++ft) {
         const int f = f0 + 16 * ft + n;
         const int fb = f0 + 16 * ft;        // the tile's first feature, the same in every lane
+        if (fb >= n_out) break;             // past the last feature (n_out is a multiple of 16)
         void* dst;
         int width, col;
         if (fb < qd) {
@@ -186,23 +192,34 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
     }
 }
 
-// Column tiles per workgroup: four (x read once per weight byte up to four
-// batch tiles, 128-byte weight row segments) unless that leaves fewer
-// workgroups than half the CUs.  FTM_QKV_COLUMN_TILES (1, 2 or 4) forces
-// the choice.
+// Column tiles per workgroup.  Every CU streams weights at about the same
+// rate, so the time goes with (rounds of workgroups over the CUs) x FT; the
+// choice minimises that, and on a tie takes the larger FT (x read from L2
+// fewer times).  On 256 CUs: four for 15360 features, three for 12288 and
+// for 10240 (256 and 214 workgroups where four gave 192 and 160).
+// FTM_QKV_COLUMN_TILES (1 to 4) forces the choice.
 int column_tiles(int n_out, int n_cu) {
     const char* e = std::getenv("FTM_QKV_COLUMN_TILES");
     const int forced = e ? std::atoi(e) : 0;
-    if (forced == 1 || forced == 2 || forced == 4) return forced;
-    int ft = 4;
-    while (ft > 1 && 2 * (n_out / (16 * ft)) < n_cu) ft /= 2;
-    return ft;
+    if (forced >= 1 && forced <= 4) return forced;
+    int best = 4;
+    long best_cost = -1;
+    for (int ft = 4; ft >= 1; --ft) {
+        const long wgs = (n_out + 16 * ft - 1) / (16 * ft);
+        const long cost = (wgs + n_cu - 1) / n_cu * ft;
+        if (best_cost < 0 || cost < best_cost) {
+            best = ft;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 template <int ACT, int MT, int FT>
 hipError_t launch_mf(const QkvParams& p, hipStream_t s) {
     const int n_out = (p.H + 2 * p.Hkv) * p.D;
-    hipLaunchKernelGGL((qkv_proj_kernel<ACT, MT, FT>), dim3(n_out / (16 * FT)), dim3(64 * kWaves), 0, s, p);
+    hipLaunchKernelGGL((qkv_proj_kernel<ACT, MT, FT>), dim3((n_out + 16 * FT - 1) / (16 * FT)), dim3(64 * kWaves), 0,
+                       s, p);
     return hipGetLastError();
 }
 
@@ -211,6 +228,7 @@ hipError_t launch_m(const QkvParams& p, int ft, hipStream_t s) {
     switch (ft) {
     case 1: return launch_mf<ACT, MT, 1>(p, s);
     case 2: return launch_mf<ACT, MT, 2>(p, s);
+    case 3: return launch_mf<ACT, MT, 3>(p, s);
     case 4: return launch_mf<ACT, MT, 4>(p, s);
     default: return hipErrorInvalidValue;
     }
@@ -220,9 +238,8 @@ template <int ACT>
 hipError_t launch_t(const QkvParams& p, int n_cu, hipStream_t s) {
     const int n_out = (p.H + 2 * p.Hkv) * p.D;
     const int mt = (p.B + 15) / 16;
-    int ft = column_tiles(n_out, n_cu);
-    while (ft > 1 && n_out % (16 * ft) != 0) ft /= 2;
-    if (p.hidden % (256 / ft) != 0) return hipErrorInvalidValue;
+    const int ft = column_tiles(n_out, n_cu);
+    if (p.hidden % 256 != 0 || n_out % 16 != 0) return hipErrorInvalidValue;
     switch (mt) {
     case 1: return launch_m<ACT, 1>(p, ft, s);
     case 2: return launch_m<ACT, 2>(p, ft, s);

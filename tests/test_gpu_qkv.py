@@ -91,7 +91,7 @@ def test_projection_parity(ftm, dt, B, H, Hkv, D, hidden, with_bias):
     check_proj(case, got, ref, absdot, f"{dt} B{B} H{H}/{Hkv} D{D} hidden{hidden} bias{with_bias}")
 
 
-@pytest.mark.parametrize("ft", ["1", "2", "4"])
+@pytest.mark.parametrize("ft", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("dt,B,hidden", [("bf16", 16, 1024), ("f16", 40, 768), ("bf16", 64, 2048)])
 def test_column_tiles(ftm, monkeypatch, ft, dt, B, hidden):
     """Every number of column tiles per workgroup (forced), with one to four
@@ -102,6 +102,33 @@ def test_column_tiles(ftm, monkeypatch, ft, dt, B, hidden):
     got = run(ftm, inp, case)
     ref, absdot = reference(inp, case)
     check_proj(case, got, ref, absdot, f"{dt} B{B} hidden{hidden} column tiles {ft}")
+
+
+@pytest.mark.parametrize("ft", ["3", "4"])
+@pytest.mark.parametrize("dt,B,H,Hkv,D,hidden", [("bf16", 9, 8, 1, 64, 768),     # 640 features
+                                                 ("f16", 33, 6, 2, 80, 512),     # 800 features
+                                                 ("bf16", 64, 5, 5, 128, 1024)]) # 1920: 48 x 40
+def test_partial_last_workgroup(ftm, monkeypatch, ft, dt, B, H, Hkv, D, hidden):
+    """Feature counts that are not a multiple of the workgroup's 16 FT
+    columns: the last workgroup's rows past the end read as zero and its
+    tiles past the end are not written (every output is checked, and the
+    buffers past the outputs are not touched)."""
+    monkeypatch.setenv("FTM_QKV_COLUMN_TILES", ft)
+    case = W.ProjCase("t", B, H, Hkv, D, hidden, dt, seed=41 + B + D)
+    inp = W.make_proj_inputs(case)
+    tdt = W.TORCH_DTYPES[dt]
+    g = {k: v.cuda() for k, v in inp.items()}
+    # each output is the head of a buffer whose tail holds a sentinel
+    sizes = [B * H * D, B * Hkv * D, B * Hkv * D]
+    bufs = [torch.full((n + 4096,), 12345.0, dtype=tdt, device="cuda") for n in sizes]
+    q, k, v = (bufs[0][:sizes[0]].view(B, H, D), bufs[1][:sizes[1]].view(B, Hkv, D),
+               bufs[2][:sizes[2]].view(B, Hkv, D))
+    ftm.ftm_qkv_proj(g["x"], g["w"], g["bias"], q, k, v)
+    torch.cuda.synchronize()
+    for buf, n in zip(bufs, sizes):
+        assert bool((buf[n:] == 12345.0).all()), f"ft {ft}: a write past an output buffer"
+    ref, absdot = reference(inp, case)
+    check_proj(case, (q, k, v), ref, absdot, f"{dt} B{B} H{H}/{Hkv} D{D} partial last workgroup ft {ft}")
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
