@@ -162,12 +162,17 @@ struct Shape {
 Shape choose_shape(int kv, int head_dim, int gtile, int units, int step, int n_cu) {
     int nw = g_waves.load();
     if (nw == 0) nw = env_int("FTM_WAVES", 0);
+    bool short_pass = false;
     if (nw != 4 && nw != 16) {
         nw = (ftm::wide_ok(kv, gtile) && units < 2 * n_cu) ? 16 : 4;
-        // a sequence that one 4-wave iteration covers leaves most of a
-        // 16-wave workgroup idle: the 4-wave single pass is shorter (batch 1,
-        // 8 heads x 64, fp32, 128 positions: 3.8 against 4.9 us per step)
-        if (nw == 16 && step <= ftm::tile_rows(kv, head_dim, gtile, 4)) nw = 4;
+        // a short sequence leaves much of a 16-wave workgroup idle: up to
+        // four 4-wave iterations, a 4-wave single pass is shorter (7b layer
+        // shape at 128 / 256 / 512 positions: 6.6 / 9.1 / 13.9 against
+        // 7.6 / 9.9 / 14.4 us; equal at 768, slower at 1024)
+        if (nw == 16 && step <= 4 * ftm::tile_rows(kv, head_dim, gtile, 4)) {
+            nw = 4;
+            short_pass = true;
+        }
     }
     if (nw == 16 && !ftm::wide_ok(kv, gtile)) nw = 4;
     const int tile = ftm::tile_rows(kv, head_dim, gtile, nw);
@@ -176,6 +181,8 @@ Shape choose_shape(int kv, int head_dim, int gtile, int units, int step, int n_c
     int chunk;
     if (forced > 0) {
         chunk = forced;
+    } else if (short_pass) {
+        chunk = step;                       // one pass per (b, j): no combine
     } else {
         const long target_blocks = nw == 16 ? n_cu : 4L * n_cu;
         long want_s = (target_blocks + units - 1) / units;
