@@ -22,6 +22,7 @@
 // ([pptc.cn/news/144085] section 3.4) and an INT8 cache converted back at
 // compute time ([pptc.cn/news/144085] section 3.1; [intelliparadigm.com
 // .../2131745] section 2.1).  Scores never leave registers.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 
@@ -1477,33 +1478,26 @@ int group_tile(int G) {
 }
 
 int gqa_blocks_per_cu() {
-    const char* e = std::getenv("FTM_GQA_BLOCKS_PER_CU");
-    const int v = e ? std::atoi(e) : 0;
+    const int v = tuning().gqa_blocks_per_cu;
     return v > 0 && v <= 16 ? v : kGqaBlocksPerCu;
 }
 
 void gqa_skew(int& a, int& b) {
-    a = kGqaSkewA;
-    b = kGqaSkewB;
-    const char* e = std::getenv("FTM_GQA_SKEW");
-    int x = 0, y = 0;
-    if (e && std::sscanf(e, "%d,%d", &x, &y) == 2 && x >= 1 && x <= 16 && y >= 1 && y <= 16) {
-        a = x;
-        b = y;
-    }
+    const Tuning& t = tuning();
+    const bool set = t.gqa_skew_a >= 1 && t.gqa_skew_a <= 16 && t.gqa_skew_b >= 1 && t.gqa_skew_b <= 16;
+    a = set ? t.gqa_skew_a : kGqaSkewA;
+    b = set ? t.gqa_skew_b : kGqaSkewB;
 }
 
 int gqa_unit_cost() {
-    const char* e = std::getenv("FTM_GQA_UNIT_COST");
-    const int v = e ? std::atoi(e) : -1;
+    const int v = tuning().gqa_unit_cost;
     return v >= 0 && v <= 64 ? v : kGqaUnitCost;
 }
 
 bool use_gqa_mfma(int kv, int gtile, int batch) {
     if (!((kv == KV_F16 || kv == KV_BF16) && (gtile == 4 || gtile == 8))) return false;
     if (batch > kGqaMaxBatch) return false;
-    const char* e = std::getenv("FTM_GQA_VALU");
-    return !(e && *e == '1');
+    return tuning().gqa_valu != 1;
 }
 
 int tile_rows(int kv, int head_dim, int gtile, int nw) {
@@ -1522,6 +1516,19 @@ hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, in
     case KV_I8: return dispatch_d<KV_I8>(p, head_dim, gtile, nw, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+namespace {
+__global__ void __launch_bounds__(256) zero_ints_kernel(int* dst, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_zero_ints(int* dst, size_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = std::min<size_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s) {

@@ -29,32 +29,26 @@ int fail(int status, const std::string& msg) {
 // ---------------------------------------------------------------------------
 // Workspace: one growing buffer per (device, stream).  Reused across calls
 // ([lpnh.cn/news/2765398] section 2.2: intermediate buffers are pooled and
-// recycled instead of allocated per layer).
+// recycled instead of allocated per layer).  A call that needs more
+// allocates a larger buffer (at least twice the old one, so the kept
+// buffers together stay below the current one) and keeps the old one
+// until ftm_release_workspaces: hipFree would wait for the device, and
+// work already enqueued, or a captured graph, may still use it.
 // ---------------------------------------------------------------------------
 struct Workspace {
     void* ptr = nullptr;        // split partials
     size_t bytes = 0;
     int* counters = nullptr;    // per-unit counts of the balanced schedule, zero between calls
     size_t n_counters = 0;
-    bool captured = false;      // a graph may hold these buffers: retire them, never free
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-// Buffers replaced while a captured graph may still use them; freed only
-// by ftm_release_workspaces.
+// Buffers that larger ones replaced, freed by ftm_release_workspaces.
 std::vector<std::pair<int, void*>> g_retired;
 
-// Frees `ptr`, or keeps it for ftm_release_workspaces when a graph may use it.
-hipError_t drop_buffer(int device, void* ptr, bool captured) {
-    if (captured) {
-        g_retired.push_back({device, ptr});
-        return hipSuccess;
-    }
-    return hipFree(ptr);
-}
-
-// Partials buffer of at least `bytes` and, when n_counters > 0, a zeroed
-// counter array of at least that many ints, for (device, stream).
+// Partials buffer of at least `bytes` and, when n_counters > 0, a counter
+// array of at least that many ints, zero when the kernels on `stream`
+// reach it, for (device, stream).  Never waits for the device.
 int get_workspace(int device, hipStream_t stream, size_t bytes, size_t n_counters, bool capturing,
                   void** out, int** counters) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -63,43 +57,35 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t n_counter
         return fail(FTM_ERR_INVALID_ARG,
                     "the stream is being captured and its workspace would have to grow: make one "
                     "call of this shape on this stream before capturing");
-    if (capturing) w.captured = true;
     if (w.bytes < bytes) {
-        if (w.ptr) {
-            // hipFree waits for the device, so work still using the old
-            // buffer has finished before it goes away
-            hipError_t e = drop_buffer(device, w.ptr, w.captured);
-            w.ptr = nullptr;
-            w.bytes = 0;
-            if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipFree: ") + hipGetErrorString(e));
-        }
-        size_t grow = bytes + bytes / 4;
-        hipError_t e = hipMalloc(&w.ptr, grow);
+        const size_t grow = std::max(bytes + bytes / 4, 2 * w.bytes);
+        void* np = nullptr;
+        hipError_t e = hipMalloc(&np, grow);
         if (e != hipSuccess) {
-            w.ptr = nullptr;
             (void)hipGetLastError();
             return fail(FTM_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(grow) +
                                                    " bytes: " + hipGetErrorString(e));
         }
+        if (w.ptr) g_retired.push_back({device, w.ptr});
+        w.ptr = np;
         w.bytes = grow;
     }
     if (w.n_counters < n_counters) {
-        if (w.counters) {
-            hipError_t e = drop_buffer(device, w.counters, w.captured);
-            w.counters = nullptr;
-            w.n_counters = 0;
-            if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipFree: ") + hipGetErrorString(e));
-        }
-        size_t grow = n_counters + n_counters / 4 + 64;
-        hipError_t e = hipMalloc(&w.counters, grow * sizeof(int));
-        if (e == hipSuccess) e = hipMemset(w.counters, 0, grow * sizeof(int));
-        if (e == hipSuccess) e = hipDeviceSynchronize();
+        const size_t grow = std::max(n_counters + n_counters / 4 + 64, 2 * w.n_counters);
+        int* nc = nullptr;
+        hipError_t e = hipMalloc(&nc, grow * sizeof(int));
         if (e != hipSuccess) {
-            if (w.counters) (void)hipFree(w.counters);
-            w.counters = nullptr;
             (void)hipGetLastError();
             return fail(FTM_ERR_OUT_OF_MEMORY, std::string("counter array: ") + hipGetErrorString(e));
         }
+        // cleared on the call's stream, ahead of the kernel that uses it
+        e = ftm::launch_zero_ints(nc, grow, stream);
+        if (e != hipSuccess) {
+            g_retired.push_back({device, nc});
+            return fail(FTM_ERR_HIP, std::string("counter clear: ") + hipGetErrorString(e));
+        }
+        if (w.counters) g_retired.push_back({device, w.counters});
+        w.counters = nc;
         w.n_counters = grow;
     }
     *out = w.ptr;
@@ -145,6 +131,30 @@ int env_int(const char* name, int dflt) {
     return v && *v ? std::atoi(v) : dflt;
 }
 
+ftm::Tuning read_tuning() {
+    ftm::Tuning t{};
+    t.validate = env_int("FTM_VALIDATE", 0);
+    t.waves = env_int("FTM_WAVES", 0);
+    t.split_chunk = env_int("FTM_SPLIT_CHUNK", 0);
+    t.gqa_valu = env_int("FTM_GQA_VALU", 0);
+    t.gqa_blocks_per_cu = env_int("FTM_GQA_BLOCKS_PER_CU", 0);
+    t.gqa_unit_cost = env_int("FTM_GQA_UNIT_COST", -1);
+    t.gqa_skew_a = t.gqa_skew_b = 0;
+    if (const char* e = std::getenv("FTM_GQA_SKEW")) {
+        int a = 0, b = 0;
+        if (std::sscanf(e, "%d,%d", &a, &b) == 2) {
+            t.gqa_skew_a = a;
+            t.gqa_skew_b = b;
+        }
+    }
+    t.qkv_column_tiles = env_int("FTM_QKV_COLUMN_TILES", 0);
+    return t;
+}
+
+// The current settings.  A reload publishes a new copy and leaves the old
+// one in place (a reader may still hold it; reloads are rare).
+std::atomic<const ftm::Tuning*> g_tuning{nullptr};
+
 // Launch shape: waves per workgroup and chunk length.
 //
 // The kernel is bound by HBM bandwidth, which needs about 64 KiB of loads in
@@ -161,7 +171,7 @@ struct Shape {
 
 Shape choose_shape(int kv, int head_dim, int gtile, int units, int step, int n_cu) {
     int nw = g_waves.load();
-    if (nw == 0) nw = env_int("FTM_WAVES", 0);
+    if (nw == 0) nw = ftm::tuning().waves;
     bool short_pass = false;
     if (nw != 4 && nw != 16) {
         nw = (ftm::wide_ok(kv, gtile) && units < 2 * n_cu) ? 16 : 4;
@@ -177,7 +187,7 @@ Shape choose_shape(int kv, int head_dim, int gtile, int units, int step, int n_c
     if (nw == 16 && !ftm::wide_ok(kv, gtile)) nw = 4;
     const int tile = ftm::tile_rows(kv, head_dim, gtile, nw);
     int forced = g_split_chunk.load();
-    if (forced == 0) forced = env_int("FTM_SPLIT_CHUNK", 0);
+    if (forced == 0) forced = ftm::tuning().split_chunk;
     int chunk;
     if (forced > 0) {
         chunk = forced;
@@ -222,6 +232,16 @@ struct Call {
 
 }  // namespace
 
+const ftm::Tuning& ftm::tuning() {
+    const Tuning* t = g_tuning.load(std::memory_order_acquire);
+    if (t) return *t;
+    const Tuning* fresh = new Tuning(read_tuning());
+    const Tuning* expected = nullptr;
+    if (g_tuning.compare_exchange_strong(expected, fresh, std::memory_order_acq_rel)) return *fresh;
+    delete fresh;
+    return *expected;
+}
+
 // A captured sequence of calls, instantiated for replay.
 struct ftm_graph_s {
     hipGraph_t graph;
@@ -234,7 +254,7 @@ const char* ftm_version(void) { return "libftm 0.1 (gfx950)"; }
 
 const char* ftm_last_error(void) { return g_last_error.c_str(); }
 
-size_t ftm_kv_cache_bytes(int batch, int n_kv_heads, int max_seq_len, int head_dim, int kv_dtype) {
+size_t ftm_kv_cache_bytes(int batch, int n_kv_heads, int max_seq_len, int head_dim, ftm_dtype kv_dtype) {
     if (batch < 1 || n_kv_heads < 1 || max_seq_len < 1 || head_dim < 1) return 0;
     size_t elem;
     switch (kv_dtype) {
@@ -260,33 +280,24 @@ int ftm_set_workgroup_waves(int waves) {
 
 void ftm_release_workspaces(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
+    std::vector<std::pair<int, void*>> all;
+    all.swap(g_retired);
     for (auto& kv : g_ws) {
-        if (kv.second.ptr) {
-            int cur = 0;
-            (void)hipGetDevice(&cur);
-            (void)hipSetDevice(kv.first.first);
-            (void)hipFree(kv.second.ptr);
-            (void)hipSetDevice(cur);
-        }
+        if (kv.second.ptr) all.push_back({kv.first.first, kv.second.ptr});
+        if (kv.second.counters) all.push_back({kv.first.first, kv.second.counters});
     }
-    for (auto& kv : g_ws) {
-        if (kv.second.counters) {
-            int cur = 0;
-            (void)hipGetDevice(&cur);
-            (void)hipSetDevice(kv.first.first);
-            (void)hipFree(kv.second.counters);
-            (void)hipSetDevice(cur);
-        }
-    }
-    for (auto& r : g_retired) {
-        int cur = 0;
-        (void)hipGetDevice(&cur);
+    g_ws.clear();
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (auto& r : all) {
         (void)hipSetDevice(r.first);
         (void)hipFree(r.second);
-        (void)hipSetDevice(cur);
     }
-    g_retired.clear();
-    g_ws.clear();
+    (void)hipSetDevice(cur);
+}
+
+void ftm_tuning_reload(void) {
+    g_tuning.store(new ftm::Tuning(read_tuning()), std::memory_order_release);
 }
 
 int ftm_timing_enable(int capacity) {
@@ -398,7 +409,7 @@ int decode_impl(const Call& a) {
         capturing = cs != hipStreamCaptureStatusNone;
     }
 
-    if (env_int("FTM_VALIDATE", 0) && a.seq_lens) {
+    if (ftm::tuning().validate && a.seq_lens) {
         if (capturing)
             return fail(FTM_ERR_INVALID_ARG, "FTM_VALIDATE reads seq_lens on the host and cannot run under stream capture");
         std::vector<int32_t> h(a.batch);
@@ -508,7 +519,7 @@ extern "C" {
 int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                    void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
                    int max_seq_len, int step, int n_heads, int n_kv_heads, int head_dim,
-                   int kv_dtype, float* kv_scales, void* out, void* stream_ptr) {
+                   ftm_dtype kv_dtype, float* kv_scales, void* out, hipStream_t stream_ptr) {
     if (max_seq_len < 1) return fail(FTM_ERR_INVALID_ARG, "max_seq_len must be >= 1");
     int st = check_common(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len,
                           step, n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales, out, "max_seq_len");
@@ -523,8 +534,8 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
 int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                          void* k_pages, void* v_pages, const int32_t* block_table, int n_pages,
                          int page_size, int max_pages_per_seq, const int32_t* seq_lens, int batch,
-                         int step, int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
-                         float* kv_scales, void* out, void* stream_ptr) {
+                         int step, int n_heads, int n_kv_heads, int head_dim, ftm_dtype kv_dtype,
+                         float* kv_scales, void* out, hipStream_t stream_ptr) {
     if (!block_table) return fail(FTM_ERR_INVALID_ARG, "block_table is NULL");
     if (((uintptr_t)block_table & 3u) != 0) return fail(FTM_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
     if (n_pages < 1 || max_pages_per_seq < 1)
@@ -548,8 +559,8 @@ int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new, co
 }
 
 int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k_new, void* v_new,
-                 int batch, int hidden, int n_heads, int n_kv_heads, int head_dim, int act_dtype,
-                 void* stream_ptr) {
+                 int batch, int hidden, int n_heads, int n_kv_heads, int head_dim, ftm_dtype act_dtype,
+                 hipStream_t stream_ptr) {
     if (!x || !w || !q || !k_new || !v_new)
         return fail(FTM_ERR_INVALID_ARG, "a required pointer (x, w, q, k_new, v_new) is NULL");
     if (batch < 1 || hidden < 1 || n_heads < 1 || n_kv_heads < 1 || head_dim < 1)
@@ -688,8 +699,8 @@ extern "C" {
 
 int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                     void* k_cache, void* v_cache, const int32_t* seq_lens, int batch, int max_seq_len,
-                    int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype, float* kv_scales,
-                    void* out, void* stream_ptr) {
+                    int prompt_len, int n_heads, int n_kv_heads, int head_dim, ftm_dtype kv_dtype,
+                    float* kv_scales, void* out, hipStream_t stream_ptr) {
     return prefill_impl(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len, "max_seq_len",
                         prompt_len, n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales, out, stream_ptr, nullptr, 0,
                         0, 0);
@@ -698,8 +709,8 @@ int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const v
 int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                           void* k_pages, void* v_pages, const int32_t* block_table, int n_pages, int page_size,
                           int max_pages_per_seq, const int32_t* seq_lens, int batch, int prompt_len, int n_heads,
-                          int n_kv_heads, int head_dim, int kv_dtype, float* kv_scales, void* out,
-                          void* stream_ptr) {
+                          int n_kv_heads, int head_dim, ftm_dtype kv_dtype, float* kv_scales, void* out,
+                          hipStream_t stream_ptr) {
     if (!block_table) return fail(FTM_ERR_INVALID_ARG, "block_table is NULL");
     if (((uintptr_t)block_table & 3u) != 0) return fail(FTM_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
     if (n_pages < 1 || max_pages_per_seq < 1)
@@ -719,7 +730,7 @@ int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, c
                         kv_scales, out, stream_ptr, block_table, shift, max_pages_per_seq, n_pages);
 }
 
-int ftm_graph_begin(void* stream) {
+int ftm_graph_begin(hipStream_t stream) {
     if (!stream) return fail(FTM_ERR_INVALID_ARG, "the null stream cannot be captured: pass a created stream");
     hipError_t e = hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
@@ -727,7 +738,7 @@ int ftm_graph_begin(void* stream) {
     return FTM_OK;
 }
 
-int ftm_graph_end(void* stream, ftm_graph* graph) {
+int ftm_graph_end(hipStream_t stream, ftm_graph* graph) {
     if (!stream || !graph) return fail(FTM_ERR_INVALID_ARG, "ftm_graph_end: stream and graph must be non-NULL");
     *graph = nullptr;
     hipGraph_t g = nullptr;
@@ -747,7 +758,7 @@ int ftm_graph_end(void* stream, ftm_graph* graph) {
     return FTM_OK;
 }
 
-int ftm_graph_launch(ftm_graph graph, void* stream) {
+int ftm_graph_launch(ftm_graph graph, hipStream_t stream) {
     if (!graph) return fail(FTM_ERR_INVALID_ARG, "ftm_graph_launch: graph is NULL");
     hipError_t e = hipGraphLaunch(graph->exec, (hipStream_t)stream);
     if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipGraphLaunch: ") + hipGetErrorString(e));

@@ -43,6 +43,20 @@ struct Params {
     int n_pages;            // pages in the pool
 };
 
+// Tuning variables, read from the environment once (ftm_tuning_reload reads
+// them again).  0 or -1 means "not set": the built-in choice applies.
+struct Tuning {
+    int validate;           // FTM_VALIDATE=1: blocking host check of seq_lens
+    int waves;              // FTM_WAVES: 4 or 16 waves per single-head workgroup
+    int split_chunk;        // FTM_SPLIT_CHUNK: positions per split chunk
+    int gqa_valu;           // FTM_GQA_VALU=1: grouped heads on the vector pass
+    int gqa_blocks_per_cu;  // FTM_GQA_BLOCKS_PER_CU: 1..16
+    int gqa_unit_cost;      // FTM_GQA_UNIT_COST: 0..64, -1 unset
+    int gqa_skew_a, gqa_skew_b;  // FTM_GQA_SKEW=a,b: 1..16 each
+    int qkv_column_tiles;   // FTM_QKV_COLUMN_TILES: 1..4
+};
+const Tuning& tuning();
+
 // Group tile (query heads served by one pass over a KV head) for G heads.
 int group_tile(int G);
 // Positions one workgroup of `nw` waves of the vector-ALU pass covers per
@@ -114,5 +128,8 @@ hipError_t launch_prefill_attention_i8(const PrefillParams& p, int head_dim, hip
 // act: KV_F16 or KV_BF16; B <= 64, hidden a multiple of 256, (H + 2 Hkv) D a multiple of 16.
 hipError_t launch_qkv_proj(const QkvParams& p, int act, int n_cu, hipStream_t s);
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);
+// Sets n ints at `dst` to zero with a kernel on `s` (no memset node, so it
+// may also be recorded into a graph).
+hipError_t launch_zero_ints(int* dst, size_t n, hipStream_t s);
 
 }  // namespace ftm

@@ -199,8 +199,7 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
 // for 10240 (256 and 214 workgroups where four gave 192 and 160).
 // FTM_QKV_COLUMN_TILES (1 to 4) forces the choice.
 int column_tiles(int n_out, int n_cu) {
-    const char* e = std::getenv("FTM_QKV_COLUMN_TILES");
-    const int forced = e ? std::atoi(e) : 0;
+    const int forced = tuning().qkv_column_tiles;
     if (forced >= 1 && forced <= 4) return forced;
     int best = 4;
     long best_cost = -1;

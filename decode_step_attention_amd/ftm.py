@@ -28,6 +28,7 @@ EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_qkv_proj", "ftm_prefil
            "ftm_kv_cache_bytes",
            "ftm_last_error",
            "ftm_version", "ftm_set_split_chunk", "ftm_set_workgroup_waves", "ftm_release_workspaces",
+           "ftm_tuning_reload",
            "ftm_graph_begin", "ftm_graph_end", "ftm_graph_launch", "ftm_graph_destroy",
            "ftm_timing_enable", "ftm_timing_disable", "ftm_timing_read")
 
@@ -71,6 +72,8 @@ def _load() -> ctypes.CDLL:
     lib.ftm_set_workgroup_waves.restype = i32
     lib.ftm_release_workspaces.argtypes = []
     lib.ftm_release_workspaces.restype = None
+    lib.ftm_tuning_reload.argtypes = []
+    lib.ftm_tuning_reload.restype = None
     lib.ftm_timing_enable.argtypes = [i32]
     lib.ftm_timing_enable.restype = i32
     lib.ftm_timing_disable.argtypes = []
@@ -106,6 +109,11 @@ def ftm_set_workgroup_waves(waves: int) -> int:
 
 def ftm_release_workspaces() -> None:
     lib.ftm_release_workspaces()
+
+
+def ftm_tuning_reload() -> None:
+    """Makes the library read the FTM_* tuning variables of os.environ again."""
+    lib.ftm_tuning_reload()
 
 
 def _check(rc: int) -> None:
@@ -406,3 +414,19 @@ def ftm_graph_launch(graph: int, stream: int) -> None:
 
 def ftm_graph_destroy(graph: Optional[int]) -> None:
     _check(lib.ftm_graph_destroy(ctypes.c_void_p(graph)))
+
+
+# The boundary's calls without the C prefix (ftm.decode_mha, ...): the same
+# functions under the names the Python side of the boundary uses.
+decode_mha = ftm_decode_mha
+decode_mha_prepared = ftm_decode_mha_prepared
+decode_mha_paged = ftm_decode_mha_paged
+decode_mha_paged_prepared = ftm_decode_mha_paged_prepared
+qkv_proj = ftm_qkv_proj
+prefill_mha = ftm_prefill_mha
+prefill_mha_paged = ftm_prefill_mha_paged
+last_error = ftm_last_error
+version = ftm_version
+kv_cache_bytes = ftm_kv_cache_bytes
+release_workspaces = ftm_release_workspaces
+tuning_reload = ftm_tuning_reload

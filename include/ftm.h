@@ -20,9 +20,24 @@
  * ([lpnh.cn/news/2765398] section 2.1; [framerc.cn/news/4453289] section 2.2).
  *
  * All pointers are caller-owned device pointers unless stated otherwise.
- * Calls only enqueue work on the given stream: they never synchronise and
- * never read device memory on the host.  Errors are returned before anything
- * is enqueued; the library never aborts the process.
+ * Errors are returned before anything is enqueued; the library never aborts
+ * the process (FasterTransformer aborts on a bad length,
+ * [lmnt.cn/news/219530] section 5.2).
+ *
+ * Blocking.  The compute calls (ftm_decode_mha, ftm_decode_mha_paged,
+ * ftm_decode_mha_static, ftm_qkv_proj, ftm_prefill_mha,
+ * ftm_prefill_mha_paged) only enqueue work on their stream and return: they
+ * never wait for the device and never read device memory on the host
+ * (there is no synchronisation on the decode path,
+ * [lmnt.cn/news/219530] section 6.1).  A call that needs a larger
+ * workspace allocates it with hipMalloc and clears what must start at zero
+ * with a kernel on the call's stream; the buffer it replaces is kept, not
+ * freed (hipFree would wait for the device), until
+ * ftm_release_workspaces.  The calls that do wait: ftm_release_workspaces
+ * (frees), ftm_timing_read (waits for the events it reads), and any compute
+ * call while FTM_VALIDATE=1 is set in the environment (it copies seq_lens to
+ * the host and waits for the stream).  ftm_graph_end and ftm_graph_destroy
+ * instantiate and free graphs on the host and may wait for the device.
  */
 #ifndef FTM_H
 #define FTM_H
@@ -33,6 +48,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* HIP's stream handle, as hip_runtime_api.h declares it (a repeated
+ * identical typedef is valid C11 and C++).  NULL is the null stream. */
+typedef struct ihipStream_t* hipStream_t;
 
 /* Cache element types ([lpnh.cn/news/2765398] section 6.1 and
  * [intelliparadigm.com .../2131745] section 4.1: fp16/bf16 storage;
@@ -110,8 +129,8 @@ typedef enum {
 int ftm_decode_mha(const void* q, const void* k_new, const void* v_new,
                    const void* qkv_bias, void* k_cache, void* v_cache,
                    const int32_t* seq_lens, int batch, int max_seq_len, int step,
-                   int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
-                   float* kv_scales, void* out, void* stream);
+                   int n_heads, int n_kv_heads, int head_dim, ftm_dtype kv_dtype,
+                   float* kv_scales, void* out, hipStream_t stream);
 
 /*
  * ftm_decode_mha_paged -- the same decode step over a paged KV cache.
@@ -153,8 +172,8 @@ int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new,
                          const void* qkv_bias, void* k_pages, void* v_pages,
                          const int32_t* block_table, int n_pages, int page_size,
                          int max_pages_per_seq, const int32_t* seq_lens, int batch, int step,
-                         int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
-                         float* kv_scales, void* out, void* stream);
+                         int n_heads, int n_kv_heads, int head_dim, ftm_dtype kv_dtype,
+                         float* kv_scales, void* out, hipStream_t stream);
 
 /*
  * ftm_qkv_proj -- the fused QKV projection that feeds a decode step.
@@ -185,7 +204,7 @@ int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new,
  */
 int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k_new,
                  void* v_new, int batch, int hidden, int n_heads, int n_kv_heads, int head_dim,
-                 int act_dtype, void* stream);
+                 ftm_dtype act_dtype, hipStream_t stream);
 
 /*
  * ftm_prefill_mha -- prefill: the whole prompt of every sequence in one step.
@@ -237,7 +256,7 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
 int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                     void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
                     int max_seq_len, int prompt_len, int n_heads, int n_kv_heads, int head_dim,
-                    int kv_dtype, float* kv_scales, void* out, void* stream);
+                    ftm_dtype kv_dtype, float* kv_scales, void* out, hipStream_t stream);
 
 /*
  * ftm_prefill_mha_paged -- prefill into a paged KV cache.
@@ -264,8 +283,8 @@ int ftm_prefill_mha(const void* q, const void* k_new, const void* v_new, const v
 int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
                           void* k_pages, void* v_pages, const int32_t* block_table, int n_pages,
                           int page_size, int max_pages_per_seq, const int32_t* seq_lens, int batch,
-                          int prompt_len, int n_heads, int n_kv_heads, int head_dim, int kv_dtype,
-                          float* kv_scales, void* out, void* stream);
+                          int prompt_len, int n_heads, int n_kv_heads, int head_dim, ftm_dtype kv_dtype,
+                          float* kv_scales, void* out, hipStream_t stream);
 
 /* ---- HIP graphs ----------------------------------------------------------
  * A decode step of a model is one call per layer on fixed buffers; its
@@ -294,9 +313,9 @@ int ftm_prefill_mha_paged(const void* q, const void* k_new, const void* v_new, c
  * or FTM_ERR_INVALID_ARG / FTM_ERR_HIP with ftm_last_error() set.
  */
 typedef struct ftm_graph_s* ftm_graph;
-int ftm_graph_begin(void* stream);
-int ftm_graph_end(void* stream, ftm_graph* graph);
-int ftm_graph_launch(ftm_graph graph, void* stream);
+int ftm_graph_begin(hipStream_t stream);
+int ftm_graph_end(hipStream_t stream, ftm_graph* graph);
+int ftm_graph_launch(ftm_graph graph, hipStream_t stream);
 int ftm_graph_destroy(ftm_graph graph);
 
 /* Bytes of one layer's K and V cache (plus INT8 scales) for the layout
@@ -305,13 +324,17 @@ int ftm_graph_destroy(ftm_graph graph);
  * [pptc.cn/news/144085] section 3.1 (batch x length x layers x hidden x
  * bytes, counted for K and V).  Returns 0 for invalid arguments. */
 size_t ftm_kv_cache_bytes(int batch, int n_kv_heads, int max_seq_len, int head_dim,
-                          int kv_dtype);
+                          ftm_dtype kv_dtype);
 
 /* Message for the last failed call on this host thread ("" if none).
- * Owned by the library; valid until the next call on this thread. */
+ * Owned by the library; valid until the next call on this thread.  Errors
+ * are returned as a status with this message instead of aborting the
+ * process, which is what FasterTransformer does when a length passes the
+ * cache's capacity ([lmnt.cn/news/219530] section 5.2). */
 const char* ftm_last_error(void);
 
-/* Library version string, owned by the library. */
+/* Library version string ("libftm <version> (gfx950)"), owned by the
+ * library.  Not a step of the method: it names the build a caller loaded. */
 const char* ftm_version(void);
 
 /* Chunk length, in positions, of the split-sequence pass (flash-decoding:
@@ -330,10 +353,23 @@ int ftm_set_split_chunk(int positions);
  * previous setting, or -1 for another value. */
 int ftm_set_workgroup_waves(int waves);
 
-/* Frees every workspace the library holds (all devices and streams).  The
- * caller must make sure no call of this library is still running, and must
- * not replay graphs captured before the release. */
+/* Frees every workspace the library holds (all devices and streams),
+ * including the buffers that larger ones replaced.  Workspaces are
+ * allocated once and reused across calls and layers instead of per call
+ * ([lpnh.cn/news/2765398] section 2.2: intermediate buffers are pooled
+ * and recycled; [lmnt.cn/news/219530] section 6.4), so this is the one
+ * place they are freed.  It waits for the device (hipFree).  The caller
+ * must make sure no call of this library is still running, and must not
+ * replay graphs captured before the release. */
 void ftm_release_workspaces(void);
+
+/* Re-reads the tuning variables of the environment (FTM_VALIDATE,
+ * FTM_WAVES, FTM_SPLIT_CHUNK, FTM_GQA_VALU, FTM_GQA_BLOCKS_PER_CU,
+ * FTM_GQA_UNIT_COST, FTM_GQA_SKEW, FTM_QKV_COLUMN_TILES).  The library
+ * reads them once, at its first call, and not again on the call path;
+ * a process that changes them calls this afterwards.  Not a step of the
+ * method: the variables choose launch shapes for measurement and tests. */
+void ftm_tuning_reload(void);
 
 /* ---- kernel timing -------------------------------------------------------
  * For measurement only.  While enabled, every ftm_decode_mha(_paged) and

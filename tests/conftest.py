@@ -23,3 +23,19 @@ def oracle_mod():
     import oracle
     oracle._load()
     return oracle
+
+
+@pytest.fixture
+def tuning(monkeypatch):
+    """Sets FTM_* tuning variables for one test.  The library reads them once,
+    so every change is followed by ftm_tuning_reload, and so is the restore."""
+    from decode_step_attention_amd import ftm
+
+    class Tuning:
+        def set(self, name, value):
+            monkeypatch.setenv(name, str(value))
+            ftm.ftm_tuning_reload()
+
+    yield Tuning()
+    monkeypatch.undo()
+    ftm.ftm_tuning_reload()

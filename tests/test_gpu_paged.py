@@ -117,8 +117,8 @@ def test_paged_parity(ftm, kv, D, H, Hkv, P, chunk, waves):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "f16"])
-def test_paged_grouped_heads_vector_path(ftm, monkeypatch, kv):
-    monkeypatch.setenv("FTM_GQA_VALU", "1")
+def test_paged_grouped_heads_vector_path(ftm, tuning, kv):
+    tuning.set("FTM_GQA_VALU", "1")
     case = small(kv, D=128, H=8, Hkv=1, seed=51)
     run_paged(ftm, case, 32, tag=f"paged {kv} G8 vector path")
 

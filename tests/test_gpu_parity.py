@@ -157,13 +157,13 @@ def test_prepared_call_matches_plain_call(ftm):
 @pytest.mark.parametrize("kv,D,G,scale", [("bf16", 128, 8, None), ("f16", 128, 8, None),
                                            ("bf16", 64, 4, None), ("f16", 64, 8, None),
                                            ("bf16", 128, 8, 1.0), ("f16", 128, 4, 1.0)])
-def test_grouped_heads_matrix_core_and_vector_paths(ftm, monkeypatch, vector_alu, kv, D, G, scale):
+def test_grouped_heads_matrix_core_and_vector_paths(ftm, tuning, vector_alu, kv, D, G, scale):
     """Groups of 4 and 8 heads over fp16/bf16 caches run q.K on the matrix
     cores with the query split into two halves; FTM_GQA_VALU=1 selects the
     vector-ALU pass.  Both meet the bar, also with unit-scale data, where
     scores reach several units and the query split matters."""
     if vector_alu:
-        monkeypatch.setenv("FTM_GQA_VALU", "1")
+        tuning.set("FTM_GQA_VALU", "1")
     case = small(kv, D=D, H=2 * G, Hkv=2, B=3, seed=50 + G + D)
     if scale is not None:
         case = case.with_(value_scale=scale)
@@ -192,14 +192,14 @@ def test_grouped_heads_balanced_schedule(ftm, B, Lmax, lens, kv):
 
 
 @pytest.mark.parametrize("cost,per_cu", [(0, 1), (5, 1), (14, 2), (3, 3)])
-def test_grouped_heads_range_boundaries(ftm, monkeypatch, cost, per_cu):
+def test_grouped_heads_range_boundaries(ftm, tuning, cost, per_cu):
     """The grouped-query schedule hands equal tile ranges to the workgroups;
     the per-unit charge and the workgroups per CU move the range boundaries
     inside units, so that ranges start and end mid-unit, hold several whole
     units, or begin in one unit's charge.  Every placement meets the bar and
     repeated calls give identical bits."""
-    monkeypatch.setenv("FTM_GQA_UNIT_COST", str(cost))
-    monkeypatch.setenv("FTM_GQA_BLOCKS_PER_CU", str(per_cu))
+    tuning.set("FTM_GQA_UNIT_COST", str(cost))
+    tuning.set("FTM_GQA_BLOCKS_PER_CU", str(per_cu))
     case = small("bf16", B=23, H=16, Hkv=2, Lmax=2500, lens=(1, 2500), seed=70 + cost)
     run_and_compare(ftm, case, tag=f"ranges cost{cost} per_cu{per_cu}")
     inp = W.make_inputs(case, "cuda")
@@ -210,11 +210,11 @@ def test_grouped_heads_range_boundaries(ftm, monkeypatch, cost, per_cu):
 
 
 @pytest.mark.parametrize("skew", ["1,1", "2,1", "8,7", "1,4"])
-def test_grouped_heads_wave_shares(ftm, monkeypatch, skew):
+def test_grouped_heads_wave_shares(ftm, tuning, skew):
     """The grouped-query pass deals each round of tiles out unevenly between
     the older and the younger waves of a workgroup; every split covers each
     tile once, meets the bar and gives identical bits on repeated calls."""
-    monkeypatch.setenv("FTM_GQA_SKEW", skew)
+    tuning.set("FTM_GQA_SKEW", skew)
     case = small("f16", B=9, H=16, Hkv=2, Lmax=3000, lens=(1, 3000), seed=80)
     run_and_compare(ftm, case, tag=f"wave shares {skew}")
     inp = W.make_inputs(case, "cuda")

@@ -93,10 +93,10 @@ def test_projection_parity(ftm, dt, B, H, Hkv, D, hidden, with_bias):
 
 @pytest.mark.parametrize("ft", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("dt,B,hidden", [("bf16", 16, 1024), ("f16", 40, 768), ("bf16", 64, 2048)])
-def test_column_tiles(ftm, monkeypatch, ft, dt, B, hidden):
+def test_column_tiles(ftm, tuning, ft, dt, B, hidden):
     """Every number of column tiles per workgroup (forced), with one to four
     batch tiles."""
-    monkeypatch.setenv("FTM_QKV_COLUMN_TILES", ft)
+    tuning.set("FTM_QKV_COLUMN_TILES", ft)
     case = W.ProjCase("t", B, 8, 2, 128, hidden, dt, seed=31 + B)
     inp = W.make_proj_inputs(case)
     got = run(ftm, inp, case)
@@ -108,12 +108,12 @@ def test_column_tiles(ftm, monkeypatch, ft, dt, B, hidden):
 @pytest.mark.parametrize("dt,B,H,Hkv,D,hidden", [("bf16", 9, 8, 1, 64, 768),     # 640 features
                                                  ("f16", 33, 6, 2, 80, 512),     # 800 features
                                                  ("bf16", 64, 5, 5, 128, 1024)]) # 1920: 48 x 40
-def test_partial_last_workgroup(ftm, monkeypatch, ft, dt, B, H, Hkv, D, hidden):
+def test_partial_last_workgroup(ftm, tuning, ft, dt, B, H, Hkv, D, hidden):
     """Feature counts that are not a multiple of the workgroup's 16 FT
     columns: the last workgroup's rows past the end read as zero and its
     tiles past the end are not written (every output is checked, and the
     buffers past the outputs are not touched)."""
-    monkeypatch.setenv("FTM_QKV_COLUMN_TILES", ft)
+    tuning.set("FTM_QKV_COLUMN_TILES", ft)
     case = W.ProjCase("t", B, H, Hkv, D, hidden, dt, seed=41 + B + D)
     inp = W.make_proj_inputs(case)
     tdt = W.TORCH_DTYPES[dt]

@@ -279,3 +279,52 @@ def test_paged_prefill_argument_errors_return_before_any_device_call(kw, status,
     rc, msg = call_prefill_paged(**kw)
     assert rc == status, msg
     assert needle in msg
+
+
+def _compile(tmp_path, compiler, lang_flags, body, extra=()):
+    import subprocess
+    src = tmp_path / ("probe.c" if compiler == "gcc" else "probe.cpp")
+    src.write_text(body)
+    cmd = [compiler, *lang_flags, "-fsyntax-only", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+           *extra, str(src)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_header_is_plain_c11(tmp_path):
+    """include/ftm.h compiles as C11 on its own: plain pointers, sizes and the
+    two enums, with HIP's stream handle declared as HIP declares it."""
+    _compile(tmp_path, "gcc", ["-std=c11"], '#include "ftm.h"\n'
+             "static int (*p)(const void*, const void*, const void*, const void*, void*, void*,\n"
+             "              const int32_t*, int, int, int, int, int, int, ftm_dtype, float*, void*,\n"
+             "              hipStream_t) = ftm_decode_mha;\n"
+             "int main(void) { return p == 0; }\n")
+
+
+def test_header_next_to_hip_runtime(tmp_path):
+    """The header's stream typedef is HIP's own: including both compiles."""
+    _compile(tmp_path, "g++", ["-std=c++17", "-D__HIP_PLATFORM_AMD__"],
+             '#include <hip/hip_runtime_api.h>\n#include "ftm.h"\n'
+             "int main() { hipStream_t s = nullptr; ftm_dtype d = FTM_F16;\n"
+             "  return ftm_decode_mha(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,\n"
+             "                        1, 1, 1, 1, 1, 64, d, nullptr, nullptr, s); }\n",
+             extra=("-I", "/opt/rocm/include"))
+
+
+def test_compute_calls_never_wait_for_the_device():
+    """The compute path of the C ABI holds no host synchronisation and no
+    hipFree: the only waits are the documented ones (ftm_release_workspaces,
+    ftm_timing_read, the FTM_VALIDATE check)."""
+    src = open(os.path.join(ROOT, "decode_step_attention_amd", "csrc", "ftm_api.cpp")).read()
+    assert "hipDeviceSynchronize" not in src
+    assert "hipMemset" not in src
+    waits = [m.start() for m in re.finditer(r"hipStreamSynchronize|hipEventSynchronize|hipFree\(", src)]
+    allowed = {
+        "hipStreamSynchronize": "FTM_VALIDATE",
+        "hipEventSynchronize": "int ftm_timing_read(",
+        "hipFree(": "void ftm_release_workspaces(",
+    }
+    for pos in waits:
+        name = next(k for k in allowed if src.startswith(k, pos))
+        owner = src.rfind(allowed[name], 0, pos)
+        assert owner >= 0 and pos - owner < 1500, f"{name} at offset {pos} outside {allowed[name]}"
