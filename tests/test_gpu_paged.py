@@ -109,6 +109,17 @@ PATHS = [
 ]
 
 
+@pytest.mark.parametrize("step", [512, 513])
+def test_paged_default_launch_shape_at_the_short_pass_limit(ftm, step):
+    """The 7B-shaped layer through the page table with the launch shape left
+    to the library, on both sides of the 4-wave single-pass limit."""
+    case = W.Case("7b-step", 8, 32, 32, 128, "f16", ctx=step, max_seq_len=step + 64,
+                  value_scale=1 / np.sqrt(128), lens=(1, step), seed=97 + step)
+    lens = W.seq_lens(case).clone()
+    lens[0] = step
+    run_paged(ftm, case, 64, lens=lens, tag=f"paged default shape step{step}")
+
+
 @pytest.mark.parametrize("kv,D,H,Hkv,P,chunk,waves", PATHS)
 def test_paged_parity(ftm, kv, D, H, Hkv, P, chunk, waves):
     case = small(kv, D=D, H=H, Hkv=Hkv, seed=41 + D + H + Hkv + P)
