@@ -26,7 +26,17 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include <map>
+#include <mutex>
+
 #include "gfx950.hpp"
+
+// Scratch memory of the allocation-free decode call (ftm_decode_mha_static):
+// each GPU the library runs on holds one copy until the process ends.  Host
+// code never passes this name to a kernel: in host code it is only a
+// stand-in, and the device address comes from hipGetSymbolAddress (see
+// ftm::static_scratch below).
+static __device__ __align__(256) unsigned char scratch[ftm::kStaticScratchBytes];
 
 namespace ftm {
 namespace {
@@ -1529,6 +1539,27 @@ hipError_t launch_zero_ints(int* dst, size_t n, hipStream_t s) {
     const size_t blocks = std::min<size_t>((n + 255) / 256, 1024);
     hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst, n);
     return hipGetLastError();
+}
+
+hipError_t static_scratch(int device, hipStream_t s, void** ptr) {
+    static std::mutex m;
+    static std::map<int, void*> addr;      // device -> its copy of `scratch`
+    std::lock_guard<std::mutex> lock(m);
+    auto it = addr.find(device);
+    if (it != addr.end()) {
+        *ptr = it->second;
+        return hipSuccess;
+    }
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the counters must start at zero; every call of the grouped-query pass
+    // leaves them at zero again
+    e = launch_zero_ints((int*)p, kStaticCounterInts, s);
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s) {

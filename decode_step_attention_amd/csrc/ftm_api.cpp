@@ -228,6 +228,8 @@ struct Call {
     // paged
     const int32_t* block_table;
     int page_shift, max_pages, n_pages;
+    // scratch from the library's fixed device array instead of the workspace
+    bool static_ws;
 };
 
 }  // namespace
@@ -474,10 +476,24 @@ int decode_impl(const Call& a) {
         p.range_min = std::max(std::max(16, p.unit_cost + 1),
                                (max_tiles + ftm::kGqaMaxPieces - 3) / (ftm::kGqaMaxPieces - 2));
         const size_t slots = (size_t)2 * p.S * gtile;
+        const size_t need = slots * (head_dim + 2) * sizeof(float);
         void* ws = nullptr;
-        int st = get_workspace(device, stream, slots * (head_dim + 2) * sizeof(float), units, capturing,
-                               &ws, &p.counters);
-        if (st != FTM_OK) return st;
+        if (a.static_ws) {
+            if (need > ftm::kStaticPartialBytes || (size_t)units > ftm::kStaticCounterInts)
+                return fail(FTM_ERR_UNSUPPORTED,
+                            "the grouped-query pass needs " + std::to_string(need) + " bytes of partials and " +
+                                std::to_string(units) + " counters; the fixed scratch holds " +
+                                std::to_string(ftm::kStaticPartialBytes) + " bytes and " +
+                                std::to_string(ftm::kStaticCounterInts) + " counters");
+            void* scratch = nullptr;
+            he = ftm::static_scratch(device, stream, &scratch);
+            if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("scratch set-up: ") + hipGetErrorString(he));
+            p.counters = (int*)scratch;
+            ws = (char*)scratch + ftm::kStaticCounterInts * sizeof(int);
+        } else {
+            int st = get_workspace(device, stream, need, units, capturing, &ws, &p.counters);
+            if (st != FTM_OK) return st;
+        }
         p.ws_o = (float*)ws;
         p.ws_ml = p.ws_o + slots * head_dim;
     } else {
@@ -487,10 +503,23 @@ int decode_impl(const Call& a) {
         p.direct = p.S == 1;
         if (!p.direct) {
             const size_t n_part = (size_t)a.batch * a.n_heads * p.S;
+            const size_t need = n_part * (head_dim + 2) * sizeof(float);
             void* ws = nullptr;
-            int st = get_workspace(device, stream, n_part * (head_dim + 2) * sizeof(float), 0, capturing,
-                                   &ws, nullptr);
-            if (st != FTM_OK) return st;
+            if (a.static_ws) {
+                if (need > ftm::kStaticPartialBytes)
+                    return fail(FTM_ERR_UNSUPPORTED,
+                                "the split pass needs " + std::to_string(need) +
+                                    " bytes of partials; the fixed scratch holds " +
+                                    std::to_string(ftm::kStaticPartialBytes));
+                void* scratch = nullptr;
+                he = ftm::static_scratch(device, stream, &scratch);
+                if (he != hipSuccess)
+                    return fail(FTM_ERR_HIP, std::string("scratch set-up: ") + hipGetErrorString(he));
+                ws = (char*)scratch + ftm::kStaticCounterInts * sizeof(int);
+            } else {
+                int st = get_workspace(device, stream, need, 0, capturing, &ws, nullptr);
+                if (st != FTM_OK) return st;
+            }
             p.ws_o = (float*)ws;
             p.ws_ml = p.ws_o + n_part * head_dim;
         }
@@ -527,7 +556,22 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new, const vo
     if ((size_t)max_seq_len * head_dim * elem_bytes(kv_dtype) > 0x7fffffffu)
         return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
     Call a{q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len, step, n_heads,
-           n_kv_heads, head_dim, kv_dtype, kv_scales, out, (hipStream_t)stream_ptr, nullptr, 0, 0, 0};
+           n_kv_heads, head_dim, kv_dtype, kv_scales, out, (hipStream_t)stream_ptr, nullptr, 0, 0, 0, false};
+    return decode_impl(a);
+}
+
+int ftm_decode_mha_static(const void* q, const void* k_new, const void* v_new, const void* qkv_bias,
+                          void* k_cache, void* v_cache, const int32_t* seq_lens, int batch,
+                          int max_seq_len, int step, int n_heads, int n_kv_heads, int head_dim,
+                          ftm_dtype kv_dtype, float* kv_scales, void* out, hipStream_t stream_ptr) {
+    if (max_seq_len < 1) return fail(FTM_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+    int st = check_common(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len,
+                          step, n_heads, n_kv_heads, head_dim, kv_dtype, kv_scales, out, "max_seq_len");
+    if (st != FTM_OK) return st;
+    if ((size_t)max_seq_len * head_dim * elem_bytes(kv_dtype) > 0x7fffffffu)
+        return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
+    Call a{q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens, batch, max_seq_len, step, n_heads,
+           n_kv_heads, head_dim, kv_dtype, kv_scales, out, stream_ptr, nullptr, 0, 0, 0, true};
     return decode_impl(a);
 }
 
@@ -554,7 +598,7 @@ int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new, co
     while ((1 << shift) < page_size) ++shift;
     Call a{q, k_new, v_new, qkv_bias, k_pages, v_pages, seq_lens, batch, (int)cap, step, n_heads,
            n_kv_heads, head_dim, kv_dtype, kv_scales, out, (hipStream_t)stream_ptr, block_table, shift,
-           max_pages_per_seq, n_pages};
+           max_pages_per_seq, n_pages, false};
     return decode_impl(a);
 }
 

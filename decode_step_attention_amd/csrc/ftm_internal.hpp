@@ -132,4 +132,14 @@ hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);
 // may also be recorded into a graph).
 hipError_t launch_zero_ints(int* dst, size_t n, hipStream_t s);
 
+// Scratch of the allocation-free decode call: a fixed device array of
+// kStaticScratchBytes per GPU, the grouped-query counters in its first
+// kStaticCounterInts ints and the split partials after them.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr size_t kStaticCounterInts = 16384;
+constexpr size_t kStaticPartialBytes = kStaticScratchBytes - kStaticCounterInts * sizeof(int);
+// The device address of the current device's scratch (taken once per
+// device; the first call also clears the counters with a kernel on `s`).
+hipError_t static_scratch(int device, hipStream_t s, void** ptr);
+
 }  // namespace ftm

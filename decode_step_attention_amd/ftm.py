@@ -24,7 +24,7 @@ _ACT = {FTM_F32: torch.float32, FTM_F16: torch.float16, FTM_BF16: torch.bfloat16
         FTM_I8: torch.float16}
 
 # Every symbol include/ftm.h declares.
-EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_paged", "ftm_qkv_proj", "ftm_prefill_mha", "ftm_prefill_mha_paged",
+EXPORTS = ("ftm_decode_mha", "ftm_decode_mha_static", "ftm_decode_mha_paged", "ftm_qkv_proj", "ftm_prefill_mha", "ftm_prefill_mha_paged",
            "ftm_kv_cache_bytes",
            "ftm_last_error",
            "ftm_version", "ftm_set_split_chunk", "ftm_set_workgroup_waves", "ftm_release_workspaces",
@@ -42,6 +42,8 @@ def _load() -> ctypes.CDLL:
     lib.ftm_decode_mha.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                    i32, vp, vp, vp]
     lib.ftm_decode_mha.restype = i32
+    lib.ftm_decode_mha_static.argtypes = lib.ftm_decode_mha.argtypes
+    lib.ftm_decode_mha_static.restype = i32
     lib.ftm_decode_mha_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i32,
                                          i32, i32, i32, i32, vp, vp, vp]
     lib.ftm_decode_mha_paged.restype = i32
@@ -228,6 +230,17 @@ def ftm_decode_mha(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     are updated in place; out is written."""
     _check(lib.ftm_decode_mha(*_marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens,
                                         step, out, kv_scales, stream)))
+
+
+def ftm_decode_mha_static(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                          qkv_bias: Optional[torch.Tensor], k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          seq_lens: Optional[torch.Tensor], step: int, out: torch.Tensor,
+                          kv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+    """ftm_decode_mha with its scratch in the library's fixed device array:
+    no allocation (see include/ftm.h for the limit, and for why calls that
+    overlap on one GPU race)."""
+    _check(lib.ftm_decode_mha_static(*_marshal(q, k_new, v_new, qkv_bias, k_cache, v_cache, seq_lens,
+                                               step, out, kv_scales, stream)))
 
 
 def _prepared(f, args, keep) -> Callable[[], None]:
@@ -420,6 +433,7 @@ def ftm_graph_destroy(graph: Optional[int]) -> None:
 # functions under the names the Python side of the boundary uses.
 decode_mha = ftm_decode_mha
 decode_mha_prepared = ftm_decode_mha_prepared
+decode_mha_static = ftm_decode_mha_static
 decode_mha_paged = ftm_decode_mha_paged
 decode_mha_paged_prepared = ftm_decode_mha_paged_prepared
 qkv_proj = ftm_qkv_proj

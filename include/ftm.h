@@ -133,6 +133,37 @@ int ftm_decode_mha(const void* q, const void* k_new, const void* v_new,
                    float* kv_scales, void* out, hipStream_t stream);
 
 /*
+ * ftm_decode_mha_static -- ftm_decode_mha without any allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels, results and errors as ftm_decode_mha, but the
+ * scratch memory of the step (the split partials and the per-unit counters
+ * of the grouped-query pass) is a fixed device array of 8 MiB that each GPU
+ * holds from the library's first use until the process ends, instead of
+ * the per-stream workspace.  The call never calls hipMalloc or hipFree; the
+ * first call on a device that needs scratch takes the array's address
+ * (hipGetSymbolAddress) and clears its counters with a kernel on `stream`.
+ *
+ * Limit: a step whose scratch exceeds the array returns FTM_ERR_UNSUPPORTED
+ * before anything is enqueued: at most 8 MiB - 64 KiB of partials
+ * (batch * n_heads * chunks * (head_dim + 2) * 4 bytes for a split pass;
+ * 2 * workgroups * group tile * (head_dim + 2) * 4 for the grouped-query
+ * pass) and 16384 (sequence, KV head, head group) units.  A single pass
+ * needs no scratch.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (on different streams, or on different host threads)
+ * race and give wrong results.  Serialise them, or use ftm_decode_mha,
+ * whose workspace is per stream.
+ */
+int ftm_decode_mha_static(const void* q, const void* k_new, const void* v_new,
+                          const void* qkv_bias, void* k_cache, void* v_cache,
+                          const int32_t* seq_lens, int batch, int max_seq_len, int step,
+                          int n_heads, int n_kv_heads, int head_dim, ftm_dtype kv_dtype,
+                          float* kv_scales, void* out, hipStream_t stream);
+
+/*
  * ftm_decode_mha_paged -- the same decode step over a paged KV cache.
  *
  * The cache is cut into fixed-size pages that sequences take as needed,
