@@ -9,7 +9,12 @@ workload.  Inputs are seeded synthetic tensors already resident in HBM; the
 layer caches rotate so that the working set exceeds the 256 MB last-level
 cache.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config 7b] [--graph]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--graph]
+
+With no --config the line's value is the 7b workload (the configuration the
+metric is quoted on), and the tiny, sizing32, gqa and int8 workloads are
+reported beside it under "configs", each with its own roofline and CPU
+baseline.
 
 --graph records each step's calls once into a HIP graph (ftm_graph_*) and
 times graph replays instead of one library call per layer.
@@ -74,11 +79,29 @@ def describe(case: W.Case) -> str:
             + (f", {case.layers} layers" if case.layers > 1 else ""))
 
 
-def cpu_baseline(case, inputs, lens, budget_s: float):
+# Threads the oracle may use: the host CPUs this process may run on, capped
+# at the 16-CPU share one GPU of the box is given.
+CPU_SHARE = 16
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, inputs, lens, budget_s: float, threads: int = 0):
     """The CPU oracle, as it stands, on the host cores: a bounded sample of the
-    same workload (whole sequences of layer 0), timed like the GPU step."""
+    same workload (whole sequences of layer 0), timed like the GPU step.
+    threads 0: every CPU of the affinity mask up to the 16-CPU share."""
     import oracle
-    ncores = min(len(os.sched_getaffinity(0)), 16)
+    affinity = len(os.sched_getaffinity(0))
+    ncores = threads if threads > 0 else min(affinity, CPU_SHARE)
     inp = inputs[0]
     act, kvd = case.act_dtype, case.kv_dtype
     per_seq = case.n_kv_heads * 2 * case.max_seq_len * case.head_dim * W.ELEM_BYTES[kvd]
@@ -122,9 +145,9 @@ def cpu_baseline(case, inputs, lens, budget_s: float):
         total += dt
         runs += 1
     return {"value": sample_bytes / best / 1e9, "unit": "GB/s", "cores": ncores, "kind": "oracle",
-            "tokens_per_s": nb / best,
-            "sample": f"layer 0, sequences 0..{nb - 1} of {case.batch} ({sample_bytes / 2**20:.0f} MiB "
-                      f"of K/V), fp64 oracle, best of {runs} runs, {total:.1f} s in total"}
+            "tokens_per_s": nb / best, "affinity_cpus": affinity, "cpu_model": cpu_model(),
+            "sample": f"layer 0, sequences 0..{nb - 1} of {case.batch} ({sample_bytes / 2**20:.3g} MiB "
+                      f"of K/V), fp64 oracle on {ncores} threads, best of {runs} runs, {total:.1f} s in total"}
 
 
 def device_copy_gbs(dev) -> float:
@@ -339,36 +362,12 @@ def run_prefill(args, case):
     print(json.dumps(result), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="7b",
-                    choices=sorted(W.CASES) + sorted(W.PROJ_CASES) + sorted(W.PREFILL_CASES))
-    ap.add_argument("--cpu-budget", type=float, default=10.0,
-                    help="seconds of oracle time for the CPU baseline (0 skips it)")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay each step from a HIP graph instead of one call per layer")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path (the attention "
-              "shards by batch or KV-head group with no exchange). Run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    if args.config in W.PROJ_CASES:
-        run_projection(args, W.PROJ_CASES[args.config])
-        return
-    if args.config in W.PREFILL_CASES:
-        run_prefill(args, W.PREFILL_CASES[args.config])
-        return
+def run_decode(args, case: W.Case, cpu_budget: float) -> dict:
+    """One decode workload: the whole path timed over args.steps steps after
+    args.warmup untimed ones, with its roofline and the CPU oracle beside it."""
     from decode_step_attention_amd import ftm
 
     dev = torch.device("cuda:0")
-    case = W.CASES[args.config]
     layers = case.layers
     rotate = max(case.rotate, layers)
     lens = W.seq_lens(case)
@@ -448,6 +447,7 @@ def main():
     # timed region 1: the whole path, nothing else on the stream; a HIP event
     # pair on the launch stream brackets the region
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     r0.record(stream)
     for i in range(args.steps):
@@ -501,7 +501,7 @@ def main():
         timing = "event pair around every attention launch in timed region 2"
     achieved = kv_layer / (avg_att_us * 1e-6) / 1e9
     kernel = dominant_kernel(case)
-    traffic = read_traffic(kernel, args.config)
+    traffic = read_traffic(kernel, case.name)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
@@ -535,9 +535,69 @@ def main():
         "device_copy_GBs": round(copy_gbs, 1),
         "roofline": roof,
     }
-    if args.cpu_budget > 0:
-        print("# timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(case, inputs, lens_np, args.cpu_budget)
+    if cpu_budget > 0:
+        print(f"# timing the CPU oracle on {case.name}", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case, inputs, lens_np, cpu_budget)
+        if case.name in ONE_THREAD_CONFIGS:
+            one = cpu_baseline(case, inputs, lens_np, 0.0, threads=1)
+            result["cpu_baseline"]["one_thread"] = {"value": one["value"], "unit": "GB/s",
+                                                    "tokens_per_s": one["tokens_per_s"], "sample": one["sample"]}
+    del inputs, calls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result
+
+
+# The headline workload, and the others reported beside it in the same line.
+HEADLINE = "7b"
+SECONDARY = ("tiny", "sizing32", "gqa", "int8")
+# Workloads whose oracle is also timed on one thread.
+ONE_THREAD_CONFIGS = ("tiny", "7b")
+SUMMARY_KEYS = ("value", "unit", "pct_hbm_peak", "tokens_per_s", "ms_per_step", "gpu_ms_per_step", "dtype",
+                "kernels_per_step", "step_us_per_step_events", "roofline", "cpu_baseline")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", default=None,
+                    choices=sorted(W.CASES) + sorted(W.PROJ_CASES) + sorted(W.PREFILL_CASES),
+                    help="one workload only (default: the 7b headline, with tiny, sizing32, gqa and int8 "
+                         "reported beside it under \"configs\")")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time for the CPU baseline of the headline (0 skips it)")
+    ap.add_argument("--cpu-budget-others", type=float, default=5.0,
+                    help="seconds of oracle time for each other workload's CPU baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a HIP graph instead of one call per layer")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path (the attention "
+              "shards by batch or KV-head group with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.config in W.PROJ_CASES:
+        run_projection(args, W.PROJ_CASES[args.config])
+        return
+    if args.config in W.PREFILL_CASES:
+        run_prefill(args, W.PREFILL_CASES[args.config])
+        return
+    if args.config is not None:
+        print(json.dumps(run_decode(args, W.CASES[args.config], args.cpu_budget)), flush=True)
+        return
+    t_start = time.perf_counter()
+    result = run_decode(args, W.CASES[HEADLINE], args.cpu_budget)
+    others = {}
+    for name in SECONDARY:
+        r = run_decode(args, W.CASES[name], args.cpu_budget_others if args.cpu_budget > 0 else 0.0)
+        others[name] = {"workload": r["config"]["workload"], **{key: r[key] for key in SUMMARY_KEYS if key in r}}
+    result["configs"] = others
+    result["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
     print(json.dumps(result), flush=True)
 
 
