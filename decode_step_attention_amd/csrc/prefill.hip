@@ -279,6 +279,12 @@ prefill_attn_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char vscl0[SCB];
     __shared__ __attribute__((aligned(16))) unsigned char kscl1[SCB];
     __shared__ __attribute__((aligned(16))) unsigned char vscl1[SCB];
+    // the bias terms b_q . k of a K tile's 64 keys (float caches with a
+    // bias), double-buffered by tile parity: wave w computes keys 16 w ..
+    // 16 w + 15 when the tile lands, every wave reads its own keys' terms
+    constexpr bool kSharedBias = BIAS && !SC;
+    __shared__ __attribute__((aligned(16))) float bkt0[kSharedBias ? kPK : 4];
+    __shared__ __attribute__((aligned(16))) float bkt1[kSharedBias ? kPK : 4];
     auto kswz = [](int r) { return (r * NCH / 16) & (NCH - 1); };
     auto vswz = [](int r) { return 2 * ((r * NCH / 16) & (NCH / 2 - 1)); };
 
@@ -497,8 +503,8 @@ prefill_attn_kernel(const PrefillParams p) {
     };
 
     // unscaled S^T for the 32 keys of step jj from K buffer kt: row = key
-    // 32 jj + 16 h2 + 4g + i, column = query tq + 16 qb + n; entry kQB holds
-    // b_q . k (every column alike)
+    // 32 jj + 16 h2 + 4g + i, column = query tq + 16 qb + n; with the INT8
+    // staging, entry kQB holds b_q . k (every column alike)
     typedef f32x4 Scores[kQB + 1][2];
     auto qk = [&](Scores& sa, const unsigned char* kt, int half) {
 #pragma unroll
@@ -512,7 +518,7 @@ prefill_attn_kernel(const PrefillParams p) {
                 const vec8 ka = MF::bits8(*(const u32x4*)(kt + (32 * half + 16 * h2) * ROW + koff[kk]));
 #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) sa[qb][h2] = MF::mma32(ka, qv[qb][kk], sa[qb][h2]);
-                if constexpr (BIAS) sa[kQB][h2] = MF::mma32(ka, bv[kk], sa[kQB][h2]);
+                if constexpr (BIAS && SC) sa[kQB][h2] = MF::mma32(ka, bv[kk], sa[kQB][h2]);
             }
         }
     };
@@ -532,10 +538,25 @@ prefill_attn_kernel(const PrefillParams p) {
             }
     };
 
+    // b_q . k for keys 16 wave .. +15 of the K tile in kt, into bkt: one
+    // matrix-core product per 32 head elements with the bias as the B
+    // operand (every column alike), so lane (g, 0) holds keys 4g .. 4g + 3
+    auto bias_terms = [&](const unsigned char* kt, float* bkt) {
+        f32x4 bt = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            bt = MF::mma32(MF::bits8(*(const u32x4*)(kt + 16 * wave * ROW + koff[kk])), bv[kk], bt);
+        if (n == 0) *(f32x4*)(bkt + 16 * wave + 4 * g) = bt;
+    };
+
     Scores scur, snext;
     __builtin_amdgcn_s_waitcnt(0x0F70);     // the first tiles (and the query) landed
     __syncthreads();
     clear_v_tail(0, vtile0);
+    if constexpr (kSharedBias) {
+        bias_terms(ktile0, bkt0);
+        lds_barrier();
+    }
     if (0 <= last_j) {
         qk(scur, ktile0, 0);
         if constexpr (SC) fold_k_scale(scur, kscl0, 0);
@@ -560,19 +581,28 @@ prefill_attn_kernel(const PrefillParams p) {
             wait_one_batch_behind();        // V(T + 1) was issued after K(T + 1)
             lds_barrier();
             issue(false, T * kPK + 2 * kPK, (u / 2) ? ktile1 : ktile0, koffs, (u / 2) ? kscl1 : kscl0);
+            // the bias terms of tile T + 1, read from the next step on
+            // (after its barrier); their buffer last served tile T - 1
+            if constexpr (kSharedBias) bias_terms((u / 2) ? ktile0 : ktile1, (u / 2) ? bkt0 : bkt1);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (j > last_j) return;
         const int kb = 32 * j;              // first key of the step
         // scores of this step; slot 4 h2 + i of this lane: key kb + 16 h2 + 4g + i
         float s[kQB][8];
+        f32x4 bk[2] = {};                   // this lane's keys' bias terms
+        if constexpr (kSharedBias) {
+            const float* bkt = ((u / 2) ? bkt1 : bkt0) + 32 * (j % 2) + 4 * g;
+            bk[0] = *(const f32x4*)bkt;
+            bk[1] = *(const f32x4*)(bkt + 16);
+        }
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    s[qb][4 * h2 + i] = BIAS && !SC ? scur[qb][h2][i] + scur[kQB][h2][i] : scur[qb][h2][i];
+                    s[qb][4 * h2 + i] = kSharedBias ? scur[qb][h2][i] + bk[h2][i] : scur[qb][h2][i];
         if (j == last_j) {                  // the diagonal step: causal mask (also covers
                                             // keys past the prompt)
 #pragma unroll
@@ -662,10 +692,6 @@ prefill_attn_kernel(const PrefillParams p) {
         for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) scur[qb][h2] = snext[qb][h2];
-        if constexpr (BIAS && !SC) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) scur[kQB][h2] = snext[kQB][h2];
-        }
     };
     for (int j0 = 0; j0 < nsteps; j0 += 4) {
         step(j0, std::integral_constant<int, 0>{});
