@@ -36,6 +36,9 @@ constexpr int kPQ = 4 * 16 * kQB;         // query positions per workgroup
 constexpr int kPK = 64;                   // key positions per LDS tile
 constexpr float kNegInfP = -__builtin_inff();
 constexpr float kLazy = 8.0f;             // log2 headroom of the softmax reference
+// The INT8 staging holds V codes times this power of two and V scales
+// divided by it (see prefill_append_i8_kernel).
+constexpr float kVStageGain = 8.0f;
 
 template <int KV, int D, bool PG>
 __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams p) {
@@ -190,9 +193,10 @@ __global__ void __launch_bounds__(256) prefill_append_i8_kernel(const PrefillPar
                                                       0x0c0c0400u);
             w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
         }
+        const float gain = which ? kVStageGain : 1.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k)         // integers of at most 8 bits: exact in fp16 under any rounding
-            hq[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cq[2 * k], cq[2 * k + 1]));
+        for (int k = 0; k < 8; ++k)         // integers of at most 11 bits: exact in fp16 under any rounding
+            hq[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cq[2 * k] * gain, cq[2 * k + 1] * gain));
         if (crow >= 0) {
             *(u32x4*)((int8_t*)(which ? p.v_cache : p.k_cache) + (size_t)crow * D + e0) = u32x4{w[0], w[1], w[2], w[3]};
             if (e0 == 0) p.kv_scales[which * half + srow] = scale;
@@ -200,7 +204,13 @@ __global__ void __launch_bounds__(256) prefill_append_i8_kernel(const PrefillPar
         uint16_t* st = (uint16_t*)(which ? p.stage_v : p.stage_k) + stage_row * D + e0;
         *(u32x4*)st = u32x4{hq[0], hq[1], hq[2], hq[3]};
         *(u32x4*)(st + 8) = u32x4{hq[4], hq[5], hq[6], hq[7]};
-        if (e0 == 0) (which ? p.stage_vs : p.stage_ks)[stage_row] = scale;
+        // V is staged as code x kVStageGain with its scale / kVStageGain: the
+        // attention puts each softmax weight (at most 2^kLazy) times its key's
+        // staged V scale into fp16, and a row of fp16 values plus bias can
+        // reach an absmax of 131008 (scale 1031.6); divided by 8 that product
+        // stays below 33013 for every finite input.  Only a power of two
+        // moves between the two factors of each product.
+        if (e0 == 0) (which ? p.stage_vs : p.stage_ks)[stage_row] = which ? scale * (1.0f / kVStageGain) : scale;
     }
 }
 

@@ -269,9 +269,10 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
  * call that would grow it is refused, as for ftm_decode_mha.  The attention
  * multiplies each raw score by its key's K scale and each softmax weight
  * (at most 2^8 against the running reference) by its key's V scale in
- * fp32 before the weight enters the matrix cores in fp16: a V row's
- * absolute maximum must stay below about 32500 (256 s_v within the fp16
- * range).  INT8 limits: prompt_len * head_dim * 2 and
+ * fp32 before the weight enters the matrix cores in fp16; the staging
+ * holds V codes times 8 and V scales divided by 8, so that product stays
+ * within the fp16 range for every finite fp16 input and bias (only a power
+ * of two moves between the two factors).  INT8 limits: prompt_len * head_dim * 2 and
  * prompt_len * n_kv_heads * head_dim / 16 below 2^31 (FTM_ERR_UNSUPPORTED).
  * Two kernels are enqueued (append, then attention).  The attention runs on
  * the matrix cores with fp32

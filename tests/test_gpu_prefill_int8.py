@@ -213,3 +213,42 @@ def test_int8_prefill_quantisation_ties(ftm):
             row[pos % 128] = 127.0 if pos % 2 == 0 else 127.0 * (1 + 2 ** -10)
             t[pos % 2, pos, pos % 2] = row.to(torch.float16)
     run_and_compare(ftm, case, inp, "int8 prefill quantisation ties", paged=False)
+
+
+def test_int8_prefill_v_rows_of_any_fp16_size(ftm):
+    """V rows whose absolute maximum is far past 32496, where a weight (up to
+    2^8 against the running reference) times the V scale would leave the
+    fp16 range if the staging held the plain scale: one row at 40000, and
+    every row of another KV head shifted by a bias of up to 30000 with one
+    of them reaching 60000 (outputs stay inside the fp16 range).  Every
+    output row meets the bar against the oracle and the cache holds its
+    codes and scales."""
+    case = W.PrefillCase("t", 2, 200, 8, 2, 128, "i8", 208, lens=(150, 200), seed=151)
+    inp = W.make_prefill_inputs(case, "cpu", poison=True)
+    H, Hkv, D = case.n_heads, case.n_kv_heads, case.head_dim
+    inp["v_new"][0, 77, 1, :] = torch.linspace(-40000.0, 40000.0, D).half()
+    inp["v_new"][1, 30, 0, :] = torch.linspace(-30000.0, 30000.0, D).half()
+    inp["bias"][(H + Hkv) * D:(H + Hkv + 1) * D] = torch.linspace(-30000.0, 30000.0, D).half()
+    npi = host(inp)
+    lens = inp["seq_lens"].numpy().astype(np.int32)
+    ref = oracle.prefill_mha(npi["q"], npi["k_new"], npi["v_new"], npi["bias"], npi["k_cache"], npi["v_cache"],
+                             lens, H, Hkv, D, "i8", npi["kv_scales"])
+    g = {k: v.cuda() for k, v in inp.items()}
+    out = torch.zeros((case.batch, case.prompt, H, D), dtype=torch.float16, device="cuda")
+    ftm.ftm_prefill_mha(g["q"], g["k_new"], g["v_new"], g["bias"], g["k_cache"], g["v_cache"], g["seq_lens"],
+                        out, kv_scales=g["kv_scales"])
+    torch.cuda.synchronize()
+    for name in ("k_cache", "v_cache", "kv_scales"):
+        assert g[name].cpu().numpy().tobytes() == npi[name].tobytes(), name
+    assert npi["kv_scales"][1, 0, 1, 77] > 65504.0 / 256 and npi["kv_scales"][1, 1, 0, 30] > 450
+    got = out_to_f64(out)
+    ac = W.Case("p", case.batch, H, Hkv, D, "i8", ctx=case.prompt, max_seq_len=case.max_seq_len, value_scale=1.0)
+    for b in range(case.batch):
+        Sb = int(lens[b])
+        assert np.isfinite(got[b, :Sb]).all()
+        # the absolute bar grows with the values: an fp32 sum of at most Sb
+        # weighted values errs by up to Sb 2^-24 max|v|, far above 2e-3 at
+        # |v| ~ 6e4; the row-relative bar (1e-2) stays as it is
+        vmax = 127.0 * float(npi["kv_scales"][1, b, :, :Sb].max())
+        check(ac, got[b, :Sb], ref[b, :Sb], f"int8 prefill large V rows b{b}",
+              tol=(2e-3 + Sb * 2.0 ** -24 * vmax, 1e-2))
