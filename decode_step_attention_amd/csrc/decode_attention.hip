@@ -305,7 +305,10 @@ __device__ __forceinline__ void store_new_row(float* x, float* stored, float& sc
 // clipped by the buffer descriptor (they return zeros and fetch nothing), so
 // the prefetch after the last iteration costs issue slots only.
 // ---------------------------------------------------------------------------
-template <int KV, int D, int GT, int U, int NW, bool PG>
+// PG: paged cache; LP (paged only): a page holds at least the rows one wave
+// loads per iteration, so one table read and one descriptor per stream serve
+// them all.
+template <int KV, int D, int GT, int U, int NW, bool PG, bool LP>
 __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
     using E = Elem<KV>;
     using A = Act<KV>;
@@ -378,11 +381,23 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(const Params p) {
         return i * 64 + lane < WAVE_ROWS ? (base + i * 64 + lane) * 4 : 0x7fffffff;
     };
     // rows base + u*RPI .. + RPI-1 lie in one page (P >= 16 >= RPI, both
-    // powers of two, base a multiple of RPI)
+    // powers of two, base a multiple of RPI); with LP so do all WAVE_ROWS
+    // rows from base (P >= WAVE_ROWS, base a multiple of WAVE_ROWS)
     auto issue_stream = [&](const void* pool, const __amdgpu_buffer_rsrc_t& rs,
                             const __amdgpu_buffer_rsrc_t& srs, size_t splane, u32x4* dst,
                             float* sdst, int base) {
-        if constexpr (PG) {
+        if constexpr (PG && LP) {
+            const auto prs = page_rsrc(pool, ROW_BYTES, tbl, p, j, base, stream_end, bad);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(prs, (u * RPI + r) * ROW_BYTES + c * 16, 0, kStream);
+            if constexpr (I8) {
+                const auto pss = page_rsrc(p.kv_scales + splane, 4, tbl, p, j, base, stream_end, bad);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    sdst[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pss, (u * RPI + r) * 4, 0, kStream));
+            }
+        } else if constexpr (PG) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int pos = base + u * RPI;
@@ -1463,22 +1478,35 @@ hipError_t launch_gqa_t(const Params& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int KV, int D, int GT, bool PG>
-hipError_t launch_attention_t(const Params& p, int nw, hipStream_t s) {
+template <int KV, int D, int GT, bool PG, bool LP>
+hipError_t launch_attention_lp(const Params& p, int nw, hipStream_t s) {
     dim3 grid(p.S, p.Hkv * p.n_hg, p.B);
-    if constexpr ((KV == KV_F16 || KV == KV_BF16) && (GT == 4 || GT == 8)) {
-        if (p.balanced) return launch_gqa_t<KV, D, GT, PG>(p, s);
-    }
     constexpr int U = unroll_for(GT);
     if constexpr (wide_built(KV, GT)) {
         if (nw == 16) {
-            hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 16, PG>), grid, dim3(64 * 16), 0, s, p);
+            hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 16, PG, LP>), grid, dim3(64 * 16), 0, s, p);
             return hipGetLastError();
         }
     }
     if (nw != 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 4, PG>), grid, dim3(64 * 4), 0, s, p);
+    hipLaunchKernelGGL((attention_kernel<KV, D, GT, U, 4, PG, LP>), grid, dim3(64 * 4), 0, s, p);
     return hipGetLastError();
+}
+
+template <int KV, int D, int GT, bool PG>
+hipError_t launch_attention_t(const Params& p, int nw, hipStream_t s) {
+    if constexpr ((KV == KV_F16 || KV == KV_BF16) && (GT == 4 || GT == 8)) {
+        if (p.balanced) return launch_gqa_t<KV, D, GT, PG>(p, s);
+    }
+    if constexpr (PG) {
+        // rows one wave loads per iteration (the same for both workgroup shapes)
+        constexpr int ELEM = KV == KV_F32 ? 4 : (KV == KV_I8 ? 1 : 2);
+        constexpr int WAVE_ROWS = 64 / (D * ELEM / 16) * unroll_for(GT);
+        if ((1 << p.page_shift) >= WAVE_ROWS) return launch_attention_lp<KV, D, GT, true, true>(p, nw, s);
+        return launch_attention_lp<KV, D, GT, true, false>(p, nw, s);
+    } else {
+        return launch_attention_lp<KV, D, GT, false, false>(p, nw, s);
+    }
 }
 
 template <int KV, int D, bool PG>
