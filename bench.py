@@ -16,8 +16,9 @@ metric is quoted on), and the tiny, sizing32, gqa and int8 workloads are
 reported beside it under "configs", each with its own roofline and CPU
 baseline.
 
---graph records each step's calls once into a HIP graph (ftm_graph_*) and
-times graph replays instead of one library call per layer.
+--graph records the calls into HIP graphs (ftm_graph_*), each holding at
+least 32 layer calls (one 32-layer step, or 32 one-layer steps), and times
+graph replays instead of one library call per layer.
 """
 from __future__ import annotations
 
@@ -419,23 +420,33 @@ def run_decode(args, case: W.Case, cpu_budget: float) -> dict:
     kernels_per_step = ftm.ftm_timing_read(0)[0] + ftm.ftm_timing_read(1)[0]
     ftm.ftm_timing_disable()
 
+    # graph mode: one graph holds at least --graph-calls layer calls (by
+    # default GRAPH_CALLS: a whole decode step of a 32-layer model, or 32
+    # consecutive steps of a one-layer workload), so that its launch is
+    # amortised over that much work; the timed steps are rounded up to
+    # whole graphs
+    spg = max(1, args.graph_calls // layers) if args.graph else 1     # steps per graph
+    steps = -(-args.steps // spg) * spg
     graphs = []
     if args.graph:
-        # one graph per distinct step: the step's layer calls on its cache
-        # sets, captured after the warm-up has sized the stream's workspace
-        n_graphs = max(1, rotate // layers)
+        # captured after the warm-up has sized the stream's workspace; calls
+        # cycle over the cache sets and the two output buffers as eager
+        # steps do
+        n_graphs = max(1, rotate // (spg * layers))
         for gi in range(n_graphs):
             ftm.ftm_graph_begin(stream.cuda_stream)
             try:
-                for lyr in range(layers):
-                    calls[(gi * layers + lyr) % rotate][0]()
+                for c in range(spg * layers):
+                    kk = gi * spg * layers + c
+                    calls[kk % rotate][kk & 1]()
             finally:
                 graphs.append(ftm.ftm_graph_end(stream.cuda_stream))
         for gi in range(min(args.warmup, len(graphs) * 4)):
             ftm.ftm_graph_launch(graphs[gi % len(graphs)], stream.cuda_stream)
         torch.cuda.synchronize()
 
-    def run_step(i):
+    def run_unit(i):
+        """Unit i of the timed loops: one graph (spg steps) or one step."""
         nonlocal k
         if graphs:
             ftm.ftm_graph_launch(graphs[i % len(graphs)], stream.cuda_stream)
@@ -444,14 +455,15 @@ def run_decode(args, case: W.Case, cpu_budget: float) -> dict:
             call(k)
             k += 1
 
+    units = steps // spg
     # timed region 1: the whole path, nothing else on the stream; a HIP event
     # pair on the launch stream brackets the region
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     r0.record(stream)
-    for i in range(args.steps):
-        run_step(i)
+    for i in range(units):
+        run_unit(i)
     r1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -462,38 +474,39 @@ def run_decode(args, case: W.Case, cpu_budget: float) -> dict:
     if not graphs:
         # timed region 2: the same steps with a HIP event pair recorded around
         # every kernel launch, on the launch stream, for per-kernel durations
-        ftm.ftm_timing_enable(args.steps * layers + 8)
+        ftm.ftm_timing_enable(steps * layers + 8)
         torch.cuda.synchronize()
         t2 = time.perf_counter()
-        for i in range(args.steps):
-            run_step(i)
+        for i in range(units):
+            run_unit(i)
         torch.cuda.synchronize()
         t3 = time.perf_counter()
         n_att, ms_att = ftm.ftm_timing_read(0)
         n_cmb, ms_cmb = ftm.ftm_timing_read(1)
         ftm.ftm_timing_disable()
-    # timed region 3: an event pair around every step, for the distribution
-    # of step times (each pair adds its own dispatch and release, a few us)
+    # timed region 3: an event pair around every step (graph mode: every
+    # graph, divided by its steps), for the distribution of step times (each
+    # pair adds its own dispatch and release, a few us)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(units)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(units):
         ev[i][0].record(stream)
-        run_step(i)
+        run_unit(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    step_us = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    step_us = np.sort(np.array([a.elapsed_time(b) * 1e3 / spg for a, b in ev]))
     for g in graphs:
         ftm.ftm_graph_destroy(g)
     elapsed = t1 - t0
-    ms_step = elapsed * 1e3 / args.steps
-    gbs = kv_step * args.steps / elapsed / 1e9
+    ms_step = elapsed * 1e3 / steps
+    gbs = kv_step * steps / elapsed / 1e9
     per_launch_us = ms_att * 1e3 / max(n_att, 1)
     if n_cmb == 0:
         # one kernel per step: its average duration is the event-bracketed
         # region time over the launches (an event pair around every launch
         # adds its own dispatch and release time, a few us)
-        avg_att_us = region_gpu_ms * 1e3 / (args.steps * layers)
+        avg_att_us = region_gpu_ms * 1e3 / (steps * layers)
         timing = ("events bracketing timed region 1 (graph replays) / layer launches" if graphs
                   else "events bracketing timed region 1 / launches (one kernel per step)")
     else:
@@ -507,11 +520,11 @@ def run_decode(args, case: W.Case, cpu_budget: float) -> dict:
             "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
             "kernel": kernel, "avg_launch_us": round(avg_att_us, 2),
             "avg_launch_us_per_launch_events": round(per_launch_us, 2), "timing": timing,
-            "launches": n_att if n_att else args.steps * layers,
+            "launches": n_att if n_att else steps * layers,
             "algorithmic_bytes_per_launch": kv_layer}
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": case.kv_dtype, "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": describe(case), "batch": case.batch, "n_heads": case.n_heads,
@@ -519,13 +532,14 @@ def run_decode(args, case: W.Case, cpu_budget: float) -> dict:
                    "context": step, "kv_dtype": case.kv_dtype, "act_dtype": case.act_dtype,
                    "layers_per_step": layers, "cache_sets_rotated": rotate,
                    "cache_layout": f"paged, {case.page_size}-token pages" if case.page_size else "contiguous",
-                   "launch": "HIP graph replay per step" if graphs else "one library call per layer"},
+                   "launch": (f"HIP graph replay, {spg * layers} layer calls ({spg} steps) per graph" if graphs
+                              else "one library call per layer")},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(case.batch * args.steps / elapsed, 1),
+        "tokens_per_s": round(case.batch * steps / elapsed, 1),
         "kv_bytes_per_step": kv_step,
-        "ms_per_step_with_kernel_events": round((t3 - t2) * 1e3 / args.steps, 5) if not graphs else None,
+        "ms_per_step_with_kernel_events": round((t3 - t2) * 1e3 / steps, 5) if not graphs else None,
         "kernels_per_step": kernels_per_step,
-        "gpu_ms_per_step": round(region_gpu_ms / args.steps, 5),
+        "gpu_ms_per_step": round(region_gpu_ms / steps, 5),
         "combine_avg_launch_us": round(ms_cmb * 1e3 / n_cmb, 2) if n_cmb else None,
         "step_us_per_step_events": {"p50": round(float(np.percentile(step_us, 50)), 2),
                                     "p99": round(float(np.percentile(step_us, 99)), 2),
@@ -547,6 +561,9 @@ def run_decode(args, case: W.Case, cpu_budget: float) -> dict:
     torch.cuda.empty_cache()
     return result
 
+
+# Layer calls one graph holds in graph mode.
+GRAPH_CALLS = 32
 
 # The headline workload, and the others reported beside it in the same line.
 HEADLINE = "7b"
@@ -571,7 +588,9 @@ def main():
     ap.add_argument("--cpu-budget-others", type=float, default=5.0,
                     help="seconds of oracle time for each other workload's CPU baseline")
     ap.add_argument("--graph", action="store_true",
-                    help="replay each step from a HIP graph instead of one call per layer")
+                    help="replay HIP graphs of layer calls instead of one call per layer")
+    ap.add_argument("--graph-calls", type=int, default=GRAPH_CALLS,
+                    help="layer calls one graph holds (rounded to whole steps; default 32)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the attention "
