@@ -127,32 +127,6 @@ __device__ __forceinline__ void load_act(const void* base, size_t off, float* x)
     }
 }
 
-// ---------------------------------------------------------------------------
-// Cross-lane reductions.  A cache row is held by LPR consecutive lanes
-// (LPR in {4, 8, 16, 32}); the all-reduce over those lanes stays inside a
-// DPP row where it can: quad swaps, then the half-row mirror (8 lanes) or
-// rotations by 4 and 8 (16 lanes); a 32-lane row adds one cross-row swap.
-// ---------------------------------------------------------------------------
-template <int CTRL> __device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;
-
-template <int LPR> __device__ __forceinline__ float group_sum(float v) {
-    v += dpp<kQuadSwap1>(v);
-    v += dpp<kQuadSwap2>(v);
-    if constexpr (LPR == 8) v += dpp<kRowHalfMirror>(v);
-    if constexpr (LPR >= 16) {
-        v += dpp<kRowRor4>(v);
-        v += dpp<kRowRor8>(v);
-    }
-    if constexpr (LPR == 32) v += __shfl_xor(v, 16);
-    return v;
-}
 template <int LPR> __device__ __forceinline__ float group_max(float v) {
     v = fmaxf(v, dpp<kQuadSwap1>(v));
     v = fmaxf(v, dpp<kQuadSwap2>(v));

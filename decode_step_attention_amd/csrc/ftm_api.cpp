@@ -688,6 +688,8 @@ int prefill_impl(const void* q, const void* k_new, const void* v_new, const void
         n_kv_heads > 65535 * 16)
         return fail(FTM_ERR_UNSUPPORTED, "grid too large: batch <= 65535, batch * n_heads < 2^31, "
                                          "prompt_len <= 65535 * 128 and n_kv_heads <= 65535 * 16");
+    if ((size_t)((prompt_len * (size_t)head_dim + 2047) / 2048) * n_kv_heads > 0x7fffffffu)
+        return fail(FTM_ERR_UNSUPPORTED, "prompt_len * head_dim / 2048 * n_kv_heads (append blocks) must stay below 2^31");
     if (!block_table && (size_t)cache_rows * head_dim * 2 > 0x7fffffffu)
         return fail(FTM_ERR_UNSUPPORTED, "one (sequence, KV head) cache slab must stay below 2 GiB");
     if (i8 && ((size_t)prompt_len * head_dim * 2 > 0x7fffffffu ||
@@ -698,27 +700,34 @@ int prefill_impl(const void* q, const void* k_new, const void* v_new, const void
                          cache_rows, n_heads, n_kv_heads,
                          (float)(1.4426950408889634 / std::sqrt((double)head_dim)),
                          block_table, page_shift, max_pages, n_pages,
-                         kv_scales, nullptr, nullptr, nullptr, nullptr};
+                         kv_scales, nullptr, nullptr, nullptr, nullptr, nullptr};
     hipStream_t stream = (hipStream_t)stream_ptr;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (stream && hipStreamIsCapturing(stream, &cs) != hipSuccess)
         return fail(FTM_ERR_HIP, "hipStreamIsCapturing failed");
     const bool capturing = cs != hipStreamCaptureStatusNone;
-    if (i8) {
-        // the staging the attention reads: codes as fp16 and scales, K and V
+    // the stream's workspace: over an INT8 cache the staging the attention
+    // reads (codes as fp16 and scales, K and V); over a float cache with a
+    // bias the bias terms b_q . k of every prompt row and query head
+    const size_t rows = (size_t)batch * n_kv_heads * prompt_len;
+    const size_t code_bytes = rows * head_dim * 2;
+    const size_t stage_bytes = i8 ? 2 * code_bytes + 2 * rows * sizeof(float) : 0;
+    const size_t bterm_bytes = !i8 && qkv_bias ? (size_t)batch * n_heads * prompt_len * sizeof(float) : 0;
+    if (stage_bytes + bterm_bytes > 0) {
         int device = 0;
         hipError_t e = hipGetDevice(&device);
         if (e != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
-        const size_t rows = (size_t)batch * n_kv_heads * prompt_len;
-        const size_t code_bytes = rows * head_dim * 2;
         void* ws = nullptr;
-        int st = get_workspace(device, stream, 2 * code_bytes + 2 * rows * sizeof(float), 0, capturing, &ws,
-                               nullptr);
+        int st = get_workspace(device, stream, stage_bytes + bterm_bytes, 0, capturing, &ws, nullptr);
         if (st != FTM_OK) return st;
-        p.stage_k = ws;
-        p.stage_v = (char*)ws + code_bytes;
-        p.stage_ks = (float*)((char*)ws + 2 * code_bytes);
-        p.stage_vs = p.stage_ks + rows;
+        if (i8) {
+            p.stage_k = ws;
+            p.stage_v = (char*)ws + code_bytes;
+            p.stage_ks = (float*)((char*)ws + 2 * code_bytes);
+            p.stage_vs = p.stage_ks + rows;
+        } else {
+            p.bterm = (float*)ws;
+        }
     }
     const auto none = std::pair<hipEvent_t, hipEvent_t>{nullptr, nullptr};
     auto ev = capturing ? none : timing_slot(1);

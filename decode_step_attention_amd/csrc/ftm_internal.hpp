@@ -114,6 +114,9 @@ struct PrefillParams {
     void* stage_v;
     float* stage_ks;
     float* stage_vs;
+    // float caches with a bias: b_q . k of every prompt row and query head,
+    // [B, H, S] fp32, written by the append and read by the attention
+    float* bterm;
 };
 
 hipError_t launch_attention(const Params& p, int kv, int head_dim, int gtile, int nw, hipStream_t s);

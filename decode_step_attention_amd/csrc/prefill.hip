@@ -5,7 +5,8 @@
 // positions [0, t] of its KV head.
 //
 // prefill_append_kernel: the prompt's K/V rows, with the bias added in fp32,
-//   rounded to nearest even into the cache (one 16-byte slice per thread).
+//   rounded to nearest even into the cache (one 16-byte slice per thread),
+//   and, with a bias, the terms b_q . k of every row and query head.
 // prefill_attn_kernel: one workgroup of 4 waves owns 128 query positions of
 //   one query head; each wave owns two blocks of 16.  Keys [0, last query]
 //   go through LDS in 64-key tiles, loaded straight from the cache into LDS
@@ -40,20 +41,22 @@ constexpr float kLazy = 8.0f;             // log2 headroom of the softmax refere
 // divided by it (see prefill_append_i8_kernel).
 constexpr float kVStageGain = 8.0f;
 
+// Grid (ceil(S / RPB) Hkv, B): a block owns RPB consecutive positions of
+// one (sequence, KV head), so its cache rows, and its bias terms per query
+// head, are each one contiguous run; a thread owns 8 elements (16 bytes) of
+// one row, the SL threads of a row are adjacent lanes.
 template <int KV, int D, bool PG>
 __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams p) {
-    // grid (S, slices of a row / 256, B): thread c of row (b, t) owns bytes
-    // 16 c .. +15 of the row's Hkv D elements, i.e. KV head c / (D / 8)
-    constexpr int SL = D / 8;               // 16-byte slices per head row
-    const int t = blockIdx.x;
-    const int c = blockIdx.y * 256 + threadIdx.x;
-    const int b = blockIdx.z;
-    if (c >= p.Hkv * SL) return;
+    constexpr int SL = D / 8;               // threads per head row
+    constexpr int RPB = 256 / SL;           // rows per block
+    const int b = blockIdx.y;
+    const int nt = (p.S + RPB - 1) / RPB;
+    const int j = (int)blockIdx.x / nt;
+    const int t = ((int)blockIdx.x - j * nt) * RPB + (int)threadIdx.x / SL;
+    const int e0 = ((int)threadIdx.x % SL) * 8;
     const int Sb = p.seq_lens ? p.seq_lens[b] : p.S;
-    if (Sb < 1 || Sb > p.S || t >= Sb) return;         // invalid length: no append
-    const int j = c / SL;
-    const int e0 = (c % SL) * 8;
-    const size_t src = ((size_t)b * p.S + t) * p.Hkv * D + (size_t)c * 8;
+    if (Sb < 1 || Sb > p.S || t >= Sb) return;         // invalid length: no append (whole rows return)
+    const size_t src = (((size_t)b * p.S + t) * p.Hkv + j) * D + e0;
     size_t dst;
     if constexpr (PG) {
         // row t mod P of the page the table names; no append into a page
@@ -71,6 +74,7 @@ __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams
         kb = *(const u32x4*)((const uint16_t*)p.bias + (size_t)(p.H + j) * D + e0);
         vb = *(const u32x4*)((const uint16_t*)p.bias + (size_t)(p.H + p.Hkv + j) * D + e0);
     }
+    float ks[8];                            // the stored K values, as fp32
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         float x[8], bx[8];
@@ -81,9 +85,27 @@ __global__ void __launch_bounds__(256) prefill_append_kernel(const PrefillParams
         for (int e = 0; e < 8; ++e) {
             const float y = x[e] + bx[e];   // one fp32 rounding (an absent bias adds +0)
             hb[e] = KV == KV_F16 ? float_to_half_bits(y) : float_to_bf16_bits(y);
+            if (which == 0) ks[e] = KV == KV_F16 ? half_bits_to_float(hb[e]) : bf16_bits_to_float(hb[e]);
         }
         *(u32x4*)((uint16_t*)(which ? p.v_cache : p.k_cache) + dst) =
             u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+    }
+    // the bias terms b_q . k of this row for the query heads of KV head j:
+    // exact products of the stored K and the query bias, summed in fp32 over
+    // this thread's 8 elements and then over the SL threads of the row
+    // (adjacent lanes of one DPP row, SL a power of two)
+    if (p.bterm) {
+        const int G = p.H / p.Hkv;
+        for (int gi = 0; gi < G; ++gi) {
+            const int h = j * G + gi;
+            float bq[8];
+            Elem16<KV>::unpack(*(const u32x4*)((const uint16_t*)p.bias + (size_t)h * D + e0), bq);
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d = __builtin_fmaf(bq[e], ks[e], d);
+            d = group_sum<SL>(d);           // the row's SL lanes, by DPP
+            if (e0 == 0) p.bterm[((size_t)b * p.H + h) * p.S + t] = d;
+        }
     }
 }
 
@@ -283,18 +305,14 @@ prefill_attn_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char ktile1[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char vtile1[TILE];
     // SC: each wave's own copy of a tile's 64 key scales (one 4-byte load
-    // per lane), loaded with the K (or V) tile
-    constexpr int SCB = SC ? 4 * 64 * 4 : 16;
+    // per lane), loaded with the K (or V) tile.  Float caches with a bias:
+    // the K buffers hold the tile's 64 bias terms b_q . k instead.
+    constexpr bool kBiasTerms = BIAS && !SC;
+    constexpr int SCB = SC ? 4 * 64 * 4 : (kBiasTerms ? 4 * 64 * 4 : 16);
     __shared__ __attribute__((aligned(16))) unsigned char kscl0[SCB];
     __shared__ __attribute__((aligned(16))) unsigned char vscl0[SCB];
     __shared__ __attribute__((aligned(16))) unsigned char kscl1[SCB];
     __shared__ __attribute__((aligned(16))) unsigned char vscl1[SCB];
-    // the bias terms b_q . k of a K tile's 64 keys (float caches with a
-    // bias), double-buffered by tile parity: wave w computes keys 16 w ..
-    // 16 w + 15 when the tile lands, every wave reads its own keys' terms
-    constexpr bool kSharedBias = BIAS && !SC;
-    __shared__ __attribute__((aligned(16))) float bkt0[kSharedBias ? kPK : 4];
-    __shared__ __attribute__((aligned(16))) float bkt1[kSharedBias ? kPK : 4];
     auto kswz = [](int r) { return (r * NCH / 16) & (NCH - 1); };
     auto vswz = [](int r) { return 2 * ((r * NCH / 16) & (NCH / 2 - 1)); };
 
@@ -357,7 +375,9 @@ prefill_attn_kernel(const PrefillParams p) {
     const auto krs = make_rsrc((const char*)p.k_cache + row0 * ROW, (uint32_t)kend * ROW);
     const auto vrs = make_rsrc((const char*)p.v_cache + row0 * ROW, (uint32_t)kend * ROW);
     const size_t srow0 = ((size_t)b * p.Hkv + j) * p.Lmax;
-    const auto ksr = make_rsrc(SC ? (const char*)(p.stage_ks + srow0) : nullptr, SC ? (uint32_t)kend * 4 : 0u);
+    const auto ksr = make_rsrc(SC ? (const char*)(p.stage_ks + srow0)
+                                  : kBiasTerms ? (const char*)(p.bterm + ((size_t)b * p.H + h) * p.S) : nullptr,
+                               SC || kBiasTerms ? (uint32_t)kend * 4 : 0u);
     const auto vsr = make_rsrc(SC ? (const char*)(p.stage_vs + srow0) : nullptr, SC ? (uint32_t)kend * 4 : 0u);
     // one 64-key tile of K or V into LDS: NI loads per lane; load u of this
     // wave fills tile bytes base(u) .. +1023, lane i bytes base + 16 i .. +15,
@@ -383,6 +403,9 @@ prefill_attn_kernel(const PrefillParams p) {
     auto issue = [&](const bool is_v, int k0, unsigned char* dst, const int* offs, unsigned char* sdst) {
         if constexpr (SC)
             buffer_load_lds4(is_v ? vsr : ksr, sdst + wave * 256, lane * 4, __builtin_amdgcn_readfirstlane(k0 * 4));
+        if constexpr (kBiasTerms) {
+            if (!is_v) buffer_load_lds4(ksr, sdst + wave * 256, lane * 4, __builtin_amdgcn_readfirstlane(k0 * 4));
+        }
         if constexpr (!PG) {
             const auto rs = is_v ? vrs : krs;
             const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * ROW));
@@ -409,12 +432,14 @@ prefill_attn_kernel(const PrefillParams p) {
     // exactly as stored, so every product on the matrix cores is exact in
     // fp32; the scale log2(e)/sqrt(D) is applied to the fp32 scores.  Queries
     // past the prompt are zero.  The bias term b_q . k is the same for every
-    // query of the head: it is computed once per key, with the bias as a
-    // second B operand (the same in every column), and added to the scores
-    // in fp32.  The loads are unconditional (a query past the prompt reads
-    // the last row, selected away) so that they are all in flight together.
+    // query of the head: over float caches the append computed it for every
+    // key (p.bterm) and it seeds the scores' accumulators; over the INT8
+    // staging it is computed here, with the bias as a second B operand (the
+    // same in every column), and added to the scores in fp32.  The loads are
+    // unconditional (a query past the prompt reads the last row, selected
+    // away) so that they are all in flight together.
     u32x4 qraw[kQB][KK], braw[KK];
-    if constexpr (BIAS) {
+    if constexpr (BIAS && SC) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
             braw[kk] = *(const u32x4*)((const uint16_t*)p.bias + (size_t)h * D + 32 * kk + 8 * g);
@@ -436,7 +461,7 @@ prefill_attn_kernel(const PrefillParams p) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qv[qb][kk] = MF::bits8(live ? qraw[qb][kk] : u32x4{0u, 0u, 0u, 0u});
     }
-    if constexpr (BIAS) {
+    if constexpr (BIAS && SC) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) bv[kk] = MF::bits8(braw[kk]);
     }
@@ -493,8 +518,9 @@ prefill_attn_kernel(const PrefillParams p) {
     // s_waitcnt vmcnt(NI): the gfx9 encoding puts vmcnt in bits 3:0, expcnt
     // (7) in 6:4 and lgkmcnt (15) in 11:8; through the builtin the compiler
     // sees the wait too.
-    constexpr int NB = NI + (SC ? 1 : 0);  // loads per lane per refill
-    auto wait_one_batch_behind = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70 | NB); };
+    constexpr int NBK = NI + (SC || kBiasTerms ? 1 : 0);   // loads per lane per K refill
+    constexpr int NBV = NI + (SC ? 1 : 0);                 // loads per lane per V refill
+    auto wait_one_batch_behind = [&](auto nb) { __builtin_amdgcn_s_waitcnt(0x0F70 | decltype(nb)::value); };
     // A workgroup barrier for LDS that leaves the newest tile loads in
     // flight (__syncthreads would wait for every load into LDS): this wave's
     // LDS accesses complete (lgkmcnt(0); vmcnt 63, expcnt 7 untouched), then
@@ -512,15 +538,22 @@ prefill_attn_kernel(const PrefillParams p) {
         }
     };
 
-    // unscaled S^T for the 32 keys of step jj from K buffer kt: row = key
-    // 32 jj + 16 h2 + 4g + i, column = query tq + 16 qb + n; with the INT8
-    // staging, entry kQB holds b_q . k (every column alike)
+    // unscaled S^T for the 32 keys `half` of the tile in K buffer kt: row =
+    // key 32 half + 16 h2 + 4g + i, column = query tq + 16 qb + n.  Float
+    // caches with a bias: the accumulators start from the keys' bias terms
+    // (tbuf, the tile's term buffer), so the scores come out with b_q . k
+    // added.  INT8 staging with a bias: entry kQB holds b_q . k (every column
+    // alike).
     typedef f32x4 Scores[kQB + 1][2];
-    auto qk = [&](Scores& sa, const unsigned char* kt, int half) {
+    auto qk = [&](Scores& sa, const unsigned char* kt, const unsigned char* tbuf, int half) {
 #pragma unroll
-        for (int qb = 0; qb <= kQB; ++qb)
+        for (int h2 = 0; h2 < 2; ++h2) {
+            f32x4 seed = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (kBiasTerms) seed = *(const f32x4*)((const float*)(tbuf + wave * 256) + 32 * half + 16 * h2 + 4 * g);
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) sa[qb][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int qb = 0; qb < kQB; ++qb) sa[qb][h2] = seed;
+            sa[kQB][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -548,27 +581,12 @@ prefill_attn_kernel(const PrefillParams p) {
             }
     };
 
-    // b_q . k for keys 16 wave .. +15 of the K tile in kt, into bkt: one
-    // matrix-core product per 32 head elements with the bias as the B
-    // operand (every column alike), so lane (g, 0) holds keys 4g .. 4g + 3
-    auto bias_terms = [&](const unsigned char* kt, float* bkt) {
-        f32x4 bt = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            bt = MF::mma32(MF::bits8(*(const u32x4*)(kt + 16 * wave * ROW + koff[kk])), bv[kk], bt);
-        if (n == 0) *(f32x4*)(bkt + 16 * wave + 4 * g) = bt;
-    };
-
     Scores scur, snext;
     __builtin_amdgcn_s_waitcnt(0x0F70);     // the first tiles (and the query) landed
     __syncthreads();
     clear_v_tail(0, vtile0);
-    if constexpr (kSharedBias) {
-        bias_terms(ktile0, bkt0);
-        lds_barrier();
-    }
     if (0 <= last_j) {
-        qk(scur, ktile0, 0);
+        qk(scur, ktile0, kscl0, 0);
         if constexpr (SC) fold_k_scale(scur, kscl0, 0);
     }
 
@@ -581,38 +599,29 @@ prefill_attn_kernel(const PrefillParams p) {
         if constexpr (u % 2 == 0) {
             // new tile T: V(T) must have landed; V(T - 1)'s buffer is free
             if (j > 0) {
-                wait_one_batch_behind();    // K(T + 1) was issued after V(T)
+                wait_one_batch_behind(std::integral_constant<int, NBK>{});   // K(T + 1) was issued after V(T)
                 lds_barrier();
                 clear_v_tail(T, vt);
             }
             issue(true, T * kPK + kPK, (u / 2) ? vtile0 : vtile1, voffs, (u / 2) ? vscl0 : vscl1);
         } else {
             // K(T + 1) must have landed; K(T)'s buffer is free for K(T + 2)
-            wait_one_batch_behind();        // V(T + 1) was issued after K(T + 1)
+            wait_one_batch_behind(std::integral_constant<int, NBV>{});   // V(T + 1) was issued after K(T + 1)
             lds_barrier();
             issue(false, T * kPK + 2 * kPK, (u / 2) ? ktile1 : ktile0, koffs, (u / 2) ? kscl1 : kscl0);
-            // the bias terms of tile T + 1, read from the next step on
-            // (after its barrier); their buffer last served tile T - 1
-            if constexpr (kSharedBias) bias_terms((u / 2) ? ktile0 : ktile1, (u / 2) ? bkt0 : bkt1);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (j > last_j) return;
         const int kb = 32 * j;              // first key of the step
         // scores of this step; slot 4 h2 + i of this lane: key kb + 16 h2 + 4g + i
         float s[kQB][8];
-        f32x4 bk[2] = {};                   // this lane's keys' bias terms
-        if constexpr (kSharedBias) {
-            const float* bkt = ((u / 2) ? bkt1 : bkt0) + 32 * (j % 2) + 4 * g;
-            bk[0] = *(const f32x4*)bkt;
-            bk[1] = *(const f32x4*)(bkt + 16);
-        }
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    s[qb][4 * h2 + i] = kSharedBias ? scur[qb][h2][i] + bk[h2][i] : scur[qb][h2][i];
+                    s[qb][4 * h2 + i] = scur[qb][h2][i];
         if (j == last_j) {                  // the diagonal step: causal mask (also covers
                                             // keys past the prompt)
 #pragma unroll
@@ -653,7 +662,7 @@ prefill_attn_kernel(const PrefillParams p) {
         // the scheduler with this step's exponentials.  Unconditional, so
         // that no branch separates the two: after a wave's last step the
         // result is not used (and may come from stale LDS).
-        qk(snext, (u == 0 || u == 3) ? ktile0 : ktile1, (j + 1) % 2);
+        qk(snext, (u == 0 || u == 3) ? ktile0 : ktile1, (u == 0 || u == 3) ? kscl0 : kscl1, (j + 1) % 2);
         vec8 ph[kQB], pl[kQB];
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
@@ -737,7 +746,8 @@ prefill_attn_kernel(const PrefillParams p) {
 
 template <int KV, int D>
 hipError_t launch_append_t(const PrefillParams& p, hipStream_t s) {
-    const dim3 grid((unsigned)p.S, (unsigned)((p.Hkv * (D / 8) + 255) / 256), (unsigned)p.B);
+    constexpr int RPB = 256 / (D / 8);
+    const dim3 grid((unsigned)((p.S + RPB - 1) / RPB * p.Hkv), (unsigned)p.B);
     if (p.block_table)
         hipLaunchKernelGGL((prefill_append_kernel<KV, D, true>), grid, dim3(256), 0, s, p);
     else

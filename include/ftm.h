@@ -278,7 +278,11 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
  * the matrix cores with fp32
  * accumulation: the query enters exactly as stored and the bias term
  * b_q . k separately (once per key and head), so the scores are exact
- * products summed in fp32 and then scaled.  fp16 softmax weights are
+ * products summed in fp32 and then scaled.  Over fp16/bf16 caches with a
+ * bias the append computes those terms into the stream's workspace
+ * (4 batch n_heads S bytes), grown on the first call of a larger shape as
+ * for the INT8 staging (so a capture needs one eager call of the shape on
+ * the stream first).  fp16 softmax weights are
  * rounded once to nearest (11 significant bits); bf16 weights, and those
  * over INT8 codes, enter as hi and lo halves, so about 16 (bf16) or 22
  * (fp16) bits of each reach the accumulators.  Limits: batch up to 65535,

@@ -162,9 +162,10 @@ def test_capture_refuses_to_grow_the_workspace(ftm):
 def test_prefill_graph_replays_match_eager_calls(ftm, paged, dt):
     """A prefill (append + attention) captured into a graph: every replay,
     with new query values between replays and eager work in between, must
-    give the eager call's outputs and caches bit for bit.  An INT8 prefill
-    stages its codes in the stream's workspace, so one eager call on the
-    stream sizes it before the capture."""
+    give the eager call's outputs and caches bit for bit.  A prefill with a
+    bias keeps its bias terms (float caches) or its staged codes (INT8) in
+    the stream's workspace, so one eager call on the stream sizes it before
+    the capture."""
     case = W.PrefillCase("t", 2, 200, 8, 2, 128, dt, 256, lens=(120, 200), seed=111)
     inp = W.make_prefill_inputs(case, "cpu", poison=True)
     if paged:
@@ -184,9 +185,8 @@ def test_prefill_graph_replays_match_eager_calls(ftm, paged, dt):
             ftm.ftm_prefill_mha(g["q"], g["k_new"], g["v_new"], g["bias"], g[ck], g[cv], g["seq_lens"], o,
                                 stream=stream.cuda_stream, kv_scales=sc)
 
-    if dt == "i8":
-        prefill(torch.zeros_like(out))
-        stream.synchronize()
+    prefill(torch.zeros_like(out))
+    stream.synchronize()
     ftm.ftm_graph_begin(stream.cuda_stream)
     try:
         prefill(out)
