@@ -148,6 +148,7 @@ ftm::Tuning read_tuning() {
         }
     }
     t.qkv_column_tiles = env_int("FTM_QKV_COLUMN_TILES", 0);
+    t.qkv_k_split = env_int("FTM_QKV_K_SPLIT", -1);
     return t;
 }
 
@@ -633,11 +634,30 @@ int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* 
     const long long n_out = (long long)(n_heads + 2 * n_kv_heads) * head_dim;
     if (n_out / 16 > 0x7fffffffLL || n_out * hidden * 2 > (1LL << 40))
         return fail(FTM_ERR_UNSUPPORTED, "weight matrix too large");
-    ftm::QkvParams p{x, w, bias, q, k_new, v_new, batch, hidden, n_heads, n_kv_heads, head_dim};
+    ftm::QkvParams p{x, w, bias, q, k_new, v_new, batch, hidden, n_heads, n_kv_heads, head_dim, nullptr, nullptr};
     int device = 0;
     hipError_t he = hipGetDevice(&device);
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
-    he = ftm::launch_qkv_proj(p, act_dtype, cu_count(device), (hipStream_t)stream_ptr);
+    const int n_cu = cu_count(device);
+    size_t n_counters = 0;
+    const size_t need = ftm::qkv_split_workspace(p, n_cu, &n_counters);
+    if (need > 0) {
+        // the k-split partial sums: the stream's workspace, which under
+        // capture must already be large enough
+        bool capturing = false;
+        if (stream_ptr) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            he = hipStreamIsCapturing(stream_ptr, &cs);
+            if (he != hipSuccess)
+                return fail(FTM_ERR_HIP, std::string("hipStreamIsCapturing: ") + hipGetErrorString(he));
+            capturing = cs != hipStreamCaptureStatusNone;
+        }
+        void* ws = nullptr;
+        int st = get_workspace(device, stream_ptr, need, n_counters, capturing, &ws, &p.counters);
+        if (st != FTM_OK) return st;
+        p.ws = (float*)ws;
+    }
+    he = ftm::launch_qkv_proj(p, act_dtype, n_cu, (hipStream_t)stream_ptr);
     if (he != hipSuccess) return fail(FTM_ERR_HIP, std::string("projection launch: ") + hipGetErrorString(he));
     g_last_error.clear();
     return FTM_OK;

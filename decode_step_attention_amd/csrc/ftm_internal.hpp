@@ -54,6 +54,7 @@ struct Tuning {
     int gqa_unit_cost;      // FTM_GQA_UNIT_COST: 0..64, -1 unset
     int gqa_skew_a, gqa_skew_b;  // FTM_GQA_SKEW=a,b: 1..16 each
     int qkv_column_tiles;   // FTM_QKV_COLUMN_TILES: 1..4
+    int qkv_k_split;        // FTM_QKV_K_SPLIT: 1 (one pass) or 2..4, -1 unset
 };
 const Tuning& tuning();
 
@@ -87,6 +88,8 @@ struct QkvParams {
     void* k_new;            // [B, Hkv, D] act
     void* v_new;            // [B, Hkv, D] act
     int B, hidden, H, Hkv, D;
+    float* ws;              // k-split partial sums (qkv_split_workspace bytes) or null
+    int* counters;          // k-split: one count per 128-feature column, zero between calls
 };
 
 // Prefill: the whole prompt of every sequence.
@@ -130,6 +133,9 @@ hipError_t launch_prefill_append_i8(const PrefillParams& p, int head_dim, hipStr
 hipError_t launch_prefill_attention_i8(const PrefillParams& p, int head_dim, hipStream_t s);
 // act: KV_F16 or KV_BF16; B <= 64, hidden a multiple of 256, (H + 2 Hkv) D a multiple of 16.
 hipError_t launch_qkv_proj(const QkvParams& p, int act, int n_cu, hipStream_t s);
+// Workspace bytes and counters the projection of this shape uses (0 and 0
+// when it runs in one pass).
+size_t qkv_split_workspace(const QkvParams& p, int n_cu, size_t* n_counters);
 hipError_t launch_combine(const Params& p, int kv, int head_dim, hipStream_t s);
 // Sets n ints at `dst` to zero with a kernel on `s` (no memset node, so it
 // may also be recorded into a graph).

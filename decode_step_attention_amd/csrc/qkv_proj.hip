@@ -54,7 +54,7 @@ template <int ACT> struct QMma {
 // 12 loads).  The last workgroup may hold fewer than 16 FT features: its
 // weight rows past the end read as zero and its tiles past the end are not
 // written.
-template <int ACT, int MT, int FT>
+template <int ACT, int MT, int FT, bool XS>
 __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p) {
     using M = QMma<ACT>;
     constexpr int COLS = 16 * FT;           // output features per workgroup
@@ -81,12 +81,23 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
     const auto wrs = make_rsrc((const char*)p.w + (size_t)f0 * row_bytes, (uint32_t)min(COLS, n_out - f0) * row_bytes);
     const auto xrs = make_rsrc(p.x, (uint32_t)p.B * row_bytes);
 
-    // per-wave weight tiles; after the loop, the partial sums of the
-    // reduction (at most kWaves / 2 waves' MT x FT tiles at a time)
+    // per-wave weight tiles (and, with XS, x tiles); after the loop, the
+    // partial sums of the reduction (at most kWaves / 2 waves' MT x FT
+    // tiles at a time)
     constexpr int TILE = COLS * PITCH;
+    constexpr int XTILE = XS ? 16 * MT * PITCH : 0;
     constexpr int RED = kWaves / 2 * MT * FT * 64 * 16;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[TILE * kWaves > RED ? TILE * kWaves : RED];
-    unsigned char* tile = smem + wave * TILE;
+    constexpr int WAVE_LDS = TILE + XTILE;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[WAVE_LDS * kWaves > RED ? WAVE_LDS * kWaves : RED];
+    unsigned char* tile = smem + wave * WAVE_LDS;
+    unsigned char* xtile = tile + TILE;
+    // XS: x comes in whole 128-byte lines (XL lanes per row of KIT k, XR
+    // rows per instruction), is written to the wave's x tile and read back
+    // in the A-operand layout
+    constexpr int XL = KIT * 2 / 16;
+    constexpr int XR = 64 / XL;
+    constexpr int NX = 16 * MT / XR;
+    static_assert(!XS || NX * XR == 16 * MT, "the x loads cover the batch tiles");
 
     // iterations outside [it0, it1) take an offset past the descriptor's
     // range: their loads fetch nothing, so the prefetch needs no branch
@@ -99,6 +110,15 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
             wr[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (RPIW * u + lrow) * row_bytes + koff + lcol * 16,
                                                           0, kStream);
     };
+    // XS: x of the next iteration in whole lines, in flight with its weights
+    u32x4 xl[XS ? NX : 1];
+    auto issue_x = [&](int it) {
+        const uint32_t koff = it < it1 ? (uint32_t)it * (KIT * 2) : 0x40000000u;
+#pragma unroll
+        for (int u = 0; u < NX; ++u)
+            xl[u] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (XR * u + lane / XL) * row_bytes + koff + (lane % XL) * 16,
+                                                          0, 0);
+    };
     f32x4 acc[MT][FT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -106,25 +126,41 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
         for (int ft = 0; ft < FT; ++ft) acc[mt][ft] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     issue_w(it0);
+    if constexpr (XS) issue_x(it0);
     __builtin_amdgcn_sched_barrier(0);
     for (int it = it0; it < it1; ++it) {
         // this iteration's x (A operand: batch row 16 mt + n, k = 32 s + 8 g ..),
         // issued after the weights of this iteration and before those of the next
         u32x4 xr[MT][KS];
+        if constexpr (!XS) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                xr[mt][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                    xrs, (16 * mt + n) * row_bytes + (it * KIT + 32 * s + 8 * g) * 2, 0, 0);
+                for (int s = 0; s < KS; ++s)
+                    xr[mt][s] = __builtin_amdgcn_raw_buffer_load_b128(
+                        xrs, (16 * mt + n) * row_bytes + (it * KIT + 32 * s + 8 * g) * 2, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         // stage this iteration's weights, then send the next iteration's out
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int u = 0; u < NLD; ++u) *(u32x4*)(tile + (RPIW * u + lrow) * PITCH + lcol * 16) = wr[u];
+        if constexpr (XS) {
+#pragma unroll
+            for (int u = 0; u < NX; ++u) *(u32x4*)(xtile + (XR * u + lane / XL) * PITCH + (lane % XL) * 16) = xl[u];
+        }
         __builtin_amdgcn_sched_barrier(0);
         issue_w(it + 1);
+        if constexpr (XS) issue_x(it + 1);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (XS) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    xr[mt][s] = *(const u32x4*)(xtile + (16 * mt + n) * PITCH + (32 * s + 8 * g) * 2);
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // B operand: feature 16 ft + n, k = 32 s + 8 g ..
 #pragma unroll
@@ -192,6 +228,160 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
     }
 }
 
+// Batches above 32 rows: x is then about as large as a 48- or 64-feature
+// slice of the weights, and every workgroup of the one-pass kernel reads
+// all of it from L2, which costs time on top of the weight stream (at 64
+// rows and 64 features per workgroup, 8.6 us of 37).  This variant gives a
+// workgroup 128 features over 1/KSPLIT of the hidden dimension (KSPLIT
+// workgroups per column, enough to cover the CUs), halving x per weight
+// byte: every wave
+// owns 16 features, and per iteration the workgroup loads one x tile of
+// KIT k into LDS, shared by all eight waves (double-buffered, one barrier
+// per iteration).  Each workgroup writes its fp32 partial through to the
+// device coherence point and bumps its column's count; the workgroup that
+// completes the count adds the KSPLIT partials in split order (the sum does
+// not depend on which one finished last), adds the bias and writes q, k_new
+// and v_new.
+constexpr int kSplitKit = 256;          // k per iteration: whole 512-byte row segments
+constexpr int kSplitCols = 16 * kWaves; // features per workgroup
+constexpr int kCoherent = 16;           // cache policy sc1: agent-scope coherent access
+
+template <int ACT, int MT>
+__global__ void __launch_bounds__(64 * kWaves) qkv_split_kernel(const QkvParams p, const int ksplit) {
+    using M = QMma<ACT>;
+    constexpr int KIT = kSplitKit;
+    constexpr int KS = KIT / 32;            // MFMA k-steps per iteration
+    constexpr int PITCH = KIT * 2 + 16;     // LDS row pitch: 16-byte reads of 16 rows hit distinct banks
+    constexpr int LPR = KIT / 8;            // loads: lanes per row (16 bytes each)
+    constexpr int RPI = 64 / LPR;           // loads: rows per instruction
+    constexpr int NLD = 16 / RPI;           // weight loads per wave and iteration (16 rows)
+    constexpr int XROWS = 16 * MT;          // x rows staged (rows past the batch read as zero)
+    constexpr int NXL = XROWS / kWaves / RPI;   // x loads per wave and iteration
+    static_assert(NXL * RPI * kWaves == XROWS, "the waves' x loads cover the tile");
+    constexpr int XTILE = XROWS * PITCH;
+    constexpr int WTILE = 16 * PITCH;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * XTILE + kWaves * WTILE];
+    __shared__ int sm_last;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int n = lane & 15;
+    const int lrow = lane / LPR;
+    const int lcol = lane % LPR;
+    const int col = blockIdx.x / ksplit;
+    const int kh = blockIdx.x - col * ksplit;
+    const int n_out = (p.H + 2 * p.Hkv) * p.D;
+    const int f0 = col * kSplitCols + 16 * wave;    // the wave's first feature
+    const int nit = p.hidden / KIT;
+    const int it0 = kh * nit / ksplit;
+    const int it1 = (kh + 1) * nit / ksplit;
+    const uint32_t row_bytes = (uint32_t)p.hidden * 2;
+    // the wave's weight rows (none past the end: those read as zero)
+    const auto wrs = make_rsrc((const char*)p.w + (size_t)min(f0, n_out) * row_bytes,
+                               (uint32_t)max(0, min(16, n_out - f0)) * row_bytes);
+    const auto xrs = make_rsrc(p.x, (uint32_t)p.B * row_bytes);
+    unsigned char* wtile = smem + 2 * XTILE + wave * WTILE;
+
+    // iterations past the range load from past the descriptors' ends:
+    // nothing is fetched and no branch is needed
+    u32x4 wr[NLD], xl[NXL];
+    auto issue = [&](int it) {
+        const uint32_t koff = it < it1 ? (uint32_t)it * (KIT * 2) : 0x40000000u;
+#pragma unroll
+        for (int u = 0; u < NLD; ++u)
+            wr[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (RPI * u + lrow) * row_bytes + koff + lcol * 16, 0,
+                                                          kStream);
+#pragma unroll
+        for (int u = 0; u < NXL; ++u)
+            xl[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                xrs, ((NXL * wave + u) * RPI + lrow) * row_bytes + koff + lcol * 16, 0, 0);
+    };
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    issue(it0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = it0; it < it1; ++it) {
+        unsigned char* xtile = smem + ((it - it0) & 1) * XTILE;
+        // this iteration's tiles into LDS (the x tile whose readers were two
+        // iterations back, past the last barrier), the next iteration's out
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) *(u32x4*)(wtile + (RPI * u + lrow) * PITCH + lcol * 16) = wr[u];
+#pragma unroll
+        for (int u = 0; u < NXL; ++u)
+            *(u32x4*)(xtile + ((NXL * wave + u) * RPI + lrow) * PITCH + lcol * 16) = xl[u];
+        __builtin_amdgcn_sched_barrier(0);
+        issue(it + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();                    // every wave's part of the x tile is in
+        // A operand: batch row 16 mt + n; B operand: feature f0 + n; k = 32 s + 8 g ..
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const u32x4 wb = *(const u32x4*)(wtile + n * PITCH + (32 * s + 8 * g) * 2);
+            u32x4 xa[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) xa[mt] = *(const u32x4*)(xtile + (16 * mt + n) * PITCH + (32 * s + 8 * g) * 2);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = M::mma(xa[mt], wb, acc[mt]);
+        }
+    }
+
+    // partial of this workgroup: slot (col, kh), [wave][mt][lane] f32x4
+    const size_t slot_f4 = (size_t)kWaves * MT * 64;
+    const auto wsr = make_rsrc(p.ws + (size_t)col * ksplit * slot_f4 * 4, (uint32_t)(ksplit * slot_f4 * 16));
+    auto at = [&](int k, int mt) { return (uint32_t)((((size_t)k * kWaves + wave) * MT + mt) * 64 + lane) * 16; };
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mt]), wsr, at(kh, mt), 0, kCoherent);
+    // the partial stores count as done only once the coherence point has
+    // them; then the count goes up, and the workgroup that completes it
+    // reads the others' partials with coherent loads
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        sm_last = __hip_atomic_fetch_add(&p.counters[col], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  ksplit - 1;
+    __syncthreads();
+    if (!sm_last) return;
+    f32x4 sum[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sum[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < ksplit; ++k) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 part = k == kh ? acc[mt]
+                                       : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                       wsr, at(k, mt), 0, kCoherent));
+            sum[mt] = k == 0 ? part : sum[mt] + part;
+        }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&p.counters[col], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (f0 >= n_out) return;                // past the last feature (n_out is a multiple of 16)
+
+    // C layout: lane (g, n) holds feature f0 + n for batch rows 16 mt + 4 g + i
+    const int qd = p.H * p.D, kd = p.Hkv * p.D;
+    const int f = f0 + n;
+    void* dst;
+    int width, c;
+    if (f0 < qd) {
+        dst = p.q, width = qd, c = f;
+    } else if (f0 < qd + kd) {
+        dst = p.k_new, width = kd, c = f - qd;
+    } else {
+        dst = p.v_new, width = kd, c = f - qd - kd;
+    }
+    const float bf = p.bias ? M::ld(p.bias, f) : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * mt + 4 * g + i;
+            if (row < p.B) M::st(dst, (size_t)row * width + c, p.bias ? sum[mt][i] + bf : sum[mt][i]);
+        }
+}
+
 // Column tiles per workgroup.  Every CU streams weights at about the same
 // rate, so the time goes with (rounds of workgroups over the CUs) x FT; the
 // choice minimises that, and on a tie takes the larger FT (x read from L2
@@ -214,11 +404,16 @@ int column_tiles(int n_out, int n_cu) {
     return best;
 }
 
+#ifndef FTM_QKV_XSTAGE
+#define FTM_QKV_XSTAGE 1
+#endif
 template <int ACT, int MT, int FT>
 hipError_t launch_mf(const QkvParams& p, hipStream_t s) {
     const int n_out = (p.H + 2 * p.Hkv) * p.D;
-    hipLaunchKernelGGL((qkv_proj_kernel<ACT, MT, FT>), dim3((n_out + 16 * FT - 1) / (16 * FT)), dim3(64 * kWaves), 0,
-                       s, p);
+    // x through LDS in whole lines where the tiles fit (four column tiles)
+    constexpr bool XS = FTM_QKV_XSTAGE && FT == 4 && MT >= 2;
+    hipLaunchKernelGGL((qkv_proj_kernel<ACT, MT, FT, XS>), dim3((n_out + 16 * FT - 1) / (16 * FT)), dim3(64 * kWaves),
+                       0, s, p);
     return hipGetLastError();
 }
 
@@ -233,12 +428,57 @@ hipError_t launch_m(const QkvParams& p, int ft, hipStream_t s) {
     }
 }
 
+// k-split workgroups per 128-feature column, or 1 (one pass).  The split
+// serves batches above 32 rows where the one-pass kernel would take fewer
+// than four column tiles: there x cannot be staged through LDS beside the
+// weights and is read in the operand layout at a cost above the weights'
+// (measured at batch 64, hidden 8192, 10240 features: 40 against 53 us).
+// With four column tiles the one-pass kernel's barrier-free loop is the
+// faster (37.0 against 38.4 us at 15360 features, hidden 5120).  The split
+// count keeps the grid within the CUs, at most four, and at least two.  On
+// 256 CUs: two for 12288 features, three for 10240.
+// FTM_QKV_K_SPLIT (1 to 4) forces the choice.
+int k_split(const QkvParams& p, int n_cu) {
+    const int n_out = (p.H + 2 * p.Hkv) * p.D;
+    const int nit = p.hidden / kSplitKit;
+    const int cols = (n_out + kSplitCols - 1) / kSplitCols;
+    const int forced = tuning().qkv_k_split;
+    int ks;
+    if (forced >= 1 && forced <= 4) {
+        ks = forced;
+    } else {
+        if (p.B <= 32 || column_tiles(n_out, n_cu) == 4) return 1;
+        ks = min(4, n_cu / cols);
+    }
+    ks = min(ks, nit);
+    return ks >= 2 ? ks : 1;
+}
+
+template <int ACT, int MT>
+hipError_t launch_split(const QkvParams& p, int ks, hipStream_t s) {
+    const int n_out = (p.H + 2 * p.Hkv) * p.D;
+    const int cols = (n_out + kSplitCols - 1) / kSplitCols;
+    hipLaunchKernelGGL((qkv_split_kernel<ACT, MT>), dim3(cols * ks), dim3(64 * kWaves), 0, s, p, ks);
+    return hipGetLastError();
+}
+
 template <int ACT>
 hipError_t launch_t(const QkvParams& p, int n_cu, hipStream_t s) {
     const int n_out = (p.H + 2 * p.Hkv) * p.D;
     const int mt = (p.B + 15) / 16;
     const int ft = column_tiles(n_out, n_cu);
     if (p.hidden % 256 != 0 || n_out % 16 != 0) return hipErrorInvalidValue;
+    const int ks = k_split(p, n_cu);
+    if (ks > 1) {
+        if (!p.ws || !p.counters) return hipErrorInvalidValue;
+        switch (mt) {
+        case 1: return launch_split<ACT, 1>(p, ks, s);
+        case 2: return launch_split<ACT, 2>(p, ks, s);
+        case 3: return launch_split<ACT, 3>(p, ks, s);
+        case 4: return launch_split<ACT, 4>(p, ks, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (mt) {
     case 1: return launch_m<ACT, 1>(p, ft, s);
     case 2: return launch_m<ACT, 2>(p, ft, s);
@@ -249,6 +489,14 @@ hipError_t launch_t(const QkvParams& p, int n_cu, hipStream_t s) {
 }
 
 }  // namespace
+
+size_t qkv_split_workspace(const QkvParams& p, int n_cu, size_t* n_counters) {
+    const int ks = k_split(p, n_cu);
+    const int n_out = (p.H + 2 * p.Hkv) * p.D;
+    const size_t cols = (size_t)(n_out + kSplitCols - 1) / kSplitCols;
+    *n_counters = ks > 1 ? cols : 0;
+    return ks > 1 ? cols * ks * kWaves * ((p.B + 15) / 16) * 64 * 16 : 0;
+}
 
 hipError_t launch_qkv_proj(const QkvParams& p, int act, int n_cu, hipStream_t s) {
     switch (act) {

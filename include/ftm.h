@@ -228,10 +228,19 @@ int ftm_decode_mha_paged(const void* q, const void* k_new, const void* v_new,
  * nearest even.  When the bias is added here, pass qkv_bias = NULL to
  * ftm_decode_mha (or add it there instead, and pass NULL here).
  *
+ * Batches above 32 rows may split the hidden dimension over two to four
+ * workgroups per 128 output features; their fp32 partial sums then go
+ * through the stream's workspace (batch rounded up to 16, times 512 bytes
+ * per workgroup, at most about 8 MiB on 256 CUs) and are added in a fixed
+ * order, so the result does not depend on timing.  Under stream capture
+ * that workspace must already exist: make one eager call of the shape on
+ * the stream first.
+ *
  * Supported: batch 1..64, hidden a multiple of 256 up to 65536, head_dim a
  * multiple of 16.  All pointers 16-byte aligned; q, k_new and v_new must
  * not overlap x or w.  Errors as for ftm_decode_mha (FTM_ERR_UNSUPPORTED for
- * fp32 or sizes outside the supported set).  Only enqueues on `stream`.
+ * fp32 or sizes outside the supported set, FTM_ERR_OUT_OF_MEMORY if the
+ * workspace cannot grow).  Only enqueues on `stream`.
  */
 int ftm_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k_new,
                  void* v_new, int batch, int hidden, int n_heads, int n_kv_heads, int head_dim,
@@ -401,7 +410,7 @@ void ftm_release_workspaces(void);
 
 /* Re-reads the tuning variables of the environment (FTM_VALIDATE,
  * FTM_WAVES, FTM_SPLIT_CHUNK, FTM_GQA_VALU, FTM_GQA_BLOCKS_PER_CU,
- * FTM_GQA_UNIT_COST, FTM_GQA_SKEW, FTM_QKV_COLUMN_TILES).  The library
+ * FTM_GQA_UNIT_COST, FTM_GQA_SKEW, FTM_QKV_COLUMN_TILES, FTM_QKV_K_SPLIT).  The library
  * reads them once, at its first call, and not again on the call path;
  * a process that changes them calls this afterwards.  Not a step of the
  * method: the variables choose launch shapes for measurement and tests. */

@@ -192,3 +192,82 @@ def test_projection_then_attention(ftm, dt, H, Hkv):
         d = np.abs(gk[b, :, p] - rk[b, :, p])
         ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(rk[b, :, p]), 2.0 ** MIN_EXP[dt]))) - FRAC[dt])
         assert (d <= ulp).all(), f"appended K row of sequence {b} beyond one ulp"
+
+
+# k split: dtype, B, H, Hkv, D, hidden.  Feature counts that leave the last
+# 128-feature column partial, iteration counts (hidden / 256) that do not
+# divide by the split, and one to four batch tiles.
+SPLIT_SHAPES = [
+    ("bf16", 9, 8, 1, 64, 768),         # 640 features (5 columns), 3 iterations
+    ("f16", 33, 6, 2, 80, 1280),        # 800: the last column has 32 features, 5 iterations
+    ("f16", 48, 8, 8, 128, 1536),       # three batch tiles, 6 iterations
+    ("bf16", 64, 5, 5, 128, 2048),      # 1920 features, 8 iterations
+    ("bf16", 20, 4, 4, 64, 256),        # one iteration: every split clamps to one pass
+]
+
+
+def sentinel_outputs(case, g, tdt):
+    B, H, Hkv, D = case.batch, case.n_heads, case.n_kv_heads, case.head_dim
+    sizes = [B * H * D, B * Hkv * D, B * Hkv * D]
+    bufs = [torch.full((n + 4096,), 12345.0, dtype=tdt, device="cuda") for n in sizes]
+    outs = (bufs[0][:sizes[0]].view(B, H, D), bufs[1][:sizes[1]].view(B, Hkv, D),
+            bufs[2][:sizes[2]].view(B, Hkv, D))
+    return bufs, sizes, outs
+
+
+@pytest.mark.parametrize("ks", ["1", "2", "3", "4"])
+@pytest.mark.parametrize("dt,B,H,Hkv,D,hidden", SPLIT_SHAPES)
+def test_k_split(ftm, tuning, ks, dt, B, H, Hkv, D, hidden):
+    """Every k split (forced) of the 128-feature-column variant: each
+    workgroup's fp32 partial goes through the workspace and the last one
+    of its column adds them.  Every output is checked, and nothing is
+    written past the output buffers."""
+    tuning.set("FTM_QKV_K_SPLIT", ks)
+    case = W.ProjCase("t", B, H, Hkv, D, hidden, dt, seed=53 + B + D)
+    inp = W.make_proj_inputs(case)
+    g = {k: v.cuda() for k, v in inp.items()}
+    bufs, sizes, (q, k, v) = sentinel_outputs(case, g, W.TORCH_DTYPES[dt])
+    ftm.ftm_qkv_proj(g["x"], g["w"], g["bias"], q, k, v)
+    torch.cuda.synchronize()
+    for buf, n in zip(bufs, sizes):
+        assert bool((buf[n:] == 12345.0).all()), f"k split {ks}: a write past an output buffer"
+    ref, absdot = reference(inp, case)
+    check_proj(case, (q, k, v), ref, absdot, f"{dt} B{B} H{H}/{Hkv} D{D} hidden{hidden} k split {ks}")
+
+
+@pytest.mark.parametrize("ks", ["2", "3"])
+def test_k_split_is_repeatable(ftm, tuning, ks):
+    """The partials are added in split order whichever workgroup finishes
+    last, and the column counts return to zero: repeated calls, with a call
+    of another shape between them, give the same bits."""
+    tuning.set("FTM_QKV_K_SPLIT", ks)
+    case = W.ProjCase("t", 64, 8, 2, 128, 2048, "f16", seed=61)
+    other = W.ProjCase("t", 40, 4, 4, 64, 1024, "f16", seed=62)
+    inp, inp2 = W.make_proj_inputs(case), W.make_proj_inputs(other)
+    first = [t.clone() for t in run(ftm, inp, case)]
+    for _ in range(3):
+        run(ftm, inp2, other)
+        again = run(ftm, inp, case)
+        for a, b in zip(first, again):
+            assert torch.equal(bits(a.cpu()), bits(b.cpu()))
+    ref, absdot = reference(inp, case)
+    check_proj(case, first, ref, absdot, f"repeat k split {ks}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_k_split_routing_is_exact(ftm, tuning, dt):
+    """One-hot weight rows through the k split: each feature's one product
+    lands in one split's partial and the others add exact zeros."""
+    tuning.set("FTM_QKV_K_SPLIT", "3")
+    B, H, Hkv, D, hidden = 64, 8, 2, 64, 1536
+    case = W.ProjCase("r", B, H, Hkv, D, hidden, dt, seed=7)
+    inp = W.make_proj_inputs(case)
+    N = case.n_out
+    perm = torch.from_numpy(np.random.default_rng(4).integers(0, hidden, N))
+    w = torch.zeros((N, hidden), dtype=W.TORCH_DTYPES[dt])
+    w[torch.arange(N), perm] = 1.0
+    inp["w"] = w
+    q, k, v = run(ftm, inp, case, with_bias=False)
+    y = torch.cat([q.reshape(B, -1), k.reshape(B, -1), v.reshape(B, -1)], dim=1).cpu()
+    want = inp["x"][:, perm]
+    assert torch.equal(bits(y), bits(want))
