@@ -42,9 +42,21 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "decode_step_attention_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
+# The sources each kernel is built and launched from: a counter summary
+# stays valid while none of them changes.
+SHARED_SOURCES = ("gfx950.hpp", "ftm_internal.hpp", "ftm_api.cpp")
+KERNEL_SOURCES = {
+    "attention_kernel": ("decode_attention.hip",),
+    "gqa_kernel": ("decode_attention.hip",),
+    "qkv_proj_kernel": ("qkv_proj.hip",),
+    "qkv_split_kernel": ("qkv_proj.hip",),
+    "prefill_attn_kernel": ("prefill.hip",),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in sorted(KERNEL_SOURCES[kernel] + SHARED_SOURCES):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -68,7 +80,7 @@ def read_traffic(kernel: str, config: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash(kernel):
         return None
     return t
 
