@@ -14,12 +14,14 @@
 // dimension, split in eight: wave w takes an eighth of the k range.  Per
 // iteration a wave loads 8 KiB of its weight rows (each load instruction
 // covers whole 128-512-byte row segments), stages them in LDS and reads
-// them back in the B-operand layout of v_mfma_f32_16x16x32; x, small and
-// read by every workgroup, comes from L2 directly in the A-operand layout,
-// each load serving FT products.  The next iteration's weights are in
-// flight while the matrix cores work.  The eight partial sums meet in LDS in
-// a fixed order, the bias is added in fp32, and the result is rounded to
-// nearest even.
+// them back in the B-operand layout of v_mfma_f32_16x16x32.  x, small and
+// read by every workgroup from L2, comes in the A-operand layout directly
+// (16 rows x 64 bytes per load) or, with four column tiles and more than 16
+// rows, in whole 128-byte lines through a per-wave LDS tile; each load
+// serves FT products.  The next iteration's loads are in flight while the
+// matrix cores work.  The eight partial sums meet in LDS in a fixed order,
+// the bias is added in fp32, and the result is rounded to nearest even.
+// Large batches with fewer column tiles take the k-split kernel below.
 #include <cstdlib>
 
 #include "gfx950.hpp"
