@@ -214,3 +214,95 @@ def test_prefill_graph_replays_match_eager_calls(ftm, paged, dt):
                 assert torch.equal(got_s.view(torch.int32), g["kv_scales"].view(torch.int32)), f"replay {rep}: scales"
     finally:
         ftm.ftm_graph_destroy(graph)
+
+
+@pytest.mark.parametrize("ks", ["1", "2", "3"])
+def test_projection_graph_replays_match_eager_calls(ftm, tuning, ks):
+    """The fused QKV projection captured into a graph, in one pass and with
+    the hidden dimension split over two or three workgroups (their partial
+    sums go through the stream's workspace and a per-column count that the
+    kernel clears): every replay, with new x between replays and eager work
+    in between, must give the eager call's q, k_new and v_new bit for bit.
+    One eager call on the stream sizes the workspace before the capture."""
+    tuning.set("FTM_QKV_K_SPLIT", ks)
+    case = W.ProjCase("g", 64, 8, 2, 128, 2048, "f16", seed=121)
+    g = {k: v.cuda() for k, v in W.make_proj_inputs(case).items()}
+    B, H, Hkv, D = case.batch, case.n_heads, case.n_kv_heads, case.head_dim
+    outs = [torch.empty((B, H, D), dtype=torch.float16, device="cuda"),
+            torch.empty((B, Hkv, D), dtype=torch.float16, device="cuda"),
+            torch.empty((B, Hkv, D), dtype=torch.float16, device="cuda")]
+    refs = [torch.empty_like(o) for o in outs]
+    stream = torch.cuda.Stream()
+
+    def proj(dst):
+        ftm.ftm_qkv_proj(g["x"], g["w"], g["bias"], *dst, stream=stream.cuda_stream)
+
+    proj(refs)
+    stream.synchronize()
+    ftm.ftm_graph_begin(stream.cuda_stream)
+    try:
+        proj(outs)
+    finally:
+        graph = ftm.ftm_graph_end(stream.cuda_stream)
+    try:
+        gen = torch.Generator().manual_seed(9)
+        for rep in range(3):
+            x_new = torch.randn(g["x"].shape, generator=gen).to(torch.float16)
+            g["x"].copy_(x_new.cuda())
+            for o in outs:
+                o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            ftm.ftm_graph_launch(graph, stream.cuda_stream)
+            stream.synchronize()
+            got = [o.clone() for o in outs]
+            _ = (g["x"].float() * 2).sum().item()          # eager work between replays
+            proj(refs)
+            stream.synchronize()
+            for name, a, r in zip(("q", "k_new", "v_new"), got, refs):
+                assert torch.equal(bits(a), bits(r)), f"replay {rep}: {name} differs from eager"
+    finally:
+        ftm.ftm_graph_destroy(graph)
+
+
+def test_projection_capture_needs_a_sized_workspace(ftm, tuning):
+    """A k-split projection captured before any eager call has sized the
+    stream's workspace is refused (nothing recorded, the capture stays
+    valid); a one-pass projection recorded after it replays correctly."""
+    torch.cuda.synchronize()
+    ftm.ftm_release_workspaces()            # torch may hand out a stream a previous test used
+    case = W.ProjCase("g", 48, 4, 4, 64, 1024, "bf16", seed=122)
+    g = {k: v.cuda() for k, v in W.make_proj_inputs(case).items()}
+    B, H, Hkv, D = case.batch, case.n_heads, case.n_kv_heads, case.head_dim
+
+    def buffers():
+        return [torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((B, Hkv, D), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((B, Hkv, D), dtype=torch.bfloat16, device="cuda")]
+    outs, refs = buffers(), buffers()
+    stream = torch.cuda.Stream()
+    tuning.set("FTM_QKV_K_SPLIT", "1")
+    ftm.ftm_qkv_proj(g["x"], g["w"], g["bias"], *refs, stream=stream.cuda_stream)
+    stream.synchronize()
+    err = None
+    ftm.ftm_graph_begin(stream.cuda_stream)
+    try:
+        tuning.set("FTM_QKV_K_SPLIT", "2")
+        try:
+            ftm.ftm_qkv_proj(g["x"], g["w"], g["bias"], *outs, stream=stream.cuda_stream)
+        except RuntimeError as e:
+            err = str(e)
+        tuning.set("FTM_QKV_K_SPLIT", "1")
+        ftm.ftm_qkv_proj(g["x"], g["w"], g["bias"], *outs, stream=stream.cuda_stream)
+    finally:
+        graph = ftm.ftm_graph_end(stream.cuda_stream)
+    try:
+        assert err is not None and "captured" in err, err
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        ftm.ftm_graph_launch(graph, stream.cuda_stream)
+        stream.synchronize()
+        for name, a, r in zip(("q", "k_new", "v_new"), outs, refs):
+            assert torch.equal(bits(a), bits(r)), f"{name} differs from eager"
+    finally:
+        ftm.ftm_graph_destroy(graph)
