@@ -406,14 +406,12 @@ int column_tiles(int n_out, int n_cu) {
     return best;
 }
 
-#ifndef FTM_QKV_XSTAGE
-#define FTM_QKV_XSTAGE 1
-#endif
 template <int ACT, int MT, int FT>
 hipError_t launch_mf(const QkvParams& p, hipStream_t s) {
     const int n_out = (p.H + 2 * p.Hkv) * p.D;
-    // x through LDS in whole lines where the tiles fit (four column tiles)
-    constexpr bool XS = FTM_QKV_XSTAGE && FT == 4 && MT >= 2;
+    // x through LDS in whole lines where both tiles fit in LDS (four column
+    // tiles) and x is large enough to matter (more than one batch tile)
+    constexpr bool XS = FT == 4 && MT >= 2;
     hipLaunchKernelGGL((qkv_proj_kernel<ACT, MT, FT, XS>), dim3((n_out + 16 * FT - 1) / (16 * FT)), dim3(64 * kWaves),
                        0, s, p);
     return hipGetLastError();
