@@ -84,11 +84,10 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
     const auto xrs = make_rsrc(p.x, (uint32_t)p.B * row_bytes);
 
     // per-wave weight tiles (and, with XS, x tiles); after the loop, the
-    // partial sums of the reduction (at most kWaves / 2 waves' MT x FT
-    // tiles at a time)
+    // waves' partial sums (MT x FT tiles each)
     constexpr int TILE = COLS * PITCH;
     constexpr int XTILE = XS ? 16 * MT * PITCH : 0;
-    constexpr int RED = kWaves / 2 * MT * FT * 64 * 16;
+    constexpr int RED = kWaves * MT * FT * 64 * 16;
     constexpr int WAVE_LDS = TILE + XTILE;
     __shared__ __attribute__((aligned(16))) unsigned char smem[WAVE_LDS * kWaves > RED ? WAVE_LDS * kWaves : RED];
     unsigned char* tile = smem + wave * WAVE_LDS;
@@ -176,39 +175,30 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
         }
     }
 
-    // the partial sums meet in wave 0 as a tree: waves [h, 2h) hand theirs
-    // to waves [0, h) for h = kWaves/2, ..., 1 (fixed order: the result is
-    // deterministic)
-    f32x4* red = (f32x4*)smem;              // [kWaves / 2][MT][FT][64]
+    // the eight partial sums meet in LDS: every wave writes its tiles, then
+    // wave w adds up tiles w, w + 8, ... over the waves in order (a fixed
+    // order: the result is deterministic), adds the bias and writes them
+    f32x4* red = (f32x4*)smem;              // [kWaves][MT][FT][64]
     auto slot = [&](int w, int mt, int ft) { return red + ((w * MT + mt) * FT + ft) * 64 + lane; };
+    __syncthreads();                        // the tiles are free
 #pragma unroll
-    for (int h = kWaves / 2; h >= 1; h /= 2) {
-        __syncthreads();                    // the tiles, or the previous round's slots, are free
-        if (wave >= h && wave < 2 * h) {
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int ft = 0; ft < FT; ++ft) *slot(wave - h, mt, ft) = acc[mt][ft];
-        }
-        __syncthreads();
-        if (wave < h) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int ft = 0; ft < FT; ++ft) acc[mt][ft] += *slot(wave, mt, ft);
-        }
-    }
-    if (wave != 0) return;
+        for (int ft = 0; ft < FT; ++ft) *slot(wave, mt, ft) = acc[mt][ft];
+    __syncthreads();
 
     // C layout: lane (g, n) holds feature f0 + 16 ft + n for batch rows
     // 16 mt + 4 g + i.  Column tiles never straddle the Q/K/V boundaries
     // (H D and Hkv D are multiples of 16).
     const int qd = p.H * p.D, kd = p.Hkv * p.D;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
+    for (int t = wave; t < MT * FT; t += kWaves) {
+        const int mt = t / FT, ft = t - mt * FT;
         const int f = f0 + 16 * ft + n;
         const int fb = f0 + 16 * ft;        // the tile's first feature, the same in every lane
-        if (fb >= n_out) break;             // past the last feature (n_out is a multiple of 16)
+        if (fb >= n_out) continue;          // past the last feature (n_out is a multiple of 16)
+        f32x4 sum = *slot(0, mt, ft);
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) sum += *slot(w, mt, ft);
         void* dst;
         int width, col;
         if (fb < qd) {
@@ -220,13 +210,10 @@ __global__ void __launch_bounds__(64 * kWaves) qkv_proj_kernel(const QkvParams p
         }
         const float bf = p.bias ? M::ld(p.bias, f) : 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * mt + 4 * g + i;
-                if (row < p.B)
-                    M::st(dst, (size_t)row * width + col, p.bias ? acc[mt][ft][i] + bf : acc[mt][ft][i]);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * mt + 4 * g + i;
+            if (row < p.B) M::st(dst, (size_t)row * width + col, p.bias ? sum[i] + bf : sum[i]);
+        }
     }
 }
 
